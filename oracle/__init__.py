@@ -1,0 +1,143 @@
+"""CPU oracle for the 2D (dilated) Neighborhood Attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP
+library never imports it and shares no code with it; the oracle is plain C
+(``na2d_oracle.c``), built with gcc and loaded through ctypes.
+
+Everything is computed in float64 from the exact stored input values (a
+bf16/fp16 input is widened exactly before it gets here).  The definition it
+follows, with the reading taken for every point the source pages leave open,
+is written out in the header comment of ``na2d_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "na2d_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_na2d_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/_na2d_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.na2d_oracle_forward.restype = ctypes.c_int
+        lib.na2d_oracle_forward.argtypes = [
+            dp, dp, dp, dp,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int,
+            i64p, ctypes.c_int64,
+            dp, dp, dp, i32p, i32p, ctypes.c_int]
+        lib.na2d_oracle_valid.restype = ctypes.c_int
+        lib.na2d_oracle_valid.argtypes = [ctypes.c_int] * 4
+        _lib = lib
+    return _lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _f64(x):
+    # torch tensors and numpy arrays are both accepted; widening is exact.
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def valid(H: int, W: int, kernel_size: int, dilation: int) -> bool:
+    return bool(_load().na2d_oracle_valid(H, W, kernel_size, dilation))
+
+
+def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
+            scores: bool = False, probs: bool = False, neighbours: bool = False,
+            argmax: bool = False, threads: int | None = None):
+    """Oracle forward pass.
+
+    q, k, v: [B, heads, H, W, D]; rpb: [heads, 2k-1, 2k-1] or None (zero bias).
+    idx: optional 1-D array of flat query indices into B*heads*H*W; the
+    results are then returned for those queries only, in that order.
+
+    Returns a dict with ``out`` (shape [B, heads, H, W, D], or [len(idx), D])
+    and, on request, ``scores``/``probs`` ([..., k*k]), ``neighbours`` (flat
+    pixel index i*W + j of each window slot n = a*k + c) and ``argmax``.
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 5 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, heads, H, W, D] shape")
+    B, heads, H, W, D = q.shape
+    ks, dil = int(kernel_size), int(dilation)
+    side = 2 * ks - 1
+    if rpb is not None:
+        rpb = _f64(rpb)
+        if rpb.shape != (heads, side, side):
+            raise ValueError("rpb must be [heads, 2k-1, 2k-1]")
+    if idx is not None:
+        idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1))
+        nq = idx.shape[0]
+        lead = (nq,)
+    else:
+        nq = B * heads * H * W
+        lead = (B, heads, H, W)
+    nk = ks * ks
+    out = np.empty(lead + (D,), dtype=np.float64)
+    s = np.empty(lead + (nk,), dtype=np.float64) if scores else None
+    p = np.empty(lead + (nk,), dtype=np.float64) if probs else None
+    nb = np.empty(lead + (nk,), dtype=np.int32) if neighbours else None
+    am = np.empty(lead, dtype=np.int32) if argmax else None
+    rc = lib.na2d_oracle_forward(
+        _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+        _ptr(rpb, ctypes.c_double),
+        B, heads, H, W, D, ks, dil,
+        _ptr(idx, ctypes.c_int64), nq,
+        _ptr(out, ctypes.c_double), _ptr(s, ctypes.c_double), _ptr(p, ctypes.c_double),
+        _ptr(nb, ctypes.c_int32), _ptr(am, ctypes.c_int32),
+        threads if threads else default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the problem (status %d)" % rc)
+    res = {"out": out}
+    if scores:
+        res["scores"] = s
+    if probs:
+        res["probs"] = p
+    if neighbours:
+        res["neighbours"] = nb
+    if argmax:
+        res["argmax"] = am
+    return res
