@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the fused 2D Neighborhood Attention forward pass on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one full forward pass (neighbourhood map, QK + bias, softmax, AV,
+store) over one batch of the workload, on inputs already resident in HBM.
+The default workload is the NAT-Tiny stage-1 layer: B=64, heads=2, 56x56,
+D=32, k=7, d=1, bf16 (fp32 accumulation), seeded synthetic N(0,1) data.
+
+To keep the 256 MB Infinity Cache from serving the inputs, the timed steps
+rotate through enough input/output replicas to touch >= 1 GiB.  The K timed
+launches are captured once in a HIP graph and replayed (launch overhead off
+the host); wall time brackets the replay with device synchronisations, and
+HIP events recorded on the same stream give the per-launch kernel time used
+for the roofline figure.
+
+Prints ONE JSON line (rank 0).  --gpus N > 1 is refused: this library's
+benchmark runs on a single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from vision_transformer_local_amd import inputs as I  # noqa: E402
+from vision_transformer_local_amd import na2d  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+WORKLOADS = {
+    "nat_tiny_s1": I.NAT_TINY_S1,
+    "dinat_s1_d8": I.DINAT_S1_D8,
+    "dinat_s2_d4": I.DINAT_S2_D4,
+    "sweep_56": I.NAT_TINY_SWEEP[0], "sweep_28": I.NAT_TINY_SWEEP[1],
+    "sweep_14": I.NAT_TINY_SWEEP[2], "sweep_7": I.NAT_TINY_SWEEP[3],
+    "det_k7_d1_bf16": I.DETECTION[0], "det_k7_d1_f16": I.DETECTION[1],
+    "det_k7_d8_bf16": I.DETECTION[2], "det_k7_d8_f16": I.DETECTION[3],
+    "det_k13_d1_bf16": I.DETECTION[4], "det_k13_d1_f16": I.DETECTION[5],
+    "det_k13_d8_bf16": I.DETECTION[6], "det_k13_d8_f16": I.DETECTION[7],
+    "tiny_f32": I.TINY,
+}
+KERNEL_SOURCES = ["vision_transformer_local_amd/csrc/na2d_mfma.hip",
+                  "vision_transformer_local_amd/csrc/na2d_scalar.hip",
+                  "vision_transformer_local_amd/csrc/na2d_internal.h"]
+
+
+def elem_size(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+def algorithmic_bytes(p) -> int:
+    """Bytes the method itself must move: q, k, v read once, out written once,
+    plus the bias table."""
+    s = elem_size(p.dtype)
+    side = 2 * p.kernel_size - 1
+    return 4 * p.D * s * p.n_query_heads + p.heads * side * side * s
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, path: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when none exists for this kernel source."""
+    fn = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (path, workload))
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None  # kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(p, cpu_inputs, repeats=3):
+    import oracle
+    threads = oracle.default_threads()
+    arrs = [t.to(torch.float64).numpy() for t in cpu_inputs]
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.forward(*arrs, p.kernel_size, p.dilation, threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": p.n_query_heads / t, "unit": "queries*heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "whole workload (%d query-heads), median of %d runs, float64"
+                      % (p.n_query_heads, repeats)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="nat_tiny_s1", choices=sorted(WORKLOADS))
+    ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
+    ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; --gpus %d is not supported (each (batch, "
+              "head) plane is independent, so more GPUs would each run this same kernel "
+              "on their share of the batch)." % args.gpus, file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    p = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = na2d.lib()
+
+    cpu = I.make_inputs(p, seed=0)
+    q0, k0, v0, rpb0 = cpu
+    tbytes = q0.numel() * q0.element_size()
+    attn_bytes = p.n_query_heads * p.kernel_size ** 2 * 4 if args.path == "unfused" else 0
+    per_replica = 4 * tbytes + attn_bytes
+    R = max(2, math.ceil(args.rotate_bytes / per_replica))
+    rpb = rpb0.to(dev)
+    reps = []
+    for _ in range(R):
+        q, k, v = (t.to(dev) for t in (q0, k0, v0))
+        out = torch.empty_like(q)
+        attn = (torch.empty(p.shape[:4] + (p.kernel_size ** 2,), dtype=torch.float32,
+                            device=dev) if args.path == "unfused" else None)
+        reps.append((q, k, v, out, attn))
+    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
+    algo = {"fused": 0, "fma": 1}.get(args.path, 0)
+    B, heads, H, W, D = p.shape
+    ks, dil = p.kernel_size, p.dilation
+
+    def launch(i, stream):
+        q, k, v, out, attn = reps[i % R]
+        st = ctypes.c_void_p(stream)
+        if args.path == "unfused":
+            r = L.na2d_qkrpb(q.data_ptr(), k.data_ptr(), rpb.data_ptr(), attn.data_ptr(),
+                             B, heads, H, W, D, ks, dil, dt_code, st)
+            r = r or L.na2d_softmax(attn.data_ptr(), attn.data_ptr(), B, heads, H, W, ks, st)
+            r = r or L.na2d_av(attn.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               B, heads, H, W, D, ks, dil, dt_code, st)
+        else:
+            r = L.na2d_forward_algo(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                    out.data_ptr(), B, heads, H, W, D, ks, dil, dt_code,
+                                    algo, st)
+        if r != 0:
+            raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        launch(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    # sanity: a sample of the first replica's output against the oracle
+    import numpy as np
+    import oracle
+    idx = np.random.default_rng(0).choice(p.n_query_heads, size=min(4096, p.n_query_heads),
+                                          replace=False)
+    ref = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx)["out"]
+    got = reps[0][3].reshape(-1, D)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+    max_err = float(np.abs(got - ref).max())
+
+    K = args.steps
+    graph = None
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                cap = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(K):
+                    launch(i, cap)
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay: first-replay setup stays out of the timing
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            launch(i, stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kernel_ms = ev0.elapsed_time(ev1) / K
+    value = p.n_query_heads / (ms_per_step / 1e3)
+    abytes = algorithmic_bytes(p)
+    if args.path == "unfused":
+        abytes += 4 * p.n_query_heads * p.kernel_size ** 2 * 4  # fp32 attn w, r, w, r
+    achieved = abytes / (kernel_ms / 1e3) / 1e9
+    traffic = measured_traffic(args.workload, args.path)
+
+    rec = {
+        "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
+        "value": value,
+        "unit": "queries*heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, 0.02*N(0,1) bias)",
+        "config": {"workload": "%s: %s" % (args.workload, p.describe()),
+                   "B": B, "heads": heads, "H": H, "W": W, "D": D,
+                   "kernel_size": ks, "dilation": dil, "path": args.path,
+                   "timing": args.mode, "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "kernel_ms": kernel_ms,
+        "algorithmic_bytes_per_step": abytes,
+        "sample_max_abs_err": max_err,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(p, cpu)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

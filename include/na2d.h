@@ -1,0 +1,126 @@
+/*
+ * na2d.h -- C ABI of libna2d: forward pass of 2D (dilated) Neighborhood
+ * Attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (NAT model doc, Overview; NAT repository README,
+ * introduction; DiNAT walk-through blog, section "What is DiNAT"):
+ * every query pixel attends to a k x k window of key pixels taken every d
+ * pixels (dilation d).  The window is placed inside the query's residue class
+ * (the pixels with the same row mod d and column mod d), centred on the query
+ * and shifted inward at the borders, so every query keeps exactly k*k
+ * neighbours.  Scores are q.k / sqrt(D) plus a per-head relative-position
+ * bias looked up by the key-minus-query offset counted in steps of d; a
+ * softmax over the k*k neighbours follows, then the probability-weighted sum
+ * of the value rows.  The blog's module code shows the decomposition this
+ * header mirrors: natten2dqkrpb -> softmax(dim=-1) -> natten2dav.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no memory and keeps no mutable global state.
+ *  - q, k, v and out are dense [B, heads, H, W, D] (D fastest) in `dtype`.
+ *  - rpb is dense [heads, 2k-1, 2k-1] in `dtype`; entry [h][dy+k-1][dx+k-1]
+ *    is the bias of a key dy window-steps below and dx steps right of the
+ *    query.  rpb == NULL means a zero bias.
+ *  - attn (the unfused path's score / probability tensor) is always fp32,
+ *    dense [B, heads, H, W, k*k]; neighbour slot n = a*k + c is window row a,
+ *    window column c.
+ *  - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *    returns without waiting.  A fault inside a kernel is reported by the
+ *    caller's next synchronisation, not by the return value.
+ *  - Outputs must not overlap inputs (except na2d_softmax, which may run in
+ *    place with attn_in == attn_out).
+ *  - Every argument check runs before any HIP call.  Calls are thread-safe.
+ *
+ * Status codes
+ * ------------
+ *  NA2D_ERROR_INVALID_VALUE: a size < 1; kernel_size even or < 1;
+ *    dilation < 1; H or W smaller than kernel_size * dilation (the caller must
+ *    pad such maps, as the DiNAT module's maybe_pad does); a required pointer
+ *    NULL or not 16-byte aligned; dtype or algorithm not in its enum;
+ *    overlapping output and input; B*heads*H*W*max(D, k*k) beyond 2^60.
+ *  NA2D_ERROR_NOT_SUPPORTED: a valid problem this build does not implement:
+ *    D != 32, kernel_size > 13, or more than 2^31-1 workgroups.
+ *  NA2D_ERROR_LAUNCH_FAILURE: the HIP runtime refused a launch.
+ */
+#ifndef NA2D_H
+#define NA2D_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NA2D_DTYPE_F32 = 0,
+    NA2D_DTYPE_BF16 = 1,
+    NA2D_DTYPE_F16 = 2
+} na2d_dtype_t;
+
+typedef enum {
+    NA2D_SUCCESS = 0,
+    NA2D_ERROR_INVALID_VALUE = 1,
+    NA2D_ERROR_NOT_SUPPORTED = 2,
+    NA2D_ERROR_LAUNCH_FAILURE = 3
+} na2d_status_t;
+
+/* Kernel family used by na2d_forward_algo. */
+typedef enum {
+    NA2D_ALGO_AUTO = 0, /* MFMA for bf16/fp16, FMA for fp32 */
+    NA2D_ALGO_FMA = 1,  /* one lane per query, scalar fp32 FMA, any dtype */
+    NA2D_ALGO_MFMA = 2  /* matrix-core kernel, bf16/fp16 only */
+} na2d_algo_t;
+
+/*
+ * Fused forward pass: out = softmax(q.k/sqrt(D) + rpb) . v over each query's
+ * dilated k x k window, in one kernel; the attention weights never reach
+ * memory.  Accumulation is fp32; out is rounded once to `dtype` (RNE).
+ */
+na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const void *rpb,
+                           void *out, int B, int heads, int H, int W, int D,
+                           int kernel_size, int dilation, na2d_dtype_t dtype,
+                           hipStream_t stream);
+
+/* na2d_forward with an explicit kernel family (NA2D_ALGO_MFMA with fp32 data
+ * returns NA2D_ERROR_NOT_SUPPORTED). */
+na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, const void *rpb,
+                                void *out, int B, int heads, int H, int W, int D,
+                                int kernel_size, int dilation, na2d_dtype_t dtype,
+                                na2d_algo_t algo, hipStream_t stream);
+
+/*
+ * Unfused step 1 (the blog's natten2dqkrpb): attn[b,h,i,j,n] =
+ * q[b,h,i,j].k[neighbour n] / sqrt(D) + rpb[h][offset of n], in fp32.
+ */
+na2d_status_t na2d_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
+                         int B, int heads, int H, int W, int D, int kernel_size,
+                         int dilation, na2d_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Unfused step 2 (softmax over the last axis): each row of k*k fp32 scores is
+ * replaced by exp(s - max) / sum.  attn_in == attn_out runs in place.
+ */
+na2d_status_t na2d_softmax(const float *attn_in, float *attn_out, int B, int heads, int H,
+                           int W, int kernel_size, hipStream_t stream);
+
+/*
+ * Unfused step 3 (the blog's natten2dav): out[b,h,i,j,:] =
+ * sum_n attn[b,h,i,j,n] * v[neighbour n, :], accumulated in fp32 and rounded
+ * once to `dtype`.
+ */
+na2d_status_t na2d_av(const float *attn, const void *v, void *out, int B, int heads, int H,
+                      int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
+                      hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *na2d_status_string(na2d_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int na2d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NA2D_H */

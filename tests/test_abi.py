@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/na2d.h declares, and rejects every invalid call with the documented
+status before touching the device (each call below is invalid in exactly one
+way, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from vision_transformer_local_amd import na2d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "na2d.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+F32, BF16, F16 = 0, 1, 2
+# fake, 16-byte aligned device addresses: never dereferenced because every
+# call made with them fails validation first
+P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(8)]
+NULL = ctypes.c_void_p(0)
+S = ctypes.c_void_p(0)  # stream
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(na2d_[a-z_]+)\s*\(", text)))
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(na2d.LIB_PATH)
+    na2d.lib()
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert {"na2d_forward", "na2d_qkrpb", "na2d_softmax", "na2d_av",
+            "na2d_status_string", "na2d_version", "na2d_forward_algo"} <= set(names)
+    L = na2d.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert na2d.na2d_version() >= 100
+    for code in range(4):
+        s = na2d.na2d_status_string(code)
+        assert s.startswith(["NA2D_SUCCESS", "NA2D_ERROR_INVALID_VALUE",
+                             "NA2D_ERROR_NOT_SUPPORTED", "NA2D_ERROR_LAUNCH_FAILURE"][code])
+    assert "unknown" in na2d.na2d_status_string(99)
+
+
+# (B, heads, H, W, D, k, d, dtype) -> expected status, with valid pointers
+FORWARD_CASES = [
+    ((0, 1, 14, 14, 32, 7, 1, BF16), INVALID),
+    ((1, 0, 14, 14, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 0, 14, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 14, -3, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 14, 14, 0, 7, 1, BF16), INVALID),
+    ((1, 1, 14, 14, 32, 6, 1, BF16), INVALID),    # even kernel
+    ((1, 1, 14, 14, 32, 0, 1, BF16), INVALID),
+    ((1, 1, 14, 14, 32, -1, 1, BF16), INVALID),
+    ((1, 1, 14, 14, 32, 7, 0, BF16), INVALID),    # dilation 0
+    ((1, 1, 13, 14, 32, 7, 2, BF16), INVALID),    # H < k*d
+    ((1, 1, 14, 13, 32, 7, 2, BF16), INVALID),    # W < k*d
+    ((1, 1, 6, 6, 32, 7, 1, BF16), INVALID),      # map smaller than the window
+    ((1, 1, 14, 14, 32, 7, 1, 3), INVALID),       # dtype outside the enum
+    ((1, 1, 14, 14, 32, 7, 1, -1), INVALID),
+    ((1 << 30, 1 << 30, 1 << 30, 1 << 30, 32, 7, 1, BF16), INVALID),  # > 2^60 elements
+    ((1 << 20, 1 << 10, 1 << 15, 1 << 15, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 14, 14, 64, 7, 1, BF16), UNSUPPORTED),   # D != 32
+    ((1, 1, 14, 14, 16, 7, 1, F32), UNSUPPORTED),
+    ((1, 1, 30, 30, 32, 15, 2, BF16), UNSUPPORTED),  # k > 13 (map fits 15*2)
+    ((1, 1, 30, 30, 32, 15, 1, BF16), UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("args,expect", FORWARD_CASES)
+def test_forward_validation(args, expect):
+    L = na2d.lib()
+    B, h, H, W, D, ks, d, dt = args
+    assert L.na2d_forward(P[0], P[1], P[2], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == expect
+    for algo in (0, 1, 2):
+        assert L.na2d_forward_algo(P[0], P[1], P[2], P[3], P[4], B, h, H, W, D, ks, d, dt,
+                                   algo, S) == expect
+    assert L.na2d_qkrpb(P[0], P[1], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == expect
+    assert L.na2d_av(P[4], P[2], P[5], B, h, H, W, D, ks, d, dt, S) == expect
+
+
+VALID = (1, 2, 14, 14, 32, 7, 1, BF16)
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 4])
+def test_forward_null_pointers(slot):
+    L = na2d.lib()
+    ptrs = list(P[:5])
+    ptrs[slot] = NULL
+    assert L.na2d_forward(*ptrs, *VALID, S) == INVALID
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 3, 4])
+def test_forward_misaligned_pointers(slot):
+    L = na2d.lib()
+    ptrs = list(P[:5])
+    ptrs[slot] = ctypes.c_void_p(ptrs[slot].value + 8)
+    assert L.na2d_forward(*ptrs, *VALID, S) == INVALID
+
+
+def test_forward_rejects_overlapping_output():
+    L = na2d.lib()
+    # out starts inside q
+    out = ctypes.c_void_p(P[0].value + 1024)
+    assert L.na2d_forward(P[0], P[1], P[2], P[3], out, *VALID, S) == INVALID
+    assert L.na2d_forward(P[0], P[1], P[2], P[3], P[0], *VALID, S) == INVALID
+
+
+def test_forward_rejects_bad_algo_and_mfma_fp32():
+    L = na2d.lib()
+    B, h, H, W, D, ks, d, _ = VALID
+    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, BF16, 3, S) == INVALID
+    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, BF16, -1, S) == INVALID
+    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, F32, 2, S) == UNSUPPORTED
+
+
+def test_qkrpb_and_av_pointer_rules():
+    L = na2d.lib()
+    B, h, H, W, D, ks, d, dt = VALID
+    assert L.na2d_qkrpb(NULL, P[1], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_qkrpb(P[0], NULL, P[3], P[4], B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_qkrpb(P[0], P[1], P[3], NULL, B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_qkrpb(P[0], P[1], P[3], P[0], B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_av(NULL, P[2], P[5], B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_av(P[4], NULL, P[5], B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_av(P[4], P[2], NULL, B, h, H, W, D, ks, d, dt, S) == INVALID
+    assert L.na2d_av(P[4], P[2], P[2], B, h, H, W, D, ks, d, dt, S) == INVALID
+    mis = ctypes.c_void_p(P[4].value + 4)
+    assert L.na2d_av(mis, P[2], P[5], B, h, H, W, D, ks, d, dt, S) == INVALID
+
+
+def test_softmax_rules():
+    L = na2d.lib()
+    assert L.na2d_softmax(NULL, P[1], 1, 1, 14, 14, 7, S) == INVALID
+    assert L.na2d_softmax(P[0], NULL, 1, 1, 14, 14, 7, S) == INVALID
+    assert L.na2d_softmax(P[0], P[1], 1, 1, 14, 14, 8, S) == INVALID
+    assert L.na2d_softmax(P[0], P[1], 0, 1, 14, 14, 7, S) == INVALID
+    assert L.na2d_softmax(P[0], P[1], 1, 1, 6, 14, 7, S) == INVALID
+    assert L.na2d_softmax(P[0], P[1], 1, 1, 30, 30, 15, S) == UNSUPPORTED
+    # partial overlap is rejected (full aliasing = in place is allowed)
+    part = ctypes.c_void_p(P[0].value + 64)
+    assert L.na2d_softmax(P[0], part, 1, 1, 14, 14, 7, S) == INVALID
+
+
+def test_binding_rejects_host_tensors_without_calling_the_library():
+    q = torch.zeros(1, 1, 14, 14, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        na2d.na2d_forward(q, q, q, None, torch.empty_like(q), 7, 1)
+
+
+def test_header_declares_extern_c_and_no_torch_types():
+    text = open(HEADER).read()
+    assert 'extern "C"' in text
+    for banned in ("at::", "torch::", "c10::", "#include <torch", "#include <ATen"):
+        assert banned not in text

@@ -1,0 +1,169 @@
+// na2d_api.hip -- the C ABI of libna2d: argument checking and dispatch.
+//
+// Every check runs before the first HIP call, so an invalid call has no side
+// effect on the device or the stream.  See include/na2d.h for the contract.
+#include "na2d_internal.h"
+
+#include <limits.h>
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 60;  // keeps byte counts (x4) in int64
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+  if (!a || !b) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t elem_bytes(na2d_dtype_t dt) { return dt == NA2D_DTYPE_F32 ? 4 : 2; }
+
+bool dtype_ok(int dt) {
+  return dt == NA2D_DTYPE_F32 || dt == NA2D_DTYPE_BF16 || dt == NA2D_DTYPE_F16;
+}
+
+// Checks shared by every entry point.  D < 0 means "no head dimension".
+na2d_status_t check_shape(int B, int heads, int H, int W, int D, int ks, int dil,
+                          na2d::Shape *s) {
+  if (B < 1 || heads < 1 || H < 1 || W < 1 || (D != -1 && D < 1)) return NA2D_ERROR_INVALID_VALUE;
+  if (ks < 1 || (ks % 2) == 0 || dil < 1) return NA2D_ERROR_INVALID_VALUE;
+  // The window must fit inside every residue class: H >= k*d (else pad).
+  if ((int64_t)ks * dil > H || (int64_t)ks * dil > W) return NA2D_ERROR_INVALID_VALUE;
+  // B*heads*H*W*max(D, k*k) must stay below 2^60; multiply step by step so
+  // the check itself cannot overflow.
+  const int64_t width = (int64_t)ks * ks > (D > 0 ? D : 1) ? (int64_t)ks * ks : (D > 0 ? D : 1);
+  int64_t nq = width;
+  const int64_t factors[4] = {B, heads, H, W};
+  for (int64_t f : factors) {
+    if (nq > kMaxElems / f) return NA2D_ERROR_INVALID_VALUE;
+    nq *= f;
+  }
+  nq /= width;
+  if (D != -1 && D != na2d::kHeadDim) return NA2D_ERROR_NOT_SUPPORTED;
+  if (ks > na2d::kMaxKernel) return NA2D_ERROR_NOT_SUPPORTED;
+  s->B = B; s->heads = heads; s->H = H; s->W = W; s->ks = ks; s->dil = dil; s->n_query = nq;
+  return NA2D_SUCCESS;
+}
+
+na2d_status_t from_hip(hipError_t e) {
+  if (e == hipSuccess) return NA2D_SUCCESS;
+  return e == hipErrorInvalidConfiguration ? NA2D_ERROR_NOT_SUPPORTED : NA2D_ERROR_LAUNCH_FAILURE;
+}
+
+}  // namespace
+
+extern "C" {
+
+na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, const void *rpb,
+                                void *out, int B, int heads, int H, int W, int D,
+                                int kernel_size, int dilation, na2d_dtype_t dtype,
+                                na2d_algo_t algo, hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_FMA && algo != NA2D_ALGO_MFMA)
+    return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!q || !k || !v || !out) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (rpb && !aligned16(rpb)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const int64_t tbytes = s.n_query * D * elem_bytes(dtype);
+  if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
+      overlaps(out, tbytes, v, tbytes))
+    return NA2D_ERROR_INVALID_VALUE;
+  if (rpb) {
+    const int64_t side = 2 * kernel_size - 1;
+    if (overlaps(out, tbytes, rpb, heads * side * side * elem_bytes(dtype)))
+      return NA2D_ERROR_INVALID_VALUE;
+  }
+  if (algo == NA2D_ALGO_AUTO) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
+  if (algo == NA2D_ALGO_MFMA) {
+    if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
+    bool supported = true;
+    hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, dtype, stream, &supported);
+    if (!supported) return NA2D_ERROR_NOT_SUPPORTED;
+    return from_hip(e);
+  }
+  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, dtype, stream));
+}
+
+na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const void *rpb,
+                           void *out, int B, int heads, int H, int W, int D,
+                           int kernel_size, int dilation, na2d_dtype_t dtype,
+                           hipStream_t stream) {
+  return na2d_forward_algo(q, k, v, rpb, out, B, heads, H, W, D, kernel_size, dilation, dtype,
+                           NA2D_ALGO_AUTO, stream);
+}
+
+na2d_status_t na2d_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
+                         int B, int heads, int H, int W, int D, int kernel_size,
+                         int dilation, na2d_dtype_t dtype, hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!q || !k || !attn) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(attn) || (rpb && !aligned16(rpb)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const int64_t tbytes = s.n_query * D * elem_bytes(dtype);
+  const int64_t abytes = s.n_query * kernel_size * kernel_size * 4;
+  if (overlaps(attn, abytes, q, tbytes) || overlaps(attn, abytes, k, tbytes))
+    return NA2D_ERROR_INVALID_VALUE;
+  if (rpb) {
+    const int64_t side = 2 * kernel_size - 1;
+    if (overlaps(attn, abytes, rpb, heads * side * side * elem_bytes(dtype)))
+      return NA2D_ERROR_INVALID_VALUE;
+  }
+  return from_hip(na2d::launch_qkrpb(q, k, rpb, attn, s, dtype, stream));
+}
+
+na2d_status_t na2d_softmax(const float *attn_in, float *attn_out, int B, int heads, int H,
+                           int W, int kernel_size, hipStream_t stream) {
+  na2d::Shape s;
+  // Rows only need the window to be well formed; dilation plays no role here.
+  na2d_status_t st = check_shape(B, heads, H, W, -1, kernel_size, 1, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!attn_in || !attn_out) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(attn_in) || !aligned16(attn_out)) return NA2D_ERROR_INVALID_VALUE;
+  const int64_t abytes = s.n_query * kernel_size * kernel_size * 4;
+  if (attn_in != attn_out && overlaps(attn_in, abytes, attn_out, abytes))
+    return NA2D_ERROR_INVALID_VALUE;
+  return from_hip(na2d::launch_softmax(attn_in, attn_out, s, stream));
+}
+
+na2d_status_t na2d_av(const float *attn, const void *v, void *out, int B, int heads, int H,
+                      int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
+                      hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!attn || !v || !out) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(attn) || !aligned16(v) || !aligned16(out)) return NA2D_ERROR_INVALID_VALUE;
+  const int64_t tbytes = s.n_query * D * elem_bytes(dtype);
+  const int64_t abytes = s.n_query * kernel_size * kernel_size * 4;
+  if (overlaps(out, tbytes, v, tbytes) || overlaps(out, tbytes, attn, abytes))
+    return NA2D_ERROR_INVALID_VALUE;
+  return from_hip(na2d::launch_av(attn, v, out, s, dtype, stream));
+}
+
+const char *na2d_status_string(na2d_status_t status) {
+  switch (status) {
+    case NA2D_SUCCESS: return "NA2D_SUCCESS: no error";
+    case NA2D_ERROR_INVALID_VALUE:
+      return "NA2D_ERROR_INVALID_VALUE: invalid argument (sizes, kernel_size, dilation, "
+             "map smaller than kernel_size*dilation, NULL/unaligned pointer, dtype, overlap)";
+    case NA2D_ERROR_NOT_SUPPORTED:
+      return "NA2D_ERROR_NOT_SUPPORTED: valid but not implemented (D != 32, kernel_size > 13, "
+             "MFMA with fp32, or grid too large)";
+    case NA2D_ERROR_LAUNCH_FAILURE: return "NA2D_ERROR_LAUNCH_FAILURE: kernel launch failed";
+  }
+  return "unknown na2d status";
+}
+
+int na2d_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// na2d_internal.h -- helpers shared by the kernels of libna2d (gfx950 only).
+//
+// Index conventions (NAT repository README, introduction: edge pixels are
+// special cases; DiNAT walk-through blog, "What is DiNAT": dilation d samples
+// every d-th pixel and keeps k*k tokens):
+//   a pixel row i belongs to residue class ry = i % d at sub-grid row ci = i / d;
+//   that class has Ly = ceil((H - ry) / d) rows;
+//   the query's window covers sub-grid rows [sy, sy + k) with
+//   sy = clamp(ci - k/2, 0, Ly - k)  (centred, shifted inward at the borders);
+//   the same holds for columns.
+// All kernels below work in these sub-grid coordinates and translate to
+// pixel rows ry + d * row only when they touch memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/na2d.h"
+
+namespace na2d {
+
+constexpr int kHeadDim = 32;      // D supported by this build
+constexpr int kMaxKernel = 13;    // largest supported kernel_size
+constexpr float kLog2e = 1.4426950408889634f;
+
+__host__ __device__ __forceinline__ int window_start(int c, int len, int ks) {
+  int s = c - ks / 2;
+  s = s < 0 ? 0 : s;
+  return s > len - ks ? len - ks : s;
+}
+
+__host__ __device__ __forceinline__ int class_len(int n, int residue, int dil) {
+  return (n - residue + dil - 1) / dil;
+}
+
+// Element traits: load widening to fp32 and RNE narrowing on store.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+};
+template <> struct Elem<__bf16> {
+  static __device__ __forceinline__ float to_f(__bf16 x) { return static_cast<float>(x); }
+  static __device__ __forceinline__ __bf16 from_f(float x) { return static_cast<__bf16>(x); }
+};
+template <> struct Elem<_Float16> {
+  static __device__ __forceinline__ float to_f(_Float16 x) { return static_cast<float>(x); }
+  static __device__ __forceinline__ _Float16 from_f(float x) { return static_cast<_Float16>(x); }
+};
+
+// Workgroups of one dispatch are handed to the 8 XCDs of the chip
+// round-robin (id % 8).  Renumber them so that each XCD receives one
+// contiguous run of logical ids: neighbouring tiles, which share halo rows
+// and (for d > 1) cache lines of adjacent residue classes, then meet in the
+// same L2.
+__device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
+  constexpr int kXcds = 8;
+  const int per = n / kXcds, rem = n % kXcds;
+  const int x = bid % kXcds, slot = bid / kXcds;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+// Problem description passed by value to every kernel.
+struct Shape {
+  int B, heads, H, W, ks, dil;
+  int64_t n_query;  // B * heads * H * W
+};
+
+// Launchers (one per kernel family); each returns hipSuccess or the launch
+// error.  Argument checking happens before these are reached.
+hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
+                            void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st);
+hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
+                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             bool *supported);
+hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
+                        const Shape &s, na2d_dtype_t dt, hipStream_t st);
+hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);
+hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s,
+                     na2d_dtype_t dt, hipStream_t st);
+
+}  // namespace na2d

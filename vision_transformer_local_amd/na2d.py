@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libna2d (the C ABI in include/na2d.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, their device pointers and torch's current HIP stream are passed to the
+library, and a non-zero status becomes a RuntimeError.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, the first call raises.
+
+Layouts: q, k, v, out are contiguous [B, heads, H, W, D] on the GPU in one of
+float32 / bfloat16 / float16; rpb is [heads, 2k-1, 2k-1] in the same dtype or
+None (zero bias); attn is float32 [B, heads, H, W, k*k].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libna2d.so")
+
+SUCCESS, INVALID_VALUE, NOT_SUPPORTED, LAUNCH_FAILURE = 0, 1, 2, 3
+ALGOS = {"auto": 0, "fma": 1, "mfma": 2}
+_DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+_lib = None
+
+
+class Na2dError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libna2d.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libna2d.so is not built (%s); run `python -m vision_transformer_local_amd.build`"
+                % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        L.na2d_forward.restype = i
+        L.na2d_forward.argtypes = [vp] * 5 + [i] * 8 + [vp]
+        L.na2d_forward_algo.restype = i
+        L.na2d_forward_algo.argtypes = [vp] * 5 + [i] * 9 + [vp]
+        L.na2d_qkrpb.restype = i
+        L.na2d_qkrpb.argtypes = [vp] * 4 + [i] * 8 + [vp]
+        L.na2d_softmax.restype = i
+        L.na2d_softmax.argtypes = [vp] * 2 + [i] * 5 + [vp]
+        L.na2d_av.restype = i
+        L.na2d_av.argtypes = [vp] * 3 + [i] * 8 + [vp]
+        L.na2d_status_string.restype = ctypes.c_char_p
+        L.na2d_status_string.argtypes = [i]
+        L.na2d_version.restype = i
+        L.na2d_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def na2d_status_string(status: int) -> str:
+    return lib().na2d_status_string(int(status)).decode()
+
+
+def na2d_version() -> int:
+    return int(lib().na2d_version())
+
+
+def _check(status: int, what: str):
+    if status != SUCCESS:
+        raise Na2dError(status, "%s: %s" % (what, na2d_status_string(status)))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _qkv_shape(q: torch.Tensor):
+    if q.dim() != 5:
+        raise ValueError("q must be [B, heads, H, W, D]")
+    if q.dtype not in _DTYPE_CODES:
+        raise ValueError("dtype %s not supported" % q.dtype)
+    return tuple(int(x) for x in q.shape)
+
+
+def _rpb_check(rpb, q, heads, ks):
+    if rpb is not None:
+        side = 2 * ks - 1
+        _need(rpb, "rpb", q.dtype, (heads, side, side))
+
+
+def na2d_forward_algo(q, k, v, rpb, out, kernel_size: int, dilation: int, algo: str = "auto"):
+    """Fused forward into ``out`` with an explicit kernel family."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    st = lib().na2d_forward_algo(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out),
+                                 B, heads, H, W, D, int(kernel_size), int(dilation),
+                                 _DTYPE_CODES[q.dtype], ALGOS[algo], _stream(q))
+    _check(st, "na2d_forward_algo")
+    return out
+
+
+def na2d_forward(q, k, v, rpb, out, kernel_size: int, dilation: int):
+    """Fused forward into ``out`` (MFMA kernel for bf16/fp16, FMA for fp32)."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    st = lib().na2d_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out),
+                            B, heads, H, W, D, int(kernel_size), int(dilation),
+                            _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_forward")
+    return out
+
+
+def na2d_qkrpb(q, k, rpb, attn, kernel_size: int, dilation: int):
+    """Unfused step 1: fp32 scores q.k/sqrt(D) + bias into ``attn``."""
+    B, heads, H, W, D = _qkv_shape(q)
+    _need(q, "q")
+    _need(k, "k", q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    _need(attn, "attn", torch.float32, (B, heads, H, W, kernel_size * kernel_size))
+    st = lib().na2d_qkrpb(_ptr(q), _ptr(k), _ptr(rpb), _ptr(attn), B, heads, H, W, D,
+                          int(kernel_size), int(dilation), _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_qkrpb")
+    return attn
+
+
+def na2d_softmax(attn_in, attn_out, kernel_size: int):
+    """Unfused step 2: row softmax over the last (k*k) axis; may run in place."""
+    _need(attn_in, "attn_in", torch.float32)
+    if attn_in.dim() != 5 or attn_in.shape[-1] != kernel_size * kernel_size:
+        raise ValueError("attn must be [B, heads, H, W, k*k]")
+    _need(attn_out, "attn_out", torch.float32, attn_in.shape)
+    B, heads, H, W, _ = (int(x) for x in attn_in.shape)
+    st = lib().na2d_softmax(_ptr(attn_in), _ptr(attn_out), B, heads, H, W, int(kernel_size),
+                            _stream(attn_in))
+    _check(st, "na2d_softmax")
+    return attn_out
+
+
+def na2d_av(attn, v, out, kernel_size: int, dilation: int):
+    """Unfused step 3: probability-weighted sum of value rows into ``out``."""
+    B, heads, H, W, D = _qkv_shape(v)
+    _need(v, "v")
+    _need(attn, "attn", torch.float32, (B, heads, H, W, kernel_size * kernel_size))
+    _need(out, "out", v.dtype, v.shape)
+    st = lib().na2d_av(_ptr(attn), _ptr(v), _ptr(out), B, heads, H, W, D, int(kernel_size),
+                       int(dilation), _DTYPE_CODES[v.dtype], _stream(v))
+    _check(st, "na2d_av")
+    return out
+
+
+# -- allocating conveniences (torch allocates the outputs; nothing else) ----
+
+def forward(q, k, v, rpb, kernel_size: int, dilation: int, algo: str = "auto"):
+    out = torch.empty_like(q)
+    return na2d_forward_algo(q, k, v, rpb, out, kernel_size, dilation, algo)
+
+
+def forward_unfused(q, k, v, rpb, kernel_size: int, dilation: int):
+    B, heads, H, W, _ = q.shape
+    attn = torch.empty((B, heads, H, W, kernel_size * kernel_size), dtype=torch.float32,
+                       device=q.device)
+    na2d_qkrpb(q, k, rpb, attn, kernel_size, dilation)
+    na2d_softmax(attn, attn, kernel_size)
+    out = torch.empty_like(v)
+    na2d_av(attn, v, out, kernel_size, dilation)
+    return out
