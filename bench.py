@@ -116,6 +116,8 @@ def main(argv=None):
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -130,9 +132,20 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
-    p = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the factor that turns those counters into bytes.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": max(1, args.steps)}))
+        return 0
+    p = WORKLOADS[args.workload]
     L = na2d.lib()
 
     cpu = I.make_inputs(p, seed=0)

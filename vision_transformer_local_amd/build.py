@@ -28,6 +28,9 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA sources/results in VGPRs: the AGPR form round-trips every
+    # score block through v_accvgpr moves and serialises the MFMAs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

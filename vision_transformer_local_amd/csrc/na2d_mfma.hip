@@ -10,22 +10,26 @@
 //   * Everything is expressed in residue-class (sub-grid) coordinates: with
 //     dilation d, the pixels (ry + d*ci, rx + d*cj) of one class (ry, rx) form
 //     an ordinary map on which the operator is plain neighborhood attention.
-//   * A workgroup (4 waves) owns an RY x RX block of one class of one
-//     (batch, head) plane.  It stages the block's key/value halo -- the union
-//     of its queries' clamped windows, at most (RY+k-1) x (RX+k) sub-grid
-//     pixels -- in LDS once: K row-major (16-byte chunks swizzled against bank
-//     conflicts), V transposed to [channel][pixel] so that the matrix cores can
-//     contract over pixels.
+//   * A workgroup owns an RY x RX block of one class of one (batch, head)
+//     plane.  It stages the block's key/value halo -- the union of its
+//     queries' clamped windows, at most (RY+k-1) x (RX+k) sub-grid pixels --
+//     in LDS once: K as [row][col] 64-byte pixels (16-byte chunks swizzled by
+//     column against bank conflicts) and V transposed to [row][channel][col]
+//     so the matrix cores can contract over pixels.  The LDS strides are
+//     compile-time constants; rows past the staged halo are zero-filled, so
+//     every LDS address in the tile loop is a per-lane base plus an immediate
+//     offset and no index is clamped.
 //   * A wave processes 16-query tiles (TY x TX sub-grid pixels).  The tile's
 //     keys are NB = TY + k - 1 halo rows x 16 columns (the columns start at an
 //     even LDS column so V reads are dword aligned).  Scores are produced
-//     transposed, S^T = K . Q^T, one v_mfma_f32_16x16x32 per halo row, so that
+//     transposed, S^T = K . Q^T, one v_mfma_f32_16x16x32 per halo row, so
 //     each lane ends up holding scores of ONE query: the softmax reductions
-//     need only two cross-lane steps, and the probabilities are already laid
-//     out as the B operand of the second product out^T = V^T . P^T.
+//     need two lane swaps, and the probabilities are already laid out as the
+//     B operand of the second product out^T = V^T . P^T.
 //   * The relative-position bias (pre-multiplied by sqrt(D)) and the window
 //     mask (-inf outside the query's clamped window) enter as the accumulator
-//     input of the score MFMA, so they cost no extra pass over the scores.
+//     input of the score MFMA.  For tiles whose windows are all unclamped this
+//     input is the same for every tile of the workgroup and is computed once.
 #include "na2d_internal.h"
 
 #include <limits.h>
@@ -57,14 +61,13 @@ template <> struct Mma<_Float16> {
 template <int KS> struct Geometry {
   static constexpr int TY = KS <= 7 ? 2 : (KS <= 11 ? 4 : 8);  // tile rows
   static constexpr int TX = 16 / TY;                           // tile columns
-  static constexpr int RY = KS <= 11 ? 8 : 16;                 // block rows per workgroup
-  static constexpr int RX = KS <= 7 ? 32 : (KS <= 11 ? 16 : 8);  // block columns
-  static constexpr int NB = TY + KS - 1;                       // key rows per tile (even)
-  static constexpr int HRM = RY + KS - 1;                      // staged rows (max)
-  static constexpr int HCM = (RX + KS + 1) & ~1;               // staged columns (max, even)
-  // V^T channel stride in elements; an odd number of dwords spreads the 16
-  // channels one wave reads over distinct banks.
-  static constexpr int CSTR = (HRM * HCM) % 4 == 2 ? HRM * HCM : HRM * HCM + 2;
+  static constexpr int RY = KS <= 7 ? 14 : (KS <= 11 ? 8 : 16);  // block rows
+  static constexpr int RX = KS <= 7 ? 8 : (KS <= 11 ? 8 : 4);    // block columns
+  static constexpr int NB = TY + KS - 1;          // key rows per tile (even)
+  static constexpr int HRM = RY + KS - 1;         // halo rows (max)
+  static constexpr int HCM = (RX + KS + 1) & ~1;  // halo columns (max, even)
+  static constexpr int ROWS = HRM + TY;           // LDS rows incl. zero rows read by tiles
+  static constexpr int COLS = HCM % 4 == 2 ? HCM : HCM + 2;  // odd dword count per V^T row
   static constexpr int SIDE = 2 * KS - 1;
   static constexpr int MARGIN = TY * SIDE + 32;  // keeps masked bias reads in bounds
   static_assert(TX + KS <= 16, "key columns do not cover the tile");
@@ -72,7 +75,16 @@ template <int KS> struct Geometry {
 };
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr float kSqrtD = 5.656854249492380f;  // sqrt(32)
+
+// Maximum over the 4 lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <typename T, int KS>
 __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
@@ -81,12 +93,14 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
   using G = Geometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int TY = G::TY, TX = G::TX, RY = G::RY, RX = G::RX, NB = G::NB;
-  constexpr int SIDE = G::SIDE, MARGIN = G::MARGIN, CSTR = G::CSTR;
+  constexpr int SIDE = G::SIDE, MARGIN = G::MARGIN, ROWS = G::ROWS, COLS = G::COLS;
+  constexpr int HCM = G::HCM;
   constexpr int D = kHeadDim;
+  constexpr int VROW = D * COLS / 2;  // dwords per V^T row
 
-  __shared__ u32x4 k_lds[G::HRM * G::HCM * 4];      // [pixel][chunk^swz] 16 B chunks
-  __shared__ unsigned int vt_lds[D * CSTR / 2];     // [channel][pixel pair]
-  __shared__ float b_lds[SIDE * SIDE + 2 * MARGIN]; // bias * sqrt(D), zero margins
+  __shared__ u32x4 k_lds[ROWS * HCM * 4];            // [row][col][chunk ^ swz]
+  __shared__ unsigned int vt_lds[ROWS * VROW];       // [row][channel][col pair]
+  __shared__ float b_lds[SIDE * SIDE + 2 * MARGIN];  // bias * sqrt(D), zero margins
 
   const int tid = threadIdx.x;
   const int dil = s.dil;
@@ -107,15 +121,80 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
   const int rc1 = min(rc0 + RY, Ly), cc1 = min(cc0 + RX, Lx);
   // Halo = union of the block's windows (window starts are monotone).
   const int hy0 = window_start(rc0, Ly, KS), hy1 = window_start(rc1 - 1, Ly, KS) + KS;
-  const int hx0 = window_start(cc0, Lx, KS), hx1 = window_start(cc1 - 1, Lx, KS) + KS;
+  const int hx0 = window_start(cc0, Lx, KS);
   const int hx0e = hx0 & ~1;  // even LDS column origin
-  const int HR = hy1 - hy0, HC = (hx1 - hx0e + 1) & ~1;
+  const int HR = hy1 - hy0;
 
   const int64_t hw = (int64_t)s.H * s.W;
   const T *kp = k + plane * hw * D;
   const T *vp = v + plane * hw * D;
 
   // ---- stage bias, K and V^T -------------------------------------------
+  // Each thread owns one (column, 16-byte chunk) slot of a halo row and walks
+  // down the rows, so a load address is a uniform base plus a 32-bit offset
+  // that grows by one uniform row stride per pass.  All global loads of the
+  // workgroup are issued before any of them is consumed, so their latencies
+  // overlap.  Rows past the halo (up to ROWS) are written as zeros.
+  constexpr int KIPR = HCM * 4;             // K chunks per halo row
+  constexpr int KRP = kThreads / KIPR;      // K rows per pass
+  constexpr int KPASS = (ROWS + KRP - 1) / KRP;
+  constexpr int VIPR = (COLS / 2) * 4;      // V (pixel pair, chunk) items per row
+  constexpr int VRP = kThreads / VIPR;      // V rows per pass
+  constexpr int VPASS = (ROWS + VRP - 1) / VRP;
+  constexpr int NTY = (RY + TY - 1) / TY, NTX = (RX + TX - 1) / TX;  // tile grid of a block
+  constexpr int NTILE = NTY * NTX;
+  constexpr int QIT = (NTILE + kWaves - 1) / kWaves;  // Q tiles per wave
+  static_assert(KRP >= 1 && VRP >= 1, "halo row wider than the workgroup");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 15, g = lane >> 4;
+  const int qy = ql / TX, qx = ql % TX;
+  const int nty = (rc1 - rc0 + TY - 1) / TY, ntx = (cc1 - cc0 + TX - 1) / TX;
+
+  // uniform: pixel of halo row 0, LDS column 0 (sub-grid (hy0, hx0e)), in bytes
+  const int64_t org = (int64_t)(ry + hy0 * dil) * s.W + rx + hx0e * dil;
+  const char *kb0 = (const char *)(kp + org * D);
+  const char *vb0 = (const char *)(vp + org * D);
+  const unsigned rowb = (unsigned)dil * (unsigned)s.W * (unsigned)(D * sizeof(T));
+  const unsigned colb = (unsigned)dil * (unsigned)(D * sizeof(T));
+  const int cmax = Lx - 1 - hx0e;  // last real column, relative to the LDS origin
+
+  const int kr0 = min(tid / KIPR, KRP - 1), kcol = (tid % KIPR) >> 2, kch = tid & 3;
+  const bool kact = tid < KRP * KIPR;
+  const unsigned koff = (unsigned)min(kcol, cmax) * colb + kch * 16;
+  // Loads are unconditional (rows clamped into the halo) so that they form
+  // one straight-line batch; the LDS writes below decide data versus zero.
+  u32x4 kreg[KPASS];
+  {
+    const unsigned first = koff + (unsigned)kr0 * rowb, last = koff + (unsigned)(HR - 1) * rowb;
+#pragma unroll
+    for (int it = 0; it < KPASS; ++it)
+      kreg[it] = *(const u32x4 *)(kb0 + min(first + (unsigned)(it * KRP) * rowb, last));
+  }
+  const int vr0 = min(tid / VIPR, VRP - 1), vpair = (tid % VIPR) >> 2, vch = tid & 3;
+  const bool vact = tid < VRP * VIPR;
+  const unsigned voff0 = (unsigned)min(2 * vpair, cmax) * colb + vch * 16;
+  const unsigned voff1 = (unsigned)min(2 * vpair + 1, cmax) * colb + vch * 16;
+  u32x4 va[VPASS], vbr[VPASS];
+  {
+    const unsigned r0 = (unsigned)vr0 * rowb, rl = (unsigned)(HR - 1) * rowb;
+#pragma unroll
+    for (int it = 0; it < VPASS; ++it) {
+      const unsigned ro = min(r0 + (unsigned)(it * VRP) * rowb, rl);
+      va[it] = *(const u32x4 *)(vb0 + (voff0 + ro));
+      vbr[it] = *(const u32x4 *)(vb0 + (voff1 + ro));
+    }
+  }
+  // this wave's query rows, one 16-byte slice per lane and tile
+  u32x4 qreg[QIT];
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int tile = min(wave + it * kWaves, NTILE - 1);
+    const int ty = tile / NTX, tx = tile % NTX;
+    const int ci = min(rc0 + ty * TY + qy, rc1 - 1), cj = min(cc0 + tx * TX + qx, cc1 - 1);
+    qreg[it] = *(const u32x4 *)(q + plane * hw * D +
+                                ((int64_t)(ry + ci * dil) * s.W + rx + cj * dil) * D + g * 8);
+  }
+
   for (int e = tid; e < SIDE * SIDE + 2 * MARGIN; e += kThreads) {
     const int t = e - MARGIN;
     float b = 0.f;
@@ -123,101 +202,124 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
       b = Elem<T>::to_f(rpb[(int64_t)h * SIDE * SIDE + t]) * kSqrtD;
     b_lds[e] = b;
   }
-  const int nkeys = HR * HC;
-  for (int e = tid; e < nkeys * 4; e += kThreads) {
-    const int key = e >> 2, ch = e & 3;
-    const int row = key / HC, col = key - row * HC;
-    const int gy = ry + (hy0 + row) * dil;
-    const int gx = rx + min(hx0e + col, Lx - 1) * dil;
-    k_lds[key * 4 + (ch ^ ((key >> 1) & 3))] =
-        *(const u32x4 *)(kp + ((int64_t)gy * s.W + gx) * D + ch * 8);
-  }
-  for (int e = tid; e < nkeys * 2; e += kThreads) {  // (nkeys/2 pairs) x 4 chunks
-    const int pr = e >> 2, ch = e & 3;
-    const int key0 = pr * 2;
-    const int row = key0 / HC, col = key0 - row * HC;
-    const int64_t rowoff = (int64_t)(ry + (hy0 + row) * dil) * s.W;
-    const int gx0 = rx + min(hx0e + col, Lx - 1) * dil;
-    const int gx1 = rx + min(hx0e + col + 1, Lx - 1) * dil;
-    const u32x4 a = *(const u32x4 *)(vp + (rowoff + gx0) * D + ch * 8);
-    const u32x4 b = *(const u32x4 *)(vp + (rowoff + gx1) * D + ch * 8);
-    unsigned int *dst = vt_lds + (ch * 8) * (CSTR / 2) + (key0 >> 1);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  {
+    u32x4 *dst = k_lds + (kr0 * HCM + kcol) * 4 + (kch ^ ((kcol >> 1) & 3));
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {  // dword w of a chunk = channels 2w, 2w+1
-      dst[(2 * w) * (CSTR / 2)] = (a[w] & 0xffffu) | (b[w] << 16);
-      dst[(2 * w + 1) * (CSTR / 2)] = (a[w] >> 16) | (b[w] & 0xffff0000u);
+    for (int it = 0; it < KPASS; ++it) {
+      const int row = kr0 + it * KRP;
+      if (kact && row < ROWS) dst[it * KRP * HCM * 4] = row < HR ? kreg[it] : zero4;
+    }
+  }
+  {
+    unsigned int *dst = vt_lds + vr0 * VROW + (vch * 8) * (COLS / 2) + vpair;
+#pragma unroll
+    for (int it = 0; it < VPASS; ++it) {
+      const int row = vr0 + it * VRP;
+      if (vact && row < ROWS) {
+        const u32x4 a = row < HR ? va[it] : zero4, b = row < HR ? vbr[it] : zero4;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // dword w of a chunk = channels 2w, 2w+1
+          dst[it * VRP * VROW + (2 * w) * (COLS / 2)] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
+          dst[it * VRP * VROW + (2 * w + 1) * (COLS / 2)] =
+              __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
+        }
+      }
     }
   }
   __syncthreads();
 
   // ---- 16-query tiles ----------------------------------------------------
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ql = lane & 15, g = lane >> 4;
-  const int nty = (rc1 - rc0 + TY - 1) / TY, ntx = (cc1 - cc0 + TX - 1) / TX;
   const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
-  const int chA = 8 * (ql >> 2) + (ql & 3);  // V^T row of this lane (+4 for block 1)
+  const int chA = 8 * (ql >> 2) + (ql & 3);  // V^T channel of this lane (+4 for block 1)
+  vec ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
+  constexpr int R = KS / 2;
 
-  for (int tile = wave; tile < nty * ntx; tile += kThreads / 64) {
-    const int ty = tile / ntx, tx = tile - ty * ntx;
+  // Accumulator input for tiles whose 16 windows are all unclamped: the mask
+  // and bias then depend only on the lane, and on the (per-block constant)
+  // parity shift dlt between the tile's first window column and its even
+  // LDS column.
+  const int dlt = ((cc0 - R) - hx0e) & 1;
+  f32x4 cint[NB];
+  {
+    const int rowrel = -qy, colrel = 4 * g - dlt - qx;
+    const int bb = MARGIN + (R - qy) * SIDE + (4 * g - dlt - qx + R);
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (unsigned)(rowrel + a) < (unsigned)KS &&
+                        (unsigned)(colrel + i) < (unsigned)KS;
+        cint[a][i] = ok ? b_lds[bb + a * SIDE + i] : -INFINITY;
+      }
+  }
+
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int tile = wave + it * kWaves;
+    if (tile >= NTILE) break;
+    const int ty = tile / NTX, tx = tile % NTX;
+    if (ty >= nty || tx >= ntx) continue;  // tile outside a ragged block
     const int tci0 = rc0 + ty * TY, tcj0 = cc0 + tx * TX;
-    int ci = tci0 + ql / TX, cj = tcj0 + ql % TX;
+    int ci = tci0 + qy, cj = tcj0 + qx;
     const bool valid = ci < rc1 && cj < cc1;
     ci = min(ci, rc1 - 1);  // ragged tile: recompute a real query, store nothing
     cj = min(cj, cc1 - 1);
-    const int sy = window_start(ci, Ly, KS), sx = window_start(cj, Lx, KS);
     const int Y0 = window_start(tci0, Ly, KS), X0 = window_start(tcj0, Lx, KS);
     const int X0a = X0 - ((X0 - hx0e) & 1);  // even LDS column
     const int lrow0 = Y0 - hy0, lcol0 = X0a - hx0e;
 
     const int64_t qoff =
         plane * hw * D + ((int64_t)(ry + ci * dil) * s.W + rx + cj * dil) * D + g * 8;
-    const vec qv = __builtin_bit_cast(vec, *(const u32x4 *)(q + qoff));
+    const vec qv = __builtin_bit_cast(vec, qreg[it]);
 
     // S^T rows: key (Y0 + a, X0a + 4g + i) against query ql, i = 0..3.
-    const int rowrel = Y0 - sy, colrel = X0a + 4 * g - sx;
-    const int bbase = MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0a + 4 * g - cj + KS - 1);
+    const int kcol = lcol0 + ql;
+    const u32x4 *kb = k_lds + (lrow0 * HCM + kcol) * 4 + (g ^ ((kcol >> 1) & 3));
     f32x4 sc[NB];
+    const bool interior = tci0 - R >= 0 && tci0 + TY - 1 + R <= Ly - 1 && tcj0 - R >= 0 &&
+                          tcj0 + TX - 1 + R <= Lx - 1;
+    if (interior) {
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const bool rok = (unsigned)(rowrel + a) < (unsigned)KS;
-      f32x4 cinit;
+      for (int a = 0; a < NB; ++a)
+        sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, cint[a]);
+    } else {
+      const int sy = window_start(ci, Ly, KS), sx = window_start(cj, Lx, KS);
+      const int rowrel = Y0 - sy, colrel = X0a + 4 * g - sx;
+      const int bb = MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0a + 4 * g - cj + KS - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = rok && (unsigned)(colrel + i) < (unsigned)KS;
-        const float b = b_lds[bbase + a * SIDE + i];
-        cinit[i] = ok ? b : -INFINITY;
+      for (int a = 0; a < NB; ++a) {
+        f32x4 c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (unsigned)(rowrel + a) < (unsigned)KS &&
+                          (unsigned)(colrel + i) < (unsigned)KS;
+          c[i] = ok ? b_lds[bb + a * SIDE + i] : -INFINITY;
+        }
+        sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
       }
-      const int lr = min(lrow0 + a, HR - 1), lc = min(lcol0 + ql, HC - 1);
-      const int key = lr * HC + lc;
-      const vec kv = __builtin_bit_cast(vec, k_lds[key * 4 + (g ^ ((key >> 1) & 3))]);
-      sc[a] = Mma<T>::run(kv, qv, cinit);
     }
 
-    // softmax over the query's k*k keys: 4 lane groups hold disjoint keys
+    // softmax over the query's k*k keys: the 4 lane groups hold disjoint keys
     float mx = -INFINITY;
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = group_max(mx);
     const float mc = mx * c2;
-    float l = 0.f;
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
-        sc[a][i] = p;
-        l += p;
-      }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+      for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
 
-    // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA)
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
-    const int colA = lcol0 + 4 * g;
-    const int c01 = min(colA, HC - 2), c23 = min(colA + 2, HC - 2);
+    // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA); a third
+    // product against an all-ones matrix gives every lane its query's
+    // denominator, summed over exactly the 16-bit weights used above.
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
+    const unsigned int *vb = vt_lds + lrow0 * VROW + chA * (COLS / 2) + ((lcol0 + 4 * g) >> 1);
 #pragma unroll
     for (int j = 0; j < NB / 2; ++j) {
       vec pb;
@@ -226,20 +328,19 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         pb[i] = static_cast<T>(sc[2 * j][i]);
         pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
       }
-      const int r0 = min(lrow0 + 2 * j, HR - 1), r1 = min(lrow0 + 2 * j + 1, HR - 1);
-      const int k00 = (r0 * HC + c01) >> 1, k01 = (r0 * HC + c23) >> 1;
-      const int k10 = (r1 * HC + c01) >> 1, k11 = (r1 * HC + c23) >> 1;
-      const unsigned int *v0 = vt_lds + chA * (CSTR / 2);
-      const unsigned int *v1 = vt_lds + (chA + 4) * (CSTR / 2);
-      const u32x4 w0 = {v0[k00], v0[k01], v0[k10], v0[k11]};
-      const u32x4 w1 = {v1[k00], v1[k01], v1[k10], v1[k11]};
+      const unsigned int *r0 = vb + (2 * j) * VROW, *r1 = r0 + VROW;
+      constexpr int C4 = 4 * (COLS / 2);  // channel + 4
+      const u32x4 w0 = {r0[0], r0[1], r1[0], r1[1]};
+      const u32x4 w1 = {r0[C4], r0[C4 + 1], r1[C4], r1[C4 + 1]};
       o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
       o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
+      o2 = Mma<T>::run(ones, pb, o2);
     }
+    const float l = o2[0];
 
     // lane holds channels 8g..8g+3 (o0) and 8g+4..8g+7 (o1) of query ql
     if (valid) {
-      const float inv = 1.0f / l;
+      const float inv = __builtin_amdgcn_rcpf(l);
       vec res;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
