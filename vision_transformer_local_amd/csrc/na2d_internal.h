@@ -60,6 +60,25 @@ __device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Division by a divisor fixed at launch: n / d == (umulhi(n, mul) + n) >> shr
+// for 0 <= n < 2^31 (round-up multiplier method of Granlund and Montgomery,
+// "Division by invariant integers using multiplication", 1994).  Replaces
+// the ~40-instruction scalar division sequence in workgroup-id decoding.
+struct FastDiv {
+  uint32_t div, mul, shr;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.mul) + n) >> f.shr;
+}
+
 // Problem description passed by value to every kernel.
 struct Shape {
   int B, heads, H, W, ks, dil;

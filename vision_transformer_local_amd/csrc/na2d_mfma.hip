@@ -61,8 +61,10 @@ template <> struct Mma<_Float16> {
 template <int KS> struct Geometry {
   static constexpr int TY = KS <= 7 ? 2 : (KS <= 11 ? 4 : 8);  // tile rows
   static constexpr int TX = 16 / TY;                           // tile columns
-  static constexpr int RY = KS <= 7 ? 14 : (KS <= 11 ? 8 : 16);  // block rows
+  static constexpr int RY = KS <= 7 ? 28 : (KS <= 11 ? 8 : 16);  // block rows
   static constexpr int RX = KS <= 7 ? 8 : (KS <= 11 ? 8 : 4);    // block columns
+  static constexpr int THREADS = KS <= 7 ? 512 : 256;            // workgroup size
+  static constexpr int WAVES = THREADS / 64;
   static constexpr int NB = TY + KS - 1;          // key rows per tile (even)
   static constexpr int HRM = RY + KS - 1;         // halo rows (max)
   static constexpr int HCM = (RX + KS + 1) & ~1;  // halo columns (max, even)
@@ -74,7 +76,7 @@ template <int KS> struct Geometry {
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
 };
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // whole-sub-grid kernel
 constexpr int kWaves = kThreads / 64;
 constexpr float kSqrtD = 5.656854249492380f;  // sqrt(32)
 
@@ -87,10 +89,12 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 template <typename T, int KS>
-__global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
+__global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, int nby, int nbx, int total) {
+    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fdil, FastDiv fnbx,
+    FastDiv fnby, FastDiv fheads, int total) {
   using G = Geometry<KS>;
+  constexpr int kThreads = G::THREADS, kWaves = G::WAVES;
   using vec = typename Mma<T>::vec;
   constexpr int TY = G::TY, TX = G::TX, RY = G::RY, RX = G::RX, NB = G::NB;
   constexpr int SIDE = G::SIDE, MARGIN = G::MARGIN, ROWS = G::ROWS, COLS = G::COLS;
@@ -104,16 +108,20 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 
   const int tid = threadIdx.x;
   const int dil = s.dil;
-  int id = xcd_contiguous_id(blockIdx.x, total);
-  const int rx = id % dil;
-  id /= dil;
-  const int bx = id % nbx;
-  id /= nbx;
-  const int by = id % nby;
-  id /= nby;
-  const int ry = id % dil;
-  const int64_t plane = id / dil;
-  const int h = (int)(plane % s.heads);
+  uint32_t id = xcd_contiguous_id(blockIdx.x, total);
+  uint32_t t = fast_div(id, fdil);
+  const int rx = id - t * dil;
+  id = t;
+  t = fast_div(id, fnbx);
+  const int bx = id - t * fnbx.div;
+  id = t;
+  t = fast_div(id, fnby);
+  const int by = id - t * fnby.div;
+  id = t;
+  t = fast_div(id, fdil);
+  const int ry = id - t * dil;
+  const int64_t plane = t;
+  const int h = (int)(t - fast_div(t, fheads) * fheads.div);
 
   const int Ly = class_len(s.H, ry, dil), Lx = class_len(s.W, rx, dil);
   const int rc0 = by * RY, cc0 = bx * RX;
@@ -242,18 +250,21 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
   // parity shift dlt between the tile's first window column and its even
   // LDS column.
   const int dlt = ((cc0 - R) - hx0e) & 1;
+  // A key outside the window gets -inf: min(bias, row cap, column cap) with
+  // caps of +inf (inside) or -inf (outside) -- one v_min3 per element.
   f32x4 cint[NB];
   {
     const int rowrel = -qy, colrel = 4 * g - dlt - qx;
     const int bb = MARGIN + (R - qy) * SIDE + (4 * g - dlt - qx + R);
+    float ccap[4];
 #pragma unroll
-    for (int a = 0; a < NB; ++a)
+    for (int i = 0; i < 4; ++i) ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (unsigned)(rowrel + a) < (unsigned)KS &&
-                        (unsigned)(colrel + i) < (unsigned)KS;
-        cint[a][i] = ok ? b_lds[bb + a * SIDE + i] : -INFINITY;
-      }
+    for (int a = 0; a < NB; ++a) {
+      const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cint[a][i] = fminf(fminf(b_lds[bb + a * SIDE + i], rcap), ccap[i]);
+    }
   }
 
 #pragma unroll
@@ -289,15 +300,16 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
       const int sy = window_start(ci, Ly, KS), sx = window_start(cj, Lx, KS);
       const int rowrel = Y0 - sy, colrel = X0a + 4 * g - sx;
       const int bb = MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0a + 4 * g - cj + KS - 1);
+      float ccap[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
 #pragma unroll
       for (int a = 0; a < NB; ++a) {
+        const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
         f32x4 c;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = (unsigned)(rowrel + a) < (unsigned)KS &&
-                          (unsigned)(colrel + i) < (unsigned)KS;
-          c[i] = ok ? b_lds[bb + a * SIDE + i] : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) c[i] = fminf(fminf(b_lds[bb + a * SIDE + i], rcap), ccap[i]);
         sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
       }
     }
@@ -381,7 +393,7 @@ template <int KS> struct DenseGeometry {
 template <typename T, int KS>
 __global__ __launch_bounds__(kThreads) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, int items_per_head, int total,
+    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fitems, int total,
     int log2d) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
@@ -396,10 +408,10 @@ __global__ __launch_bounds__(kThreads) void dense_mfma_kernel(
 
   const int tid = threadIdx.x;
   const int dil = s.dil;
-  const int id = xcd_contiguous_id(blockIdx.x, total);
-  const int h = id / items_per_head;
+  const uint32_t id = xcd_contiguous_id(blockIdx.x, total);
+  const int h = fast_div(id, fitems);
   const int per_head = s.B << (2 * log2d);  // classes of one head
-  const int c0 = (id - h * items_per_head) * SG;
+  const int c0 = (id - h * fitems.div) * SG;
   const int ncls = min(SG, per_head - c0);
   const int64_t hw = (int64_t)s.H * s.W;
 
@@ -581,7 +593,7 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   while ((1 << log2d) < s.dil) ++log2d;
   dense_mfma_kernel<T, KS><<<dim3((unsigned)total), kThreads, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
-      (int)items_per_head, (int)total, log2d);
+      make_fastdiv((uint32_t)items_per_head), (int)total, log2d);
   return hipGetLastError();
 }
 
@@ -593,9 +605,10 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   const int nby = (Lymax + G::RY - 1) / G::RY, nbx = (Lxmax + G::RX - 1) / G::RX;
   const int64_t total = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
   if (total > INT_MAX) return hipErrorInvalidConfiguration;
-  fused_mfma_kernel<T, KS><<<dim3((unsigned)total), kThreads, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, nby, nbx,
-      (int)total);
+  fused_mfma_kernel<T, KS><<<dim3((unsigned)total), G::THREADS, 0, st>>>(
+      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
+      make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
+      make_fastdiv((uint32_t)s.heads), (int)total);
   return hipGetLastError();
 }
 
