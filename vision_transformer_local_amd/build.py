@@ -31,6 +31,9 @@ COMMON = [
     # keep MFMA sources/results in VGPRs: the AGPR form round-trips every
     # score block through v_accvgpr moves and serialises the MFMAs
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # inputs are finite: no NaN canonicalisation around min/max (infinities,
+    # used for window masking, are still honoured)
+    "-fno-honor-nans",
     "-I" + os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]

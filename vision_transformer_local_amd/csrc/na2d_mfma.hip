@@ -72,6 +72,10 @@ template <int KS> struct Geometry {
   static constexpr int COLS = HCM % 4 == 2 ? HCM : HCM + 2;  // odd dword count per V^T row
   static constexpr int SIDE = 2 * KS - 1;
   static constexpr int MARGIN = TY * SIDE + 32;  // keeps masked bias reads in bounds
+  // Interior accumulator table: entry (u, w), u = key row - query row within
+  // the tile's key block (-(TY-1)..NB-1), w = key column - query column
+  // (-TX..15), holds bias * sqrt(D) inside the k x k window and -inf outside.
+  static constexpr int IU = NB + TY - 1, IW = 16 + TX;
   static_assert(TX + KS <= 16, "key columns do not cover the tile");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
 };
@@ -100,11 +104,16 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
   constexpr int SIDE = G::SIDE, MARGIN = G::MARGIN, ROWS = G::ROWS, COLS = G::COLS;
   constexpr int HCM = G::HCM;
   constexpr int D = kHeadDim;
-  constexpr int VROW = D * COLS / 2;  // dwords per V^T row
+  // V^T: [channel][row][column pair]; an odd channel stride (in dwords)
+  // spreads the 16 channels one wave reads over distinct banks.
+  constexpr int CROW = COLS / 2;                            // dwords per channel row
+  constexpr int CSTRD = (ROWS * CROW) | 1;                  // dwords per channel
+  constexpr int R = KS / 2;
 
   __shared__ u32x4 k_lds[ROWS * HCM * 4];            // [row][col][chunk ^ swz]
-  __shared__ unsigned int vt_lds[ROWS * VROW];       // [row][channel][col pair]
+  __shared__ unsigned int vt_lds[D * CSTRD];         // [channel][row][col pair]
   __shared__ float b_lds[SIDE * SIDE + 2 * MARGIN];  // bias * sqrt(D), zero margins
+  __shared__ float i_lds[G::IU * G::IW];             // interior accumulator table
 
   const int tid = threadIdx.x;
   const int dil = s.dil;
@@ -210,26 +219,35 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
       b = Elem<T>::to_f(rpb[(int64_t)h * SIDE * SIDE + t]) * kSqrtD;
     b_lds[e] = b;
   }
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  for (int e = tid; e < G::IU * G::IW; e += kThreads) {
+    const int u = e / G::IW - (TY - 1), w = e % G::IW - TX;
+    float b = -INFINITY;
+    if ((unsigned)u < (unsigned)KS && (unsigned)w < (unsigned)KS)
+      b = rpb != nullptr ? Elem<T>::to_f(rpb[((int64_t)h * SIDE + u + R) * SIDE + w + R]) * kSqrtD
+                         : 0.f;
+    i_lds[e] = b;
+  }
+  // Rows past the halo only need finite values (every key there is masked):
+  // the clamped loads above hold real pixels, so all rows are written as is.
   {
     u32x4 *dst = k_lds + (kr0 * HCM + kcol) * 4 + (kch ^ ((kcol >> 1) & 3));
 #pragma unroll
     for (int it = 0; it < KPASS; ++it) {
       const int row = kr0 + it * KRP;
-      if (kact && row < ROWS) dst[it * KRP * HCM * 4] = row < HR ? kreg[it] : zero4;
+      if (kact && row < ROWS) dst[it * KRP * HCM * 4] = kreg[it];
     }
   }
   {
-    unsigned int *dst = vt_lds + vr0 * VROW + (vch * 8) * (COLS / 2) + vpair;
+    unsigned int *dst = vt_lds + (vch * 8) * CSTRD + vr0 * CROW + vpair;
 #pragma unroll
     for (int it = 0; it < VPASS; ++it) {
       const int row = vr0 + it * VRP;
       if (vact && row < ROWS) {
-        const u32x4 a = row < HR ? va[it] : zero4, b = row < HR ? vbr[it] : zero4;
+        const u32x4 a = va[it], b = vbr[it];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {  // dword w of a chunk = channels 2w, 2w+1
-          dst[it * VRP * VROW + (2 * w) * (COLS / 2)] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-          dst[it * VRP * VROW + (2 * w + 1) * (COLS / 2)] =
+          dst[it * VRP * CROW + (2 * w) * CSTRD] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
+          dst[it * VRP * CROW + (2 * w + 1) * CSTRD] =
               __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
         }
       }
@@ -243,28 +261,19 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
   vec ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
-  constexpr int R = KS / 2;
 
   // Accumulator input for tiles whose 16 windows are all unclamped: the mask
   // and bias then depend only on the lane, and on the (per-block constant)
   // parity shift dlt between the tile's first window column and its even
   // LDS column.
   const int dlt = ((cc0 - R) - hx0e) & 1;
-  // A key outside the window gets -inf: min(bias, row cap, column cap) with
-  // caps of +inf (inside) or -inf (outside) -- one v_min3 per element.
   f32x4 cint[NB];
   {
-    const int rowrel = -qy, colrel = 4 * g - dlt - qx;
-    const int bb = MARGIN + (R - qy) * SIDE + (4 * g - dlt - qx + R);
-    float ccap[4];
+    const float *tb = i_lds + (TY - 1 - qy) * G::IW + (TX + 4 * g - dlt - qx);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
+    for (int a = 0; a < NB; ++a)
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cint[a][i] = fminf(fminf(b_lds[bb + a * SIDE + i], rcap), ccap[i]);
-    }
+      for (int i = 0; i < 4; ++i) cint[a][i] = tb[a * G::IW + i];
   }
 
 #pragma unroll
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
     // product against an all-ones matrix gives every lane its query's
     // denominator, summed over exactly the 16-bit weights used above.
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned int *vb = vt_lds + lrow0 * VROW + chA * (COLS / 2) + ((lcol0 + 4 * g) >> 1);
+    const unsigned int *vb = vt_lds + chA * CSTRD + lrow0 * CROW + ((lcol0 + 4 * g) >> 1);
 #pragma unroll
     for (int j = 0; j < NB / 2; ++j) {
       vec pb;
@@ -340,8 +349,8 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
         pb[i] = static_cast<T>(sc[2 * j][i]);
         pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
       }
-      const unsigned int *r0 = vb + (2 * j) * VROW, *r1 = r0 + VROW;
-      constexpr int C4 = 4 * (COLS / 2);  // channel + 4
+      const unsigned int *r0 = vb + (2 * j) * CROW, *r1 = r0 + CROW;
+      constexpr int C4 = 4 * CSTRD;  // channel + 4
       const u32x4 w0 = {r0[0], r0[1], r1[0], r1[1]};
       const u32x4 w1 = {r0[C4], r0[C4 + 1], r1[C4], r1[C4 + 1]};
       o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
