@@ -53,6 +53,8 @@ WORKLOADS = {
     "tiny_f32": I.TINY,
 }
 KERNEL_SOURCES = ["vision_transformer_local_amd/csrc/na2d_mfma.hip",
+                  "vision_transformer_local_amd/csrc/na2d_dense.hip",
+                  "vision_transformer_local_amd/csrc/na2d_mfma_common.h",
                   "vision_transformer_local_amd/csrc/na2d_scalar.hip",
                   "vision_transformer_local_amd/csrc/na2d_internal.h"]
 

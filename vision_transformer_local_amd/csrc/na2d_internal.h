@@ -92,6 +92,11 @@ hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const v
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
                              bool *supported);
+// Whole-sub-grid kernel (H == W == k*d); sets *supported = false when the
+// problem is not of that kind.
+hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
+                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             bool *supported);
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);

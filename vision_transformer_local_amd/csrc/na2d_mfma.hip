@@ -10,600 +10,475 @@
 //   * Everything is expressed in residue-class (sub-grid) coordinates: with
 //     dilation d, the pixels (ry + d*ci, rx + d*cj) of one class (ry, rx) form
 //     an ordinary map on which the operator is plain neighborhood attention.
-//   * A workgroup owns an RY x RX block of one class of one (batch, head)
-//     plane.  It stages the block's key/value halo -- the union of its
-//     queries' clamped windows, at most (RY+k-1) x (RX+k) sub-grid pixels --
-//     in LDS once: K as [row][col] 64-byte pixels (16-byte chunks swizzled by
-//     column against bank conflicts) and V transposed to [row][channel][col]
-//     so the matrix cores can contract over pixels.  The LDS strides are
-//     compile-time constants; rows past the staged halo are zero-filled, so
-//     every LDS address in the tile loop is a per-lane base plus an immediate
-//     offset and no index is clamped.
-//   * A wave processes 16-query tiles (TY x TX sub-grid pixels).  The tile's
-//     keys are NB = TY + k - 1 halo rows x 16 columns (the columns start at an
-//     even LDS column so V reads are dword aligned).  Scores are produced
-//     transposed, S^T = K . Q^T, one v_mfma_f32_16x16x32 per halo row, so
-//     each lane ends up holding scores of ONE query: the softmax reductions
-//     need two lane swaps, and the probabilities are already laid out as the
-//     B operand of the second product out^T = V^T . P^T.
-//   * The relative-position bias (pre-multiplied by sqrt(D)) and the window
-//     mask (-inf outside the query's clamped window) enter as the accumulator
-//     input of the score MFMA.  For tiles whose windows are all unclamped this
-//     input is the same for every tile of the workgroup and is computed once.
-#include "na2d_internal.h"
+//   * A block is an RY x RX rectangle of queries of one class of one (batch,
+//     head) plane.  Its halo -- the union of its queries' clamped windows, at
+//     most (RY+k-1) x (RX+k-1) sub-grid pixels -- is copied to LDS by the
+//     direct global->LDS path (global_load_lds_dwordx4): K and V both as
+//     [row][column] 64-byte pixels, 16-byte chunks XOR-swizzled by column
+//     against bank conflicts.  Rows/columns past the halo hold clamped real
+//     pixels, so every LDS read is in bounds and finite without clamping.
+//   * Workgroups are persistent, one wave per 16-query tile of a block.  A
+//     workgroup walks a contiguous run of blocks (neighbouring blocks share
+//     halo rows in the same L2) with two LDS buffers: while it computes block
+//     i from one buffer, the DMA fills the other with block i+1.
+//   * Per tile (TY x TX queries): the keys are NB = TY + k - 1 halo rows x 16
+//     columns.  Scores are produced transposed, S^T = K . Q^T (one
+//     v_mfma_f32_16x16x32 per key row), so each lane holds scores of ONE
+//     query: the softmax max needs two lane swaps and the 16-bit
+//     probabilities are already the B operand of out^T = V^T . P^T.  The V^T
+//     operand is read from row-major V with ds_read_b64_tr_b16: a 16-lane
+//     group reads 4 pixels x 16 channels and each lane receives one channel
+//     of those 4 pixels.  A product against an all-ones matrix yields the
+//     softmax denominator over exactly the 16-bit weights used.
+//   * The relative-position bias (times sqrt(D)) and the window mask (-inf
+//     outside the query's clamped window) enter as the accumulator input of
+//     the score MFMA; for tiles whose windows are all unclamped it is a fixed
+//     per-lane pattern read from a small padded table.
+#include "na2d_mfma_common.h"
 
 #include <limits.h>
 
 namespace na2d {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+using namespace mfma;
 
-template <typename T> struct Mma;
-template <> struct Mma<__bf16> {
-  typedef bf16x8 vec;
-  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Mma<_Float16> {
-  typedef f16x8 vec;
-  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-};
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Tile geometry per kernel size.  A tile's 16 key columns must cover its
-// TX queries' windows plus one column of alignment slack: TX + k <= 16.
+// Block and tile geometry per kernel size.  A tile's 16 key columns cover
+// its TX queries' windows: TX + k - 1 <= 16.
 template <int KS> struct Geometry {
-  static constexpr int TY = KS <= 7 ? 2 : (KS <= 11 ? 4 : 8);  // tile rows
+  static constexpr int TY = KS <= 9 ? 2 : 4;                   // tile rows
   static constexpr int TX = 16 / TY;                           // tile columns
-  static constexpr int RY = KS <= 7 ? 28 : (KS <= 11 ? 8 : 16);  // block rows
-  static constexpr int RX = KS <= 7 ? 8 : (KS <= 11 ? 8 : 4);    // block columns
-  static constexpr int THREADS = KS <= 7 ? 512 : 256;            // workgroup size
-  static constexpr int WAVES = THREADS / 64;
-  static constexpr int NB = TY + KS - 1;          // key rows per tile (even)
-  static constexpr int HRM = RY + KS - 1;         // halo rows (max)
-  static constexpr int HCM = (RX + KS + 1) & ~1;  // halo columns (max, even)
-  static constexpr int ROWS = HRM + TY;           // LDS rows incl. zero rows read by tiles
-  static constexpr int COLS = HCM % 4 == 2 ? HCM : HCM + 2;  // odd dword count per V^T row
+  static constexpr int RY = KS <= 7 ? 28 : (KS == 9 ? 20 : (KS == 11 ? 16 : 12));
+  static constexpr int RX = 8;
+  static constexpr int NTY = RY / TY, NTX = RX / TX;
+  static constexpr int NTILE = NTY * NTX;  // one wave per tile
+  static constexpr int THREADS = NTILE * 64;
+  static constexpr int NB = TY + KS - 1;                       // key rows per tile
+  static constexpr int HRM = RY + KS - 1;                      // halo rows (max)
+  static constexpr int ROWS = HRM + TY;                        // staged rows
+  static constexpr int HCM = RX + KS - 1 > 16 ? RX + KS - 1 : 16;  // staged columns
+  static constexpr int PIX = ROWS * HCM;                       // staged pixels
   static constexpr int SIDE = 2 * KS - 1;
   static constexpr int MARGIN = TY * SIDE + 32;  // keeps masked bias reads in bounds
   // Interior accumulator table: entry (u, w), u = key row - query row within
   // the tile's key block (-(TY-1)..NB-1), w = key column - query column
   // (-TX..15), holds bias * sqrt(D) inside the k x k window and -inf outside.
   static constexpr int IU = NB + TY - 1, IW = 16 + TX;
-  static_assert(TX + KS <= 16, "key columns do not cover the tile");
+  static constexpr int NBT = SIDE * SIDE + 2 * MARGIN;  // bias table entries
+  static constexpr int NTAB = NBT + IU * IW;
+  static_assert(TX + KS - 1 <= 16, "key columns do not cover the tile");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
+  static_assert(RY % TY == 0 && RX % TX == 0, "blocks hold whole tiles");
+  static_assert((2 * PIX * 128 + 2 * NTAB * 4) <= 160 * 1024, "LDS");
 };
 
-constexpr int kThreads = 256;  // whole-sub-grid kernel
-constexpr int kWaves = kThreads / 64;
-constexpr float kSqrtD = 5.656854249492380f;  // sqrt(32)
+// Per-block coordinates (all workgroup-uniform).
+struct Block {
+  int64_t plane;
+  int h, ry, rx, Ly, Lx, rc0, rc1, cc0, cc1, hy0, hx0, HR, cmax;
+  bool valid;
+};
 
-// Maximum over the 4 lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float group_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// Block ids enumerate (plane, ry, by, bx, rx) with rx fastest.  A workgroup
+// visits consecutive ids, so it keeps the mixed-radix digits and steps them.
+struct BlockCursor {
+  int64_t plane;
+  int h, ry, by, bx, rx;
+};
+
+__device__ __forceinline__ BlockCursor cursor_at(uint32_t id, int dil, const FastDiv &fdil,
+                                                 const FastDiv &fnbx, const FastDiv &fnby,
+                                                 const FastDiv &fheads) {
+  BlockCursor c;
+  uint32_t t = fast_div(id, fdil);
+  c.rx = id - t * dil;
+  id = t;
+  t = fast_div(id, fnbx);
+  c.bx = id - t * fnbx.div;
+  id = t;
+  t = fast_div(id, fnby);
+  c.by = id - t * fnby.div;
+  id = t;
+  t = fast_div(id, fdil);
+  c.ry = id - t * dil;
+  c.plane = t;
+  c.h = (int)(t - fast_div(t, fheads) * fheads.div);
+  return c;
+}
+
+__device__ __forceinline__ void cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads) {
+  if (++c.rx < dil) return;
+  c.rx = 0;
+  if (++c.bx < nbx) return;
+  c.bx = 0;
+  if (++c.by < nby) return;
+  c.by = 0;
+  if (++c.ry < dil) return;
+  c.ry = 0;
+  ++c.plane;
+  if (++c.h == heads) c.h = 0;
+}
+
+template <int KS>
+__device__ __forceinline__ Block block_of(const BlockCursor &c, const Shape &s,
+                                          const FastDiv &fdil) {
+  using G = Geometry<KS>;
+  Block b;
+  b.plane = c.plane;
+  b.h = c.h;
+  b.ry = c.ry;
+  b.rx = c.rx;
+  // class_len(n, r, d) = (n - r + d - 1) / d
+  b.Ly = fast_div((uint32_t)(s.H - c.ry + s.dil - 1), fdil);
+  b.Lx = fast_div((uint32_t)(s.W - c.rx + s.dil - 1), fdil);
+  b.rc0 = c.by * G::RY;
+  b.cc0 = c.bx * G::RX;
+  b.valid = b.rc0 < b.Ly && b.cc0 < b.Lx;
+  b.rc1 = min(b.rc0 + G::RY, b.Ly);
+  b.cc1 = min(b.cc0 + G::RX, b.Lx);
+  b.hy0 = window_start(b.rc0, b.Ly, KS);
+  b.HR = window_start(b.rc1 - 1, b.Ly, KS) + KS - b.hy0;
+  b.hx0 = window_start(b.cc0, b.Lx, KS);
+  b.cmax = b.Lx - 1 - b.hx0;
+  return b;
+}
+
+// Copy a block's K and V halo into one LDS buffer with the direct
+// global->LDS path: 16 bytes per lane, lane i of an instruction lands at
+// base + 16*i, so each instruction fills 64 consecutive 16-byte slots.  Slot
+// (pixel, p) of the buffer holds logical chunk p ^ swz(column) of the pixel.
+template <typename T, int KS>
+__device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__restrict__ v,
+                                            const Block &b, const Shape &s, char *kbuf,
+                                            char *vbuf, int wave, int lane) {
+  using G = Geometry<KS>;
+  constexpr int NI = (G::PIX * 4 + 63) / 64;  // instructions per tensor (last one partial)
+  constexpr int NW = G::NTILE;
+  const int64_t hw = (int64_t)s.H * s.W;
+  const int64_t org = b.plane * hw + (int64_t)(b.ry + b.hy0 * s.dil) * s.W + b.rx + b.hx0 * s.dil;
+  const char *kb0 = (const char *)(k + org * kHeadDim);
+  const char *vb0 = (const char *)(v + org * kHeadDim);
+  const unsigned rowb = (unsigned)s.dil * (unsigned)s.W * (unsigned)(kHeadDim * sizeof(T));
+  const unsigned colb = (unsigned)s.dil * (unsigned)(kHeadDim * sizeof(T));
+  if constexpr (G::HCM == 16) {
+    // one instruction = one staged row of one tensor: the column / chunk part
+    // of the address is fixed per lane, the row part is uniform and shared by
+    // the K and V copies of the row
+    const int col = lane >> 2, lch = (lane & 3) ^ ((col >> 1) & 3);
+    const unsigned coff = (unsigned)min(col, b.cmax) * colb + lch * 16;
+#pragma unroll
+    for (int j = 0; j < (G::ROWS + NW - 1) / NW; ++j) {
+      const int row = wave + j * NW;
+      if (row < G::ROWS) {
+        const unsigned roff = (unsigned)min(row, b.HR - 1) * rowb;
+        __builtin_amdgcn_global_load_lds((const void *)(kb0 + (roff + coff)),
+                                         (lds_void *)(kbuf + row * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(vb0 + (roff + coff)),
+                                         (lds_void *)(vbuf + row * 1024), 16, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < (2 * NI + NW - 1) / NW; ++j) {
+      const int ins = wave + j * NW;
+      if (ins < 2 * NI) {
+        const bool isv = ins >= NI;
+        const int slot = (isv ? ins - NI : ins) * 64 + lane;
+        const int pix = slot >> 2, pch = slot & 3;
+        const int row = pix / G::HCM, col = pix - row * G::HCM;
+        const int lch = pch ^ ((col >> 1) & 3);
+        const unsigned off = (unsigned)min(row, b.HR - 1) * rowb +
+                             (unsigned)min(col, b.cmax) * colb + lch * 16;
+        char *dst = (isv ? vbuf : kbuf) + (slot - lane) * 16;
+        if (pix < G::PIX)
+          __builtin_amdgcn_global_load_lds((const void *)((isv ? vb0 : kb0) + off),
+                                           (lds_void *)dst, 16, 0, 0);
+      }
+    }
+  }
+}
+
+// Table entries (bias table with zero margins, then the interior table) this
+// thread writes: entry index into rpb, or -1 for a zero margin, -2 for -inf.
+template <int KS>
+__device__ __forceinline__ int table_index(int e) {
+  using G = Geometry<KS>;
+  constexpr int R = KS / 2;
+  if (e < G::NBT) {
+    const int t = e - G::MARGIN;
+    return (t >= 0 && t < G::SIDE * G::SIDE) ? t : -1;
+  }
+  const int f = e - G::NBT;
+  const int u = f / G::IW - (G::TY - 1), w = f % G::IW - G::TX;
+  return ((unsigned)u < (unsigned)KS && (unsigned)w < (unsigned)KS) ? (u + R) * G::SIDE + w + R
+                                                                    : -2;
+}
+
+template <int KS> struct TableRegs {
+  static constexpr int N = (Geometry<KS>::NTAB + Geometry<KS>::THREADS - 1) / Geometry<KS>::THREADS;
+};
+
+// Raw rpb values of this thread's entries for head h (loads are unconditional
+// -- margin entries read entry 0 -- so they never need an early wait).
+template <typename T, int KS>
+__device__ __forceinline__ void load_tables(const T *__restrict__ rpb, int h, int tid,
+                                            T (&reg)[TableRegs<KS>::N]) {
+  using G = Geometry<KS>;
+  if (rpb == nullptr) return;
+#pragma unroll
+  for (int it = 0; it < TableRegs<KS>::N; ++it) {
+    const int e = min(tid + it * G::THREADS, G::NTAB - 1);
+    const int idx = max(table_index<KS>(e), 0);
+    reg[it] = rpb[(int64_t)h * G::SIDE * G::SIDE + idx];
+  }
+}
+
+template <typename T, int KS>
+__device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
+                                             const T (&reg)[TableRegs<KS>::N]) {
+  using G = Geometry<KS>;
+#pragma unroll
+  for (int it = 0; it < TableRegs<KS>::N; ++it) {
+    const int e = tid + it * G::THREADS;
+    if (e < G::NTAB) {
+      const int idx = table_index<KS>(e);
+      float x = idx == -2 ? -INFINITY : 0.f;
+      if (idx >= 0 && has_rpb) x = Elem<T>::to_f(reg[it]) * kSqrtD;
+      tab[e] = x;
+    }
+  }
+}
+
+// The 16-byte Q slice of this lane for its tile of block b.
+template <typename T, int KS>
+__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, const Block &b, const Shape &s,
+                                        int wave, int ql, int g) {
+  using G = Geometry<KS>;
+  const int ty = wave / G::NTX, tx = wave % G::NTX;
+  const int ci = min(b.rc0 + ty * G::TY + ql / G::TX, b.rc1 - 1);
+  const int cj = min(b.cc0 + tx * G::TX + ql % G::TX, b.cc1 - 1);
+  const int64_t hw = (int64_t)s.H * s.W;
+  return *(const u32x4 *)(q + (b.plane * hw + (int64_t)(b.ry + ci * s.dil) * s.W + b.rx +
+                               cj * s.dil) * kHeadDim + g * 8);
+}
+
+// One 16-query tile of block b (this wave's), from one LDS buffer.
+template <typename T, int KS>
+__device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b, const Shape &s,
+                                             const char *kbuf, const char *vbuf, const float *tab,
+                                             u32x4 qraw, int wave, int lane) {
+  using G = Geometry<KS>;
+  using vec = typename Mma<T>::vec;
+  constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, HCM = G::HCM;
+  constexpr int R = KS / 2;
+  const int ql = lane & 15, g = lane >> 4;
+  const int qy = ql / TX, qx = ql % TX;
+  const int ty = wave / G::NTX, tx = wave % G::NTX;
+  const int tci0 = b.rc0 + ty * TY, tcj0 = b.cc0 + tx * TX;
+  if (tci0 >= b.rc1 || tcj0 >= b.cc1) return;  // tile outside a ragged block
+  int ci = tci0 + qy, cj = tcj0 + qx;
+  const bool valid = ci < b.rc1 && cj < b.cc1;
+  ci = min(ci, b.rc1 - 1);  // ragged tile: recompute a real query, store nothing
+  cj = min(cj, b.cc1 - 1);
+  const int Y0 = window_start(tci0, b.Ly, KS), X0 = window_start(tcj0, b.Lx, KS);
+  const int lrow0 = Y0 - b.hy0, lcol0 = X0 - b.hx0;
+  const vec qv = __builtin_bit_cast(vec, qraw);
+  const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
+
+  // S^T rows: key (Y0 + a, X0 + 4g + i) against query ql, i = 0..3.
+  const int kcol = lcol0 + ql;
+  const u32x4 *kb =
+      (const u32x4 *)(kbuf + (lrow0 * HCM + kcol) * 64) + (g ^ ((kcol >> 1) & 3));
+  f32x4 sc[NB];
+  const bool interior = tci0 - R >= 0 && tci0 + TY - 1 + R <= b.Ly - 1 && tcj0 - R >= 0 &&
+                        tcj0 + TX - 1 + R <= b.Lx - 1;
+  if (interior) {
+    const float *tb = tab + G::NBT + (TY - 1 - qy) * G::IW + (TX + 4 * g - qx);
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      f32x4 c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = tb[a * G::IW + i];
+      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
+    }
+  } else {
+    const int sy = window_start(ci, b.Ly, KS), sx = window_start(cj, b.Lx, KS);
+    const int rowrel = Y0 - sy, colrel = X0 + 4 * g - sx;
+    const float *bb = tab + G::MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0 + 4 * g - cj + KS - 1);
+    float ccap[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
+      f32x4 c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = fminf(fminf(bb[a * SIDE + i], rcap), ccap[i]);
+      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
+    }
+  }
+
+  // softmax over the query's k*k keys: the 4 lane groups hold disjoint keys
+  float mx = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
+  mx = group_max(mx);
+  const float mc = mx * c2;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+
+  // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA).  As a source
+  // of the transposing read, lane (g, 4k + qd) reads channels 4qd..4qd+3
+  // (+16 for the second channel block) of key column X0 + 4g + k.
+  const int vcol = lcol0 + 4 * g + (ql >> 2), qd = ql & 3, vs = (vcol >> 1) & 3;
+  const char *vrow = vbuf + (lrow0 * HCM + vcol) * 64 + 8 * (qd & 1);
+  const char *va0 = vrow + 16 * ((qd >> 1) ^ vs);
+  const char *va1 = vrow + 16 * (((qd >> 1) | 2) ^ vs);
+  vec ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NB / 2; ++j) {
+    vec pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = static_cast<T>(sc[2 * j][i]);
+      pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
+    }
+    constexpr int RB = HCM * 64;  // bytes per staged row
+    const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(va0 + (2 * j) * RB)));
+    const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(va0 + (2 * j + 1) * RB)));
+    const u32x2 b0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(va1 + (2 * j) * RB)));
+    const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_s16x4 *)(va1 + (2 * j + 1) * RB)));
+    const u32x4 w0 = {a0[0], a0[1], a1[0], a1[1]};
+    const u32x4 w1 = {b0[0], b0[1], b1[0], b1[1]};
+    o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
+    o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
+    o2 = Mma<T>::run(ones, pb, o2);
+  }
+
+  // lane holds channels 4g..4g+3 (o0) and 16+4g..16+4g+3 (o1) of query ql
+  if (valid) {
+    const float inv = __builtin_amdgcn_rcpf(o2[0]);
+    typedef __attribute__((ext_vector_type(4))) T vec4;
+    vec4 r0, r1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r0[i] = static_cast<T>(o0[i] * inv);
+      r1[i] = static_cast<T>(o1[i] * inv);
+    }
+    const int64_t hw = (int64_t)s.H * s.W;
+    T *o = out + (b.plane * hw + (int64_t)(b.ry + ci * s.dil) * s.W + b.rx + cj * s.dil) *
+                     kHeadDim + 4 * g;
+    *(u32x2 *)o = __builtin_bit_cast(u32x2, r0);
+    *(u32x2 *)(o + 16) = __builtin_bit_cast(u32x2, r1);
+  }
 }
 
 template <typename T, int KS>
 __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fdil, FastDiv fnbx,
-    FastDiv fnby, FastDiv fheads, int total) {
+    FastDiv fnby, FastDiv fheads, int nblocks) {
   using G = Geometry<KS>;
-  constexpr int kThreads = G::THREADS, kWaves = G::WAVES;
-  using vec = typename Mma<T>::vec;
-  constexpr int TY = G::TY, TX = G::TX, RY = G::RY, RX = G::RX, NB = G::NB;
-  constexpr int SIDE = G::SIDE, MARGIN = G::MARGIN, ROWS = G::ROWS, COLS = G::COLS;
-  constexpr int HCM = G::HCM;
-  constexpr int D = kHeadDim;
-  // V^T: [channel][row][column pair]; an odd channel stride (in dwords)
-  // spreads the 16 channels one wave reads over distinct banks.
-  constexpr int CROW = COLS / 2;                            // dwords per channel row
-  constexpr int CSTRD = (ROWS * CROW) | 1;                  // dwords per channel
-  constexpr int R = KS / 2;
+  __shared__ __attribute__((aligned(16))) char kbuf0[G::PIX * 64], vbuf0[G::PIX * 64];
+  __shared__ __attribute__((aligned(16))) char kbuf1[G::PIX * 64], vbuf1[G::PIX * 64];
+  __shared__ float tab0[G::NTAB], tab1[G::NTAB];
 
-  __shared__ u32x4 k_lds[ROWS * HCM * 4];            // [row][col][chunk ^ swz]
-  __shared__ unsigned int vt_lds[D * CSTRD];         // [channel][row][col pair]
-  __shared__ float b_lds[SIDE * SIDE + 2 * MARGIN];  // bias * sqrt(D), zero margins
-  __shared__ float i_lds[G::IU * G::IW];             // interior accumulator table
-
-  const int tid = threadIdx.x;
-  const int dil = s.dil;
-  uint32_t id = xcd_contiguous_id(blockIdx.x, total);
-  uint32_t t = fast_div(id, fdil);
-  const int rx = id - t * dil;
-  id = t;
-  t = fast_div(id, fnbx);
-  const int bx = id - t * fnbx.div;
-  id = t;
-  t = fast_div(id, fnby);
-  const int by = id - t * fnby.div;
-  id = t;
-  t = fast_div(id, fdil);
-  const int ry = id - t * dil;
-  const int64_t plane = t;
-  const int h = (int)(t - fast_div(t, fheads) * fheads.div);
-
-  const int Ly = class_len(s.H, ry, dil), Lx = class_len(s.W, rx, dil);
-  const int rc0 = by * RY, cc0 = bx * RX;
-  if (rc0 >= Ly || cc0 >= Lx) return;  // this class has fewer rows/columns
-  const int rc1 = min(rc0 + RY, Ly), cc1 = min(cc0 + RX, Lx);
-  // Halo = union of the block's windows (window starts are monotone).
-  const int hy0 = window_start(rc0, Ly, KS), hy1 = window_start(rc1 - 1, Ly, KS) + KS;
-  const int hx0 = window_start(cc0, Lx, KS);
-  const int hx0e = hx0 & ~1;  // even LDS column origin
-  const int HR = hy1 - hy0;
-
-  const int64_t hw = (int64_t)s.H * s.W;
-  const T *kp = k + plane * hw * D;
-  const T *vp = v + plane * hw * D;
-
-  // ---- stage bias, K and V^T -------------------------------------------
-  // Each thread owns one (column, 16-byte chunk) slot of a halo row and walks
-  // down the rows, so a load address is a uniform base plus a 32-bit offset
-  // that grows by one uniform row stride per pass.  All global loads of the
-  // workgroup are issued before any of them is consumed, so their latencies
-  // overlap.  Rows past the halo (up to ROWS) are written as zeros.
-  constexpr int KIPR = HCM * 4;             // K chunks per halo row
-  constexpr int KRP = kThreads / KIPR;      // K rows per pass
-  constexpr int KPASS = (ROWS + KRP - 1) / KRP;
-  constexpr int VIPR = (COLS / 2) * 4;      // V (pixel pair, chunk) items per row
-  constexpr int VRP = kThreads / VIPR;      // V rows per pass
-  constexpr int VPASS = (ROWS + VRP - 1) / VRP;
-  constexpr int NTY = (RY + TY - 1) / TY, NTX = (RX + TX - 1) / TX;  // tile grid of a block
-  constexpr int NTILE = NTY * NTX;
-  constexpr int QIT = (NTILE + kWaves - 1) / kWaves;  // Q tiles per wave
-  static_assert(KRP >= 1 && VRP >= 1, "halo row wider than the workgroup");
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave index is uniform within a wave: keep it (and all that derives from
+  // it) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
-  const int qy = ql / TX, qx = ql % TX;
-  const int nty = (rc1 - rc0 + TY - 1) / TY, ntx = (cc1 - cc0 + TX - 1) / TX;
+  // this workgroup's contiguous run of blocks
+  const int wg = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int b0 = (int)((int64_t)nblocks * wg / gridDim.x);
+  const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
+  if (b0 >= b1) return;
+  const bool has_rpb = rpb != nullptr;
 
-  // uniform: pixel of halo row 0, LDS column 0 (sub-grid (hy0, hx0e)), in bytes
-  const int64_t org = (int64_t)(ry + hy0 * dil) * s.W + rx + hx0e * dil;
-  const char *kb0 = (const char *)(kp + org * D);
-  const char *vb0 = (const char *)(vp + org * D);
-  const unsigned rowb = (unsigned)dil * (unsigned)s.W * (unsigned)(D * sizeof(T));
-  const unsigned colb = (unsigned)dil * (unsigned)(D * sizeof(T));
-  const int cmax = Lx - 1 - hx0e;  // last real column, relative to the LDS origin
-
-  const int kr0 = min(tid / KIPR, KRP - 1), kcol = (tid % KIPR) >> 2, kch = tid & 3;
-  const bool kact = tid < KRP * KIPR;
-  const unsigned koff = (unsigned)min(kcol, cmax) * colb + kch * 16;
-  // Loads are unconditional (rows clamped into the halo) so that they form
-  // one straight-line batch; the LDS writes below decide data versus zero.
-  u32x4 kreg[KPASS];
-  {
-    const unsigned first = koff + (unsigned)kr0 * rowb, last = koff + (unsigned)(HR - 1) * rowb;
-#pragma unroll
-    for (int it = 0; it < KPASS; ++it)
-      kreg[it] = *(const u32x4 *)(kb0 + min(first + (unsigned)(it * KRP) * rowb, last));
-  }
-  const int vr0 = min(tid / VIPR, VRP - 1), vpair = (tid % VIPR) >> 2, vch = tid & 3;
-  const bool vact = tid < VRP * VIPR;
-  const unsigned voff0 = (unsigned)min(2 * vpair, cmax) * colb + vch * 16;
-  const unsigned voff1 = (unsigned)min(2 * vpair + 1, cmax) * colb + vch * 16;
-  u32x4 va[VPASS], vbr[VPASS];
-  {
-    const unsigned r0 = (unsigned)vr0 * rowb, rl = (unsigned)(HR - 1) * rowb;
-#pragma unroll
-    for (int it = 0; it < VPASS; ++it) {
-      const unsigned ro = min(r0 + (unsigned)(it * VRP) * rowb, rl);
-      va[it] = *(const u32x4 *)(vb0 + (voff0 + ro));
-      vbr[it] = *(const u32x4 *)(vb0 + (voff1 + ro));
-    }
-  }
-  // this wave's query rows, one 16-byte slice per lane and tile
-  u32x4 qreg[QIT];
-#pragma unroll
-  for (int it = 0; it < QIT; ++it) {
-    const int tile = min(wave + it * kWaves, NTILE - 1);
-    const int ty = tile / NTX, tx = tile % NTX;
-    const int ci = min(rc0 + ty * TY + qy, rc1 - 1), cj = min(cc0 + tx * TX + qx, cc1 - 1);
-    qreg[it] = *(const u32x4 *)(q + plane * hw * D +
-                                ((int64_t)(ry + ci * dil) * s.W + rx + cj * dil) * D + g * 8);
-  }
-
-  for (int e = tid; e < SIDE * SIDE + 2 * MARGIN; e += kThreads) {
-    const int t = e - MARGIN;
-    float b = 0.f;
-    if (rpb != nullptr && t >= 0 && t < SIDE * SIDE)
-      b = Elem<T>::to_f(rpb[(int64_t)h * SIDE * SIDE + t]) * kSqrtD;
-    b_lds[e] = b;
-  }
-  for (int e = tid; e < G::IU * G::IW; e += kThreads) {
-    const int u = e / G::IW - (TY - 1), w = e % G::IW - TX;
-    float b = -INFINITY;
-    if ((unsigned)u < (unsigned)KS && (unsigned)w < (unsigned)KS)
-      b = rpb != nullptr ? Elem<T>::to_f(rpb[((int64_t)h * SIDE + u + R) * SIDE + w + R]) * kSqrtD
-                         : 0.f;
-    i_lds[e] = b;
-  }
-  // Rows past the halo only need finite values (every key there is masked):
-  // the clamped loads above hold real pixels, so all rows are written as is.
-  {
-    u32x4 *dst = k_lds + (kr0 * HCM + kcol) * 4 + (kch ^ ((kcol >> 1) & 3));
-#pragma unroll
-    for (int it = 0; it < KPASS; ++it) {
-      const int row = kr0 + it * KRP;
-      if (kact && row < ROWS) dst[it * KRP * HCM * 4] = kreg[it];
-    }
-  }
-  {
-    unsigned int *dst = vt_lds + (vch * 8) * CSTRD + vr0 * CROW + vpair;
-#pragma unroll
-    for (int it = 0; it < VPASS; ++it) {
-      const int row = vr0 + it * VRP;
-      if (vact && row < ROWS) {
-        const u32x4 a = va[it], b = vbr[it];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // dword w of a chunk = channels 2w, 2w+1
-          dst[it * VRP * CROW + (2 * w) * CSTRD] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-          dst[it * VRP * CROW + (2 * w + 1) * CSTRD] =
-              __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
-        }
-      }
-    }
-  }
+  // Prefetch order for block n+1 while block n computes: its Q slice (and,
+  // when the head changes, its bias-table values) first, then the K/V DMA;
+  // nothing consumes them before the end-of-block barrier, so the loads
+  // overlap the whole compute of block n.
+  T treg[TableRegs<KS>::N];
+  BlockCursor cc = cursor_at(b0, s.dil, fdil, fnbx, fnby, fheads);
+  Block cur = block_of<KS>(cc, s, fdil);
+  u32x4 qcur = load_q<T, KS>(q, cur, s, wave, ql, g);
+  load_tables<T, KS>(rpb, cur.h, tid, treg);
+  if (cur.valid) stage_block<T, KS>(k, v, cur, s, kbuf0, vbuf0, wave, lane);
+  store_tables<T, KS>(tab0, tid, has_rpb, treg);
+  int tab_h0 = cur.h, tab_h1 = -1;  // head whose tables each buffer holds
   __syncthreads();
+  const int nbx = fnbx.div, nby = fnby.div;
 
-  // ---- 16-query tiles ----------------------------------------------------
-  const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
-  const int chA = 8 * (ql >> 2) + (ql & 3);  // V^T channel of this lane (+4 for block 1)
-  vec ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
-
-  // Accumulator input for tiles whose 16 windows are all unclamped: the mask
-  // and bias then depend only on the lane, and on the (per-block constant)
-  // parity shift dlt between the tile's first window column and its even
-  // LDS column.
-  const int dlt = ((cc0 - R) - hx0e) & 1;
-  f32x4 cint[NB];
-  {
-    const float *tb = i_lds + (TY - 1 - qy) * G::IW + (TX + 4 * g - dlt - qx);
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cint[a][i] = tb[a * G::IW + i];
-  }
-
-#pragma unroll
-  for (int it = 0; it < QIT; ++it) {
-    const int tile = wave + it * kWaves;
-    if (tile >= NTILE) break;
-    const int ty = tile / NTX, tx = tile % NTX;
-    if (ty >= nty || tx >= ntx) continue;  // tile outside a ragged block
-    const int tci0 = rc0 + ty * TY, tcj0 = cc0 + tx * TX;
-    int ci = tci0 + qy, cj = tcj0 + qx;
-    const bool valid = ci < rc1 && cj < cc1;
-    ci = min(ci, rc1 - 1);  // ragged tile: recompute a real query, store nothing
-    cj = min(cj, cc1 - 1);
-    const int Y0 = window_start(tci0, Ly, KS), X0 = window_start(tcj0, Lx, KS);
-    const int X0a = X0 - ((X0 - hx0e) & 1);  // even LDS column
-    const int lrow0 = Y0 - hy0, lcol0 = X0a - hx0e;
-
-    const int64_t qoff =
-        plane * hw * D + ((int64_t)(ry + ci * dil) * s.W + rx + cj * dil) * D + g * 8;
-    const vec qv = __builtin_bit_cast(vec, qreg[it]);
-
-    // S^T rows: key (Y0 + a, X0a + 4g + i) against query ql, i = 0..3.
-    const int kcol = lcol0 + ql;
-    const u32x4 *kb = k_lds + (lrow0 * HCM + kcol) * 4 + (g ^ ((kcol >> 1) & 3));
-    f32x4 sc[NB];
-    const bool interior = tci0 - R >= 0 && tci0 + TY - 1 + R <= Ly - 1 && tcj0 - R >= 0 &&
-                          tcj0 + TX - 1 + R <= Lx - 1;
-    if (interior) {
-#pragma unroll
-      for (int a = 0; a < NB; ++a)
-        sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, cint[a]);
-    } else {
-      const int sy = window_start(ci, Ly, KS), sx = window_start(cj, Lx, KS);
-      const int rowrel = Y0 - sy, colrel = X0a + 4 * g - sx;
-      const int bb = MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0a + 4 * g - cj + KS - 1);
-      float ccap[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
-#pragma unroll
-      for (int a = 0; a < NB; ++a) {
-        const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
-        f32x4 c;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = fminf(fminf(b_lds[bb + a * SIDE + i], rcap), ccap[i]);
-        sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
+  // Two blocks per iteration so that each buffer is a fixed LDS array.
+  for (int bi = b0; bi < b1; bi += 2) {
+    {  // block bi from buffer 0; block bi+1 into buffer 1
+      const bool more = bi + 1 < b1;
+      if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
+      const Block nxt = block_of<KS>(cc, s, fdil);
+      const u32x4 qnxt = load_q<T, KS>(q, nxt, s, wave, ql, g);
+      const bool newtab = more && nxt.h != tab_h1;
+      if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
+      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, kbuf1, vbuf1, wave, lane);
+      if (cur.valid) compute_tile<T, KS>(out, cur, s, kbuf0, vbuf0, tab0, qcur, wave, lane);
+      if (!more) break;
+      if (newtab) {
+        store_tables<T, KS>(tab1, tid, has_rpb, treg);
+        tab_h1 = nxt.h;
       }
+      __syncthreads();  // also waits for the DMA (workgroup fence)
+      cur = nxt;
+      qcur = qnxt;
     }
-
-    // softmax over the query's k*k keys: the 4 lane groups hold disjoint keys
-    float mx = -INFINITY;
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
-    mx = group_max(mx);
-    const float mc = mx * c2;
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
-
-    // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA); a third
-    // product against an all-ones matrix gives every lane its query's
-    // denominator, summed over exactly the 16-bit weights used above.
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned int *vb = vt_lds + chA * CSTRD + lrow0 * CROW + ((lcol0 + 4 * g) >> 1);
-#pragma unroll
-    for (int j = 0; j < NB / 2; ++j) {
-      vec pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = static_cast<T>(sc[2 * j][i]);
-        pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
+    {  // block bi+1 from buffer 1; block bi+2 into buffer 0
+      const bool more = bi + 2 < b1;
+      if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
+      const Block nxt = block_of<KS>(cc, s, fdil);
+      const u32x4 qnxt = load_q<T, KS>(q, nxt, s, wave, ql, g);
+      const bool newtab = more && nxt.h != tab_h0;
+      if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
+      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, kbuf0, vbuf0, wave, lane);
+      if (cur.valid) compute_tile<T, KS>(out, cur, s, kbuf1, vbuf1, tab1, qcur, wave, lane);
+      if (!more) break;
+      if (newtab) {
+        store_tables<T, KS>(tab0, tid, has_rpb, treg);
+        tab_h0 = nxt.h;
       }
-      const unsigned int *r0 = vb + (2 * j) * CROW, *r1 = r0 + CROW;
-      constexpr int C4 = 4 * CSTRD;  // channel + 4
-      const u32x4 w0 = {r0[0], r0[1], r1[0], r1[1]};
-      const u32x4 w1 = {r0[C4], r0[C4 + 1], r1[C4], r1[C4 + 1]};
-      o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
-      o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
-      o2 = Mma<T>::run(ones, pb, o2);
-    }
-    const float l = o2[0];
-
-    // lane holds channels 8g..8g+3 (o0) and 8g+4..8g+7 (o1) of query ql
-    if (valid) {
-      const float inv = __builtin_amdgcn_rcpf(l);
-      vec res;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        res[i] = static_cast<T>(o0[i] * inv);
-        res[4 + i] = static_cast<T>(o1[i] * inv);
-      }
-      *(u32x4 *)(out + qoff) = __builtin_bit_cast(u32x4, res);
+      __syncthreads();
+      cur = nxt;
+      qcur = qnxt;
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Whole-sub-grid windows: H == k*d and W == k*d (d a power of two).
-//
-// Then every residue class is exactly k x k and every query's clamped window
-// is its entire class, so the operator is dense attention with bias inside
-// each class (the NAT README's self-attention equivalence, applied per
-// class).  The class is flattened: its N = k*k queries form ceil(N/16)
-// tiles and its N keys NKB blocks of 16 (padded with zero pixels, masked
-// with -inf).  The accumulator input (bias * sqrt(D), -inf on padding) of a
-// (tile, key block) pair is the same for every class of a head, so each wave
-// computes it once for the tiles it owns.
-//
-// A workgroup owns SG consecutive classes of one head, ordered (b, ry, rx)
-// with rx fastest, so for d > 1 the classes of one workgroup read whole
-// pixel rows.
-template <int KS> struct DenseGeometry {
-  static constexpr int N = KS * KS;
-  static constexpr int NT = (N + 15) / 16;             // query tiles per class
-  static constexpr int NKB = ((N + 15) / 16 + 1) & ~1; // key blocks (even)
-  static constexpr int NK = NKB * 16;                  // padded keys per class
-  static constexpr int SG = 8;                         // classes per workgroup
-  static constexpr int NTW = (NT + kWaves - 1) / kWaves;  // tiles per wave
-  static constexpr int VSTR = NK + 2;  // V^T channel stride (elements): odd dword count
-  static constexpr int SIDE = 2 * KS - 1;
-};
-
-template <typename T, int KS>
-__global__ __launch_bounds__(kThreads) void dense_mfma_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fitems, int total,
-    int log2d) {
-  using G = DenseGeometry<KS>;
-  using vec = typename Mma<T>::vec;
-  constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, SG = G::SG, NTW = G::NTW;
-  constexpr int VSTR = G::VSTR, SIDE = G::SIDE;
-  constexpr int D = kHeadDim;
-  constexpr int VCLS = D * VSTR / 2;  // dwords of V^T per class
-
-  __shared__ u32x4 k_lds[SG * NK * 4];         // [class][key][chunk ^ swz]
-  __shared__ unsigned int vt_lds[SG * VCLS];   // [class][channel][key pair]
-  __shared__ float b_lds[SIDE * SIDE];         // bias * sqrt(D)
-
-  const int tid = threadIdx.x;
-  const int dil = s.dil;
-  const uint32_t id = xcd_contiguous_id(blockIdx.x, total);
-  const int h = fast_div(id, fitems);
-  const int per_head = s.B << (2 * log2d);  // classes of one head
-  const int c0 = (id - h * fitems.div) * SG;
-  const int ncls = min(SG, per_head - c0);
-  const int64_t hw = (int64_t)s.H * s.W;
-
-  // class c of this workgroup -> (plane, ry, rx)
-  // (dilation is a power of two here, so the decode is shifts and masks)
-  auto class_pos = [&](int c, int64_t &plane, int &ry, int &rx) {
-    const int j = c0 + c;
-    rx = j & (dil - 1);
-    ry = (j >> log2d) & (dil - 1);
-    plane = (int64_t)(j >> (2 * log2d)) * s.heads + h;
-  };
-
-  // ---- stage: all loads first (unconditional, clamped), then LDS writes --
-  // A thread owns one (key, 16-byte chunk) slot of a class and visits the
-  // workgroup's classes; a load address is a uniform per-class base plus the
-  // thread's fixed 32-bit byte offset.
-  constexpr int KPC = NK * 4, KCPP = kThreads / KPC;        // K items per class, classes/pass
-  constexpr int VPC = (NK / 2) * 4, VCPP = kThreads / VPC;  // V items per class, classes/pass
-  static_assert(KCPP * KPC == kThreads && VCPP * VPC == kThreads, "class items must tile 256");
-  constexpr int KIT = SG / KCPP, VIT = SG / VCPP;
-  const unsigned rowb = (unsigned)dil * (unsigned)s.W * (unsigned)(D * sizeof(T));
-  const unsigned colb = (unsigned)dil * (unsigned)(D * sizeof(T));
-  // byte offset of pixel (0, 0) of class c (clamped to the workgroup's classes)
-  auto cls_off = [&](int c) -> int64_t {
-    const int j = c0 + min(c, ncls - 1);
-    const int rxx = j & (dil - 1), ryy = (j >> log2d) & (dil - 1);
-    const int64_t pl = (int64_t)(j >> (2 * log2d)) * s.heads + h;
-    return ((pl * hw + (int64_t)ryy * s.W + rxx) * D) * (int64_t)sizeof(T);
-  };
-  auto pick = [&](int it, int cpp, int sub) -> int64_t {
-    int64_t o = cls_off(it * cpp);
-#pragma unroll
-    for (int u = 1; u < 4; ++u)
-      if (u < cpp && sub == u) o = cls_off(it * cpp + u);
-    return o;
-  };
-
-  const int ksub = tid / KPC, kkey = (tid % KPC) >> 2, kch = tid & 3;
-  const int kkc = min(kkey, N - 1);
-  const unsigned koff = (unsigned)(kkc / KS) * rowb + (unsigned)(kkc % KS) * colb + kch * 16;
-  u32x4 kreg[KIT];
-#pragma unroll
-  for (int it = 0; it < KIT; ++it)
-    kreg[it] = *(const u32x4 *)((const char *)k + pick(it, KCPP, ksub) + koff);
-
-  const int vsub = tid / VPC, vpr = (tid % VPC) >> 2, vch = tid & 3;
-  const int vk0 = min(2 * vpr, N - 1), vk1 = min(2 * vpr + 1, N - 1);
-  const unsigned voff0 = (unsigned)(vk0 / KS) * rowb + (unsigned)(vk0 % KS) * colb + vch * 16;
-  const unsigned voff1 = (unsigned)(vk1 / KS) * rowb + (unsigned)(vk1 % KS) * colb + vch * 16;
-  u32x4 va[VIT], vb2[VIT];
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const char *base = (const char *)v + pick(it, VCPP, vsub);
-    va[it] = *(const u32x4 *)(base + voff0);
-    vb2[it] = *(const u32x4 *)(base + voff1);
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
   }
-  for (int e = tid; e < SIDE * SIDE; e += kThreads)
-    b_lds[e] = rpb != nullptr ? Elem<T>::to_f(rpb[(int64_t)h * SIDE * SIDE + e]) * kSqrtD : 0.f;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  {
-    // padding keys must hold finite values: zeros
-    u32x4 *dst = k_lds + (ksub * NK + kkey) * 4 + (kch ^ ((kkey >> 1) & 3));
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) dst[it * KCPP * NK * 4] = kkey < N ? kreg[it] : zero4;
-  }
-  {
-    unsigned int *dst = vt_lds + vsub * VCLS + (vch * 8) * (VSTR / 2) + vpr;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const u32x4 a = 2 * vpr < N ? va[it] : zero4, b = 2 * vpr + 1 < N ? vb2[it] : zero4;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dst[it * VCPP * VCLS + (2 * w) * (VSTR / 2)] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-        dst[it * VCPP * VCLS + (2 * w + 1) * (VSTR / 2)] =
-            __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
-      }
-    }
-  }
-  __syncthreads();
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int ql = lane & 15, g = lane >> 4;
-  const float c2 = kLog2e / kSqrtD;
-  const int chA = 8 * (ql >> 2) + (ql & 3);
-  vec ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
-
-  // accumulator inputs of this wave's tiles
-  f32x4 cint[NTW][NKB];
-#pragma unroll
-  for (int tw = 0; tw < NTW; ++tw) {
-    const int nq = min((wave + tw * kWaves) * 16 + ql, N - 1);
-    const int qa = nq / KS, qb = nq % KS;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int nk = kb * 16 + 4 * g + i;
-        const int ka = nk / KS, kc = nk % KS;
-        cint[tw][kb][i] = nk < N ? b_lds[(ka - qa + KS - 1) * SIDE + (kc - qb + KS - 1)] : -INFINITY;
-      }
-  }
-
-  for (int c = 0; c < ncls; ++c) {
-    int64_t plane;
-    int ry, rx;
-    class_pos(c, plane, ry, rx);
-    const u32x4 *kc = k_lds + c * NK * 4;
-    const unsigned int *vc = vt_lds + c * VCLS;
-#pragma unroll
-    for (int tw = 0; tw < NTW; ++tw) {
-      const int t = wave + tw * kWaves;
-      if (t >= NT) break;
-      const int nq0 = t * 16 + ql;
-      const int nq = min(nq0, N - 1);
-      const int64_t qoff =
-          (plane * hw + (int64_t)(ry + (nq / KS) * dil) * s.W + rx + (nq % KS) * dil) * D + g * 8;
-      const vec qv = __builtin_bit_cast(vec, *(const u32x4 *)(q + qoff));
-      f32x4 sc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int key = kb * 16 + ql;
-        sc[kb] = Mma<T>::run(__builtin_bit_cast(vec, kc[key * 4 + (g ^ ((key >> 1) & 3))]), qv,
-                             cint[tw][kb]);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][i]);
-      mx = group_max(mx);
-      const float mc = mx * c2;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c2, -mc));
-      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < NKB / 2; ++j) {
-        vec pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = static_cast<T>(sc[2 * j][i]);
-          pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
-        }
-        // keys 32j + 4g .. +3 and 32j + 16 + 4g .. +3 of channel chA (+4)
-        const unsigned int *r = vc + chA * (VSTR / 2) + 16 * j + 2 * g;
-        constexpr int C4 = 4 * (VSTR / 2);
-        const u32x4 w0 = {r[0], r[1], r[8], r[9]};
-        const u32x4 w1 = {r[C4], r[C4 + 1], r[C4 + 8], r[C4 + 9]};
-        o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
-        o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
-        o2 = Mma<T>::run(ones, pb, o2);
-      }
-      if (nq0 < N) {
-        const float inv = __builtin_amdgcn_rcpf(o2[0]);
-        vec res;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          res[i] = static_cast<T>(o0[i] * inv);
-          res[4 + i] = static_cast<T>(o1[i] * inv);
-        }
-        *(u32x4 *)(out + qoff) = __builtin_bit_cast(u32x4, res);
-      }
-    }
-  }
-}
-
-template <typename T, int KS>
-hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
-                        const Shape &s, hipStream_t st) {
-  using G = DenseGeometry<KS>;
-  const int64_t per_head = (int64_t)s.B * s.dil * s.dil;
-  const int64_t items_per_head = (per_head + G::SG - 1) / G::SG;
-  const int64_t total = items_per_head * s.heads;
-  if (total > INT_MAX || per_head > INT_MAX) return hipErrorInvalidConfiguration;
-  int log2d = 0;
-  while ((1 << log2d) < s.dil) ++log2d;
-  dense_mfma_kernel<T, KS><<<dim3((unsigned)total), kThreads, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
-      make_fastdiv((uint32_t)items_per_head), (int)total, log2d);
-  return hipGetLastError();
+  return cache[dev];
 }
 
 template <typename T, int KS>
@@ -612,26 +487,20 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   using G = Geometry<KS>;
   const int Lymax = class_len(s.H, 0, s.dil), Lxmax = class_len(s.W, 0, s.dil);
   const int nby = (Lymax + G::RY - 1) / G::RY, nbx = (Lxmax + G::RX - 1) / G::RX;
-  const int64_t total = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
-  if (total > INT_MAX) return hipErrorInvalidConfiguration;
-  fused_mfma_kernel<T, KS><<<dim3((unsigned)total), G::THREADS, 0, st>>>(
+  const int64_t nblocks = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
+  if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
+  // one persistent workgroup per compute unit (its LDS holds two blocks)
+  const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
+  fused_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
-      make_fastdiv((uint32_t)s.heads), (int)total);
+      make_fastdiv((uint32_t)s.heads), (int)nblocks);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_dtype(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, hipStream_t st, bool *supported) {
-  const bool pow2_dil = (s.dil & (s.dil - 1)) == 0;
-  if ((int64_t)s.ks * s.dil == s.H && (int64_t)s.ks * s.dil == s.W && pow2_dil) {
-    switch (s.ks) {
-      case 3: return launch_dense<T, 3>(q, k, v, rpb, out, s, st);
-      case 5: return launch_dense<T, 5>(q, k, v, rpb, out, s, st);
-      case 7: return launch_dense<T, 7>(q, k, v, rpb, out, s, st);
-    }
-  }
   switch (s.ks) {
     case 1: return launch_t<T, 1>(q, k, v, rpb, out, s, st);
     case 3: return launch_t<T, 3>(q, k, v, rpb, out, s, st);
@@ -650,6 +519,9 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
                              bool *supported) {
+  *supported = true;
+  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, dt, st, supported);
+  if (*supported) return e;
   *supported = true;
   if (dt == NA2D_DTYPE_BF16) return launch_dtype<__bf16>(q, k, v, rpb, out, s, st, supported);
   if (dt == NA2D_DTYPE_F16) return launch_dtype<_Float16>(q, k, v, rpb, out, s, st, supported);

@@ -1,0 +1,40 @@
+// na2d_mfma_common.h -- matrix-core helpers shared by the fused kernels of
+// libna2d (gfx950: v_mfma_f32_16x16x32_{bf16,f16}, v_permlane{16,32}_swap).
+#pragma once
+
+#include "na2d_internal.h"
+
+namespace na2d {
+namespace mfma {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+template <typename T> struct Mma;
+template <> struct Mma<__bf16> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<_Float16> {
+  typedef f16x8 vec;
+  static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr float kSqrtD = 5.656854249492380f;  // sqrt(32)
+
+// Maximum over the 4 lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+}  // namespace mfma
+}  // namespace na2d
