@@ -82,8 +82,10 @@ na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const vo
                            int kernel_size, int dilation, na2d_dtype_t dtype,
                            hipStream_t stream);
 
-/* na2d_forward with an explicit kernel family (NA2D_ALGO_MFMA with fp32 data
- * returns NA2D_ERROR_NOT_SUPPORTED). */
+/* na2d_forward with an explicit kernel family.  NA2D_ALGO_MFMA returns
+ * NA2D_ERROR_NOT_SUPPORTED for fp32 data and for (batch, head) planes of
+ * 2^24 pixels or more (H*W >= 16777216); NA2D_ALGO_AUTO sends such planes to
+ * the FMA kernel. */
 na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, const void *rpb,
                                 void *out, int B, int heads, int H, int W, int D,
                                 int kernel_size, int dilation, na2d_dtype_t dtype,

@@ -79,13 +79,15 @@ na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, con
     if (overlaps(out, tbytes, rpb, heads * side * side * elem_bytes(dtype)))
       return NA2D_ERROR_INVALID_VALUE;
   }
-  if (algo == NA2D_ALGO_AUTO) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
+  const bool automatic = algo == NA2D_ALGO_AUTO;
+  if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
   if (algo == NA2D_ALGO_MFMA) {
     if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
     bool supported = true;
     hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, dtype, stream, &supported);
-    if (!supported) return NA2D_ERROR_NOT_SUPPORTED;
-    return from_hip(e);
+    if (supported) return from_hip(e);
+    if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
+    // planes of 2^24 pixels or more: the general kernel handles them
   }
   return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, dtype, stream));
 }

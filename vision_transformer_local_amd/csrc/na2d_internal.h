@@ -22,6 +22,9 @@ namespace na2d {
 constexpr int kHeadDim = 32;      // D supported by this build
 constexpr int kMaxKernel = 13;    // largest supported kernel_size
 constexpr float kLog2e = 1.4426950408889634f;
+// The matrix-core kernel addresses a (batch, head) plane with 32-bit byte
+// offsets and 24-bit pixel products: planes must hold fewer pixels than this.
+constexpr int64_t kMaxPlanePixels = int64_t(1) << 24;
 
 __host__ __device__ __forceinline__ int window_start(int c, int len, int ks) {
   int s = c - ks / 2;

@@ -65,12 +65,17 @@ template <int KS> struct Geometry {
   static constexpr int PIX = ROWS * HCM;                       // staged pixels
   static constexpr int SIDE = 2 * KS - 1;
   static constexpr int MARGIN = TY * SIDE + 32;  // keeps masked bias reads in bounds
-  // Interior accumulator table: entry (u, w), u = key row - query row within
-  // the tile's key block (-(TY-1)..NB-1), w = key column - query column
-  // (-TX..15), holds bias * sqrt(D) inside the k x k window and -inf outside.
+  // LDS tables, one set per buffer.  First the interior accumulator table:
+  // entry (u, w), u = key row - query row within the tile's key block
+  // (-(TY-1)..NB-1), w = key column - query column (-TX..15), at
+  // (u + TY-1) * IW + w + TX, holds bias * sqrt(D) inside the k x k window and
+  // -inf outside.  Then the bias table (times sqrt(D)) with zero margins; its
+  // entry (0, 0) sits at BOFF.  The interior table starts at offset 0 so that
+  // a lane's reads of it fit the immediate offsets of one base address.
   static constexpr int IU = NB + TY - 1, IW = 16 + TX;
-  static constexpr int NBT = SIDE * SIDE + 2 * MARGIN;  // bias table entries
-  static constexpr int NTAB = NBT + IU * IW;
+  static constexpr int NINT = IU * IW;
+  static constexpr int BOFF = NINT + MARGIN;
+  static constexpr int NTAB = NINT + SIDE * SIDE + 2 * MARGIN;
   static_assert(TX + KS - 1 <= 16, "key columns do not cover the tile");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
   static_assert(RY % TY == 0 && RX % TX == 0, "blocks hold whole tiles");
@@ -80,7 +85,8 @@ template <int KS> struct Geometry {
 // Per-block coordinates (all workgroup-uniform).
 struct Block {
   int64_t plane;
-  int h, ry, rx, Ly, Lx, rc0, rc1, cc0, cc1, hy0, hx0, HR, cmax;
+  int h, Ly, Lx, rc0, rc1, cc0, cc1, hy0, hx0, HR, cmax;
+  int org;  // in-plane pixel index of the class origin (ry, rx)
   bool valid;
 };
 
@@ -131,8 +137,7 @@ __device__ __forceinline__ Block block_of(const BlockCursor &c, const Shape &s,
   Block b;
   b.plane = c.plane;
   b.h = c.h;
-  b.ry = c.ry;
-  b.rx = c.rx;
+  b.org = c.ry * s.W + c.rx;
   // class_len(n, r, d) = (n - r + d - 1) / d
   b.Ly = fast_div((uint32_t)(s.H - c.ry + s.dil - 1), fdil);
   b.Lx = fast_div((uint32_t)(s.W - c.rx + s.dil - 1), fdil);
@@ -154,17 +159,18 @@ __device__ __forceinline__ Block block_of(const BlockCursor &c, const Shape &s,
 // (pixel, p) of the buffer holds logical chunk p ^ swz(column) of the pixel.
 template <typename T, int KS>
 __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__restrict__ v,
-                                            const Block &b, const Shape &s, char *kbuf,
-                                            char *vbuf, int wave, int lane) {
+                                            const Block &b, const Shape &s, int64_t pstride,
+                                            char *kbuf, char *vbuf, int wave, int lane) {
   using G = Geometry<KS>;
   constexpr int NI = (G::PIX * 4 + 63) / 64;  // instructions per tensor (last one partial)
   constexpr int NW = G::NTILE;
-  const int64_t hw = (int64_t)s.H * s.W;
-  const int64_t org = b.plane * hw + (int64_t)(b.ry + b.hy0 * s.dil) * s.W + b.rx + b.hx0 * s.dil;
-  const char *kb0 = (const char *)(k + org * kHeadDim);
-  const char *vb0 = (const char *)(v + org * kHeadDim);
-  const unsigned rowb = (unsigned)s.dil * (unsigned)s.W * (unsigned)(kHeadDim * sizeof(T));
-  const unsigned colb = (unsigned)s.dil * (unsigned)(kHeadDim * sizeof(T));
+  constexpr unsigned PB = kHeadDim * sizeof(T);  // bytes per pixel
+  // halo origin, as a byte offset within the plane (planes are < 2^24 pixels)
+  const unsigned org = (unsigned)(b.org + b.hy0 * s.dil * s.W + b.hx0 * s.dil) * PB;
+  const char *kb0 = (const char *)(k + b.plane * pstride) + org;
+  const char *vb0 = (const char *)(v + b.plane * pstride) + org;
+  const unsigned rowb = (unsigned)s.dil * (unsigned)s.W * PB;
+  const unsigned colb = (unsigned)s.dil * PB;
   if constexpr (G::HCM == 16) {
     // one instruction = one staged row of one tensor: the column / chunk part
     // of the address is fixed per lane, the row part is uniform and shared by
@@ -203,18 +209,17 @@ __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__
   }
 }
 
-// Table entries (bias table with zero margins, then the interior table) this
+// Table entries (interior table, then bias table with zero margins) this
 // thread writes: entry index into rpb, or -1 for a zero margin, -2 for -inf.
 template <int KS>
 __device__ __forceinline__ int table_index(int e) {
   using G = Geometry<KS>;
   constexpr int R = KS / 2;
-  if (e < G::NBT) {
-    const int t = e - G::MARGIN;
+  if (e >= G::NINT) {
+    const int t = e - G::BOFF;
     return (t >= 0 && t < G::SIDE * G::SIDE) ? t : -1;
   }
-  const int f = e - G::NBT;
-  const int u = f / G::IW - (G::TY - 1), w = f % G::IW - G::TX;
+  const int u = e / G::IW - (G::TY - 1), w = e % G::IW - G::TX;
   return ((unsigned)u < (unsigned)KS && (unsigned)w < (unsigned)KS) ? (u + R) * G::SIDE + w + R
                                                                     : -2;
 }
@@ -254,24 +259,33 @@ __device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
   }
 }
 
-// The 16-byte Q slice of this lane for its tile of block b.
-template <typename T, int KS>
-__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, const Block &b, const Shape &s,
-                                        int wave, int ql, int g) {
-  using G = Geometry<KS>;
-  const int ty = wave / G::NTX, tx = wave % G::NTX;
-  const int ci = min(b.rc0 + ty * G::TY + ql / G::TX, b.rc1 - 1);
-  const int cj = min(b.cc0 + tx * G::TX + ql % G::TX, b.cc1 - 1);
-  const int64_t hw = (int64_t)s.H * s.W;
-  return *(const u32x4 *)(q + (b.plane * hw + (int64_t)(b.ry + ci * s.dil) * s.W + b.rx +
-                               cj * s.dil) * kHeadDim + g * 8);
+// In-plane pixel index of this lane's query in block b: block row lr, block
+// column lc, clamped into a ragged block (such lanes recompute a real query
+// and store nothing).  Planes hold fewer than 2^24 pixels, so 24-bit
+// multiplies suffice.
+__device__ __forceinline__ int query_pixel(const Block &b, const Shape &s, int lr, int lc) {
+  const int ci = b.rc0 + min(lr, b.rc1 - 1 - b.rc0);
+  const int cj = b.cc0 + min(lc, b.cc1 - 1 - b.cc0);
+  return b.org + (int)__umul24((unsigned)ci, (unsigned)(s.dil * s.W)) +
+         (int)__umul24((unsigned)cj, (unsigned)s.dil);
+}
+
+// The 16-byte Q slice (channels 8g..8g+7) of the query at pixel pix.
+template <typename T>
+__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, const Block &b, int64_t pstride,
+                                        int pix, int g) {
+  const char *qp = (const char *)(q + b.plane * pstride);
+  return *(const u32x4 *)(qp + ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 16u));
 }
 
 // One 16-query tile of block b (this wave's), from one LDS buffer.
+// One 16-query tile of block b (this wave's), from one LDS buffer; the
+// query of this lane sits at in-plane pixel pix.
 template <typename T, int KS>
 __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b, const Shape &s,
-                                             const char *kbuf, const char *vbuf, const float *tab,
-                                             u32x4 qraw, int wave, int lane) {
+                                             int64_t pstride, int pix, const char *kbuf,
+                                             const char *vbuf, const float *tab, u32x4 qraw,
+                                             int wave, int lane) {
   using G = Geometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, HCM = G::HCM;
@@ -281,10 +295,6 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
   const int ty = wave / G::NTX, tx = wave % G::NTX;
   const int tci0 = b.rc0 + ty * TY, tcj0 = b.cc0 + tx * TX;
   if (tci0 >= b.rc1 || tcj0 >= b.cc1) return;  // tile outside a ragged block
-  int ci = tci0 + qy, cj = tcj0 + qx;
-  const bool valid = ci < b.rc1 && cj < b.cc1;
-  ci = min(ci, b.rc1 - 1);  // ragged tile: recompute a real query, store nothing
-  cj = min(cj, b.cc1 - 1);
   const int Y0 = window_start(tci0, b.Ly, KS), X0 = window_start(tcj0, b.Lx, KS);
   const int lrow0 = Y0 - b.hy0, lcol0 = X0 - b.hx0;
   const vec qv = __builtin_bit_cast(vec, qraw);
@@ -298,7 +308,7 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
   const bool interior = tci0 - R >= 0 && tci0 + TY - 1 + R <= b.Ly - 1 && tcj0 - R >= 0 &&
                         tcj0 + TX - 1 + R <= b.Lx - 1;
   if (interior) {
-    const float *tb = tab + G::NBT + (TY - 1 - qy) * G::IW + (TX + 4 * g - qx);
+    const float *tb = tab + (TY - 1 - qy) * G::IW + (TX + 4 * g - qx);
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
       f32x4 c;
@@ -307,19 +317,33 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
       sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
     }
   } else {
+    // The query's window starts sy, sx lie TY-1 resp. TX-1 at most past the
+    // tile's Y0, X0, so key rows TY-1..k-1 of the key block are inside every
+    // lane's row window: only the first and last TY-1 rows need a row test.
+    const int ci = min(tci0 + qy, b.rc1 - 1), cj = min(tcj0 + qx, b.cc1 - 1);
     const int sy = window_start(ci, b.Ly, KS), sx = window_start(cj, b.Lx, KS);
     const int rowrel = Y0 - sy, colrel = X0 + 4 * g - sx;
-    const float *bb = tab + G::MARGIN + (Y0 - ci + KS - 1) * SIDE + (X0 + 4 * g - cj + KS - 1);
+    int bidx = G::BOFF + (Y0 - ci + KS - 1) * SIDE + (X0 + 4 * g - cj + KS - 1);
+    asm volatile("" : "+v"(bidx));  // one base register; the reads use immediate offsets
+    const float *bb = tab + bidx;
+    // +inf inside the window, -inf outside; hidden from the optimiser so that
+    // each entry costs one min and the table reads stay unconditional
     float ccap[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
       ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
+      asm volatile("" : "+v"(ccap[i]));
+    }
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
-      const float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
+      const bool rtest = !(a >= TY - 1 && a <= KS - 1);
+      float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
+      if (rtest) asm volatile("" : "+v"(rcap));
       f32x4 c;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = fminf(fminf(bb[a * SIDE + i], rcap), ccap[i]);
+      for (int i = 0; i < 4; ++i)
+        c[i] = rtest ? fminf(fminf(bb[a * SIDE + i], ccap[i]), rcap)
+                     : fminf(bb[a * SIDE + i], ccap[i]);
       sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
     }
   }
@@ -373,7 +397,7 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
   }
 
   // lane holds channels 4g..4g+3 (o0) and 16+4g..16+4g+3 (o1) of query ql
-  if (valid) {
+  if (tci0 + qy < b.rc1 && tcj0 + qx < b.cc1) {
     const float inv = __builtin_amdgcn_rcpf(o2[0]);
     typedef __attribute__((ext_vector_type(4))) T vec4;
     vec4 r0, r1;
@@ -382,11 +406,10 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
       r0[i] = static_cast<T>(o0[i] * inv);
       r1[i] = static_cast<T>(o1[i] * inv);
     }
-    const int64_t hw = (int64_t)s.H * s.W;
-    T *o = out + (b.plane * hw + (int64_t)(b.ry + ci * s.dil) * s.W + b.rx + cj * s.dil) *
-                     kHeadDim + 4 * g;
+    char *o = (char *)(out + b.plane * pstride) +
+              ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u);
     *(u32x2 *)o = __builtin_bit_cast(u32x2, r0);
-    *(u32x2 *)(o + 16) = __builtin_bit_cast(u32x2, r1);
+    *(u32x2 *)(o + 16 * sizeof(T)) = __builtin_bit_cast(u32x2, r1);
   }
 }
 
@@ -410,6 +433,9 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
   const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
   if (b0 >= b1) return;
   const bool has_rpb = rpb != nullptr;
+  const int64_t pstride = (int64_t)s.H * s.W * kHeadDim;  // elements per plane
+  // this lane's query position within a block
+  const int lr = (wave / G::NTX) * G::TY + ql / G::TX, lc = (wave % G::NTX) * G::TX + ql % G::TX;
 
   // Prefetch order for block n+1 while block n computes: its Q slice (and,
   // when the head changes, its bias-table values) first, then the K/V DMA;
@@ -418,9 +444,10 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
   T treg[TableRegs<KS>::N];
   BlockCursor cc = cursor_at(b0, s.dil, fdil, fnbx, fnby, fheads);
   Block cur = block_of<KS>(cc, s, fdil);
-  u32x4 qcur = load_q<T, KS>(q, cur, s, wave, ql, g);
+  int pcur = query_pixel(cur, s, lr, lc);
+  u32x4 qcur = load_q<T>(q, cur, pstride, pcur, g);
   load_tables<T, KS>(rpb, cur.h, tid, treg);
-  if (cur.valid) stage_block<T, KS>(k, v, cur, s, kbuf0, vbuf0, wave, lane);
+  if (cur.valid) stage_block<T, KS>(k, v, cur, s, pstride, kbuf0, vbuf0, wave, lane);
   store_tables<T, KS>(tab0, tid, has_rpb, treg);
   int tab_h0 = cur.h, tab_h1 = -1;  // head whose tables each buffer holds
   __syncthreads();
@@ -432,11 +459,13 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
       const bool more = bi + 1 < b1;
       if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
       const Block nxt = block_of<KS>(cc, s, fdil);
-      const u32x4 qnxt = load_q<T, KS>(q, nxt, s, wave, ql, g);
+      const int pnxt = query_pixel(nxt, s, lr, lc);
+      const u32x4 qnxt = load_q<T>(q, nxt, pstride, pnxt, g);
       const bool newtab = more && nxt.h != tab_h1;
       if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
-      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, kbuf1, vbuf1, wave, lane);
-      if (cur.valid) compute_tile<T, KS>(out, cur, s, kbuf0, vbuf0, tab0, qcur, wave, lane);
+      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, pstride, kbuf1, vbuf1, wave, lane);
+      if (cur.valid)
+        compute_tile<T, KS>(out, cur, s, pstride, pcur, kbuf0, vbuf0, tab0, qcur, wave, lane);
       if (!more) break;
       if (newtab) {
         store_tables<T, KS>(tab1, tid, has_rpb, treg);
@@ -444,17 +473,20 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
       }
       __syncthreads();  // also waits for the DMA (workgroup fence)
       cur = nxt;
+      pcur = pnxt;
       qcur = qnxt;
     }
     {  // block bi+1 from buffer 1; block bi+2 into buffer 0
       const bool more = bi + 2 < b1;
       if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
       const Block nxt = block_of<KS>(cc, s, fdil);
-      const u32x4 qnxt = load_q<T, KS>(q, nxt, s, wave, ql, g);
+      const int pnxt = query_pixel(nxt, s, lr, lc);
+      const u32x4 qnxt = load_q<T>(q, nxt, pstride, pnxt, g);
       const bool newtab = more && nxt.h != tab_h0;
       if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
-      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, kbuf0, vbuf0, wave, lane);
-      if (cur.valid) compute_tile<T, KS>(out, cur, s, kbuf1, vbuf1, tab1, qcur, wave, lane);
+      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, pstride, kbuf0, vbuf0, wave, lane);
+      if (cur.valid)
+        compute_tile<T, KS>(out, cur, s, pstride, pcur, kbuf1, vbuf1, tab1, qcur, wave, lane);
       if (!more) break;
       if (newtab) {
         store_tables<T, KS>(tab0, tid, has_rpb, treg);
@@ -462,6 +494,7 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
       }
       __syncthreads();
       cur = nxt;
+      pcur = pnxt;
       qcur = qnxt;
     }
   }
@@ -501,6 +534,11 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
 template <typename T>
 hipError_t launch_dtype(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, hipStream_t st, bool *supported) {
+  // in-plane offsets are 32-bit and pixel products 24-bit
+  if ((int64_t)s.H * s.W >= kMaxPlanePixels) {
+    *supported = false;
+    return hipSuccess;
+  }
   switch (s.ks) {
     case 1: return launch_t<T, 1>(q, k, v, rpb, out, s, st);
     case 3: return launch_t<T, 3>(q, k, v, rpb, out, s, st);
