@@ -50,18 +50,27 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Block and tile geometry per kernel size.  A tile's 16 key columns cover
 // its TX queries' windows: TX + k - 1 <= 16.
-template <int KS> struct Geometry {
+constexpr int default_rows(int ks) { return ks <= 7 ? 32 : (ks == 9 ? 24 : 16); }
+
+template <int KS, int RYV = default_rows(KS)> struct Geometry {
   static constexpr int TY = KS <= 9 ? 2 : 4;                   // tile rows
   static constexpr int TX = 16 / TY;                           // tile columns
-  static constexpr int RY = KS <= 7 ? 28 : (KS == 9 ? 20 : (KS == 11 ? 16 : 12));
+  // Block rows: the waves (one per tile) come in multiples of 4, so that
+  // they spread evenly over the 4 SIMDs, or 14 waves for k <= 7 where that
+  // tiles the map with fewer blocks; at most what the two LDS buffers allow.
+  static constexpr int RY = RYV;
   static constexpr int RX = 8;
   static constexpr int NTY = RY / TY, NTX = RX / TX;
   static constexpr int NTILE = NTY * NTX;  // one wave per tile
   static constexpr int THREADS = NTILE * 64;
   static constexpr int NB = TY + KS - 1;                       // key rows per tile
   static constexpr int HRM = RY + KS - 1;                      // halo rows (max)
-  static constexpr int ROWS = HRM + TY;                        // staged rows
   static constexpr int HCM = RX + KS - 1 > 16 ? RX + KS - 1 : 16;  // staged columns
+  // A tile reads 16 key columns from its first one, at most RX - TX past the
+  // block's: with HCM < RX - TX + 16 the last reads run into the next staged
+  // row, so one more row keeps them inside the buffer (they only ever meet
+  // masked keys).
+  static constexpr int ROWS = HRM + (RX - TX + 16 > HCM ? 1 : 0);  // staged rows
   static constexpr int PIX = ROWS * HCM;                       // staged pixels
   static constexpr int SIDE = 2 * KS - 1;
   static constexpr int MARGIN = TY * SIDE + 32;  // keeps masked bias reads in bounds
@@ -79,15 +88,8 @@ template <int KS> struct Geometry {
   static_assert(TX + KS - 1 <= 16, "key columns do not cover the tile");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
   static_assert(RY % TY == 0 && RX % TX == 0, "blocks hold whole tiles");
+  static_assert(THREADS <= 1024, "one workgroup");
   static_assert((2 * PIX * 128 + 2 * NTAB * 4) <= 160 * 1024, "LDS");
-};
-
-// Per-block coordinates (all workgroup-uniform).
-struct Block {
-  int64_t plane;
-  int h, Ly, Lx, rc0, rc1, cc0, cc1, hy0, hx0, HR, cmax;
-  int org;  // in-plane pixel index of the class origin (ry, rx)
-  bool valid;
 };
 
 // Block ids enumerate (plane, ry, by, bx, rx) with rx fastest.  A workgroup
@@ -117,58 +119,111 @@ __device__ __forceinline__ BlockCursor cursor_at(uint32_t id, int dil, const Fas
   return c;
 }
 
-__device__ __forceinline__ void cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads) {
-  if (++c.rx < dil) return;
+// Steps to the next id; true when (plane, ry, by) changed.
+__device__ __forceinline__ bool cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads) {
+  if (++c.rx < dil) return false;
   c.rx = 0;
-  if (++c.bx < nbx) return;
+  if (++c.bx < nbx) return false;
   c.bx = 0;
-  if (++c.by < nby) return;
+  if (++c.by < nby) return true;
   c.by = 0;
-  if (++c.ry < dil) return;
+  if (++c.ry < dil) return true;
   c.ry = 0;
   ++c.plane;
   if (++c.h == heads) c.h = 0;
+  return true;
 }
 
-template <int KS>
-__device__ __forceinline__ Block block_of(const BlockCursor &c, const Shape &s,
-                                          const FastDiv &fdil) {
-  using G = Geometry<KS>;
-  Block b;
-  b.plane = c.plane;
-  b.h = c.h;
-  b.org = c.ry * s.W + c.rx;
+// A block splits into a row part, which depends on (plane, ry, by) only and
+// is recomputed when those change, and a column part, which depends on
+// (rx, bx).  Both include what this wave's tile and this lane's query need.
+// Byte offsets within a plane fit 32 bits (planes hold < 2^24 pixels).
+struct RowPart {
+  int64_t pofs;    // element offset of the (batch, head) plane
+  int h, Ly, rc0, rc1, hy0, HR;
+  int tci0, Y0;    // first query row of this wave's tile; first key row of its key block
+  unsigned hrow;   // byte offset of the first halo row: (ry + hy0*d) * W * 64
+  int ry;
+  int ok, inner;   // block row exists; the tile's windows are unclamped in y
+};
+
+struct ColPart {
+  int Lx, cc0, cc1, hx0, cmax;
+  int tcj0, X0;
+  unsigned hcol;   // byte offset of the first halo column: (rx + hx0*d) * 64
+  int rx;
+  int ok, inner;
+};
+
+template <typename T, int KS, int RY>
+__device__ __forceinline__ RowPart row_part(const BlockCursor &c, const Shape &s,
+                                            const FastDiv &fdil, int64_t pstride, int ty, int lr) {
+  using G = Geometry<KS, RY>;
+  constexpr int R = KS / 2;
+  RowPart r;
+  r.pofs = c.plane * pstride;
+  r.h = c.h;
   // class_len(n, r, d) = (n - r + d - 1) / d
-  b.Ly = fast_div((uint32_t)(s.H - c.ry + s.dil - 1), fdil);
-  b.Lx = fast_div((uint32_t)(s.W - c.rx + s.dil - 1), fdil);
-  b.rc0 = c.by * G::RY;
-  b.cc0 = c.bx * G::RX;
-  b.valid = b.rc0 < b.Ly && b.cc0 < b.Lx;
-  b.rc1 = min(b.rc0 + G::RY, b.Ly);
-  b.cc1 = min(b.cc0 + G::RX, b.Lx);
-  b.hy0 = window_start(b.rc0, b.Ly, KS);
-  b.HR = window_start(b.rc1 - 1, b.Ly, KS) + KS - b.hy0;
-  b.hx0 = window_start(b.cc0, b.Lx, KS);
-  b.cmax = b.Lx - 1 - b.hx0;
-  return b;
+  r.Ly = fast_div((uint32_t)(s.H - c.ry + s.dil - 1), fdil);
+  r.rc0 = c.by * G::RY;
+  r.ok = r.rc0 < r.Ly;
+  r.rc1 = min(r.rc0 + G::RY, r.Ly);
+  r.hy0 = window_start(r.rc0, r.Ly, KS);
+  r.HR = window_start(r.rc1 - 1, r.Ly, KS) + KS - r.hy0;
+  r.tci0 = r.rc0 + ty * G::TY;
+  r.Y0 = window_start(r.tci0, r.Ly, KS);
+  r.inner = r.tci0 >= R && r.tci0 + G::TY - 1 + R <= r.Ly - 1;
+  r.hrow = (unsigned)((c.ry + r.hy0 * s.dil) * s.W) * (unsigned)(kHeadDim * sizeof(T));
+  r.ry = c.ry;
+  return r;
+}
+
+template <typename T, int KS>
+__device__ __forceinline__ ColPart col_part(const BlockCursor &c, const Shape &s,
+                                            const FastDiv &fdil, int tx, int lc) {
+  using G = Geometry<KS>;
+  constexpr int R = KS / 2;
+  ColPart q;
+  q.Lx = fast_div((uint32_t)(s.W - c.rx + s.dil - 1), fdil);
+  q.cc0 = c.bx * G::RX;
+  q.ok = q.cc0 < q.Lx;
+  q.cc1 = min(q.cc0 + G::RX, q.Lx);
+  q.hx0 = window_start(q.cc0, q.Lx, KS);
+  q.cmax = q.Lx - 1 - q.hx0;
+  q.tcj0 = q.cc0 + tx * G::TX;
+  q.X0 = window_start(q.tcj0, q.Lx, KS);
+  q.inner = q.tcj0 >= R && q.tcj0 + G::TX - 1 + R <= q.Lx - 1;
+  q.hcol = (unsigned)(c.rx + q.hx0 * s.dil) * (unsigned)(kHeadDim * sizeof(T));
+  q.rx = c.rx;
+  return q;
+}
+
+// In-plane pixel index of this lane's query (block row lr, block column lc),
+// clamped into a ragged block: such lanes recompute a real query and store
+// nothing.
+__device__ __forceinline__ int query_pixel(const RowPart &r, const ColPart &c, const Shape &s,
+                                           int lr, int lc) {
+  const int ci = r.rc0 + min(lr, r.rc1 - 1 - r.rc0);
+  const int cj = c.cc0 + min(lc, c.cc1 - 1 - c.cc0);
+  return (int)__umul24(r.ry + __umul24((unsigned)ci, (unsigned)s.dil), (unsigned)s.W) + c.rx +
+         (int)__umul24((unsigned)cj, (unsigned)s.dil);
 }
 
 // Copy a block's K and V halo into one LDS buffer with the direct
 // global->LDS path: 16 bytes per lane, lane i of an instruction lands at
 // base + 16*i, so each instruction fills 64 consecutive 16-byte slots.  Slot
 // (pixel, p) of the buffer holds logical chunk p ^ swz(column) of the pixel.
-template <typename T, int KS>
+template <typename T, int KS, int RY>
 __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__restrict__ v,
-                                            const Block &b, const Shape &s, int64_t pstride,
+                                            const RowPart &r, const ColPart &c, const Shape &s,
                                             char *kbuf, char *vbuf, int wave, int lane) {
-  using G = Geometry<KS>;
+  using G = Geometry<KS, RY>;
   constexpr int NI = (G::PIX * 4 + 63) / 64;  // instructions per tensor (last one partial)
   constexpr int NW = G::NTILE;
   constexpr unsigned PB = kHeadDim * sizeof(T);  // bytes per pixel
-  // halo origin, as a byte offset within the plane (planes are < 2^24 pixels)
-  const unsigned org = (unsigned)(b.org + b.hy0 * s.dil * s.W + b.hx0 * s.dil) * PB;
-  const char *kb0 = (const char *)(k + b.plane * pstride) + org;
-  const char *vb0 = (const char *)(v + b.plane * pstride) + org;
+  const unsigned org = r.hrow + c.hcol;  // halo origin within the plane
+  const char *kb0 = (const char *)(k + r.pofs) + org;
+  const char *vb0 = (const char *)(v + r.pofs) + org;
   const unsigned rowb = (unsigned)s.dil * (unsigned)s.W * PB;
   const unsigned colb = (unsigned)s.dil * PB;
   if constexpr (G::HCM == 16) {
@@ -176,15 +231,16 @@ __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__
     // of the address is fixed per lane, the row part is uniform and shared by
     // the K and V copies of the row
     const int col = lane >> 2, lch = (lane & 3) ^ ((col >> 1) & 3);
-    const unsigned coff = (unsigned)min(col, b.cmax) * colb + lch * 16;
+    unsigned coff = (unsigned)min(col, c.cmax) * colb + lch * 16;
+    asm volatile("" : "+v"(coff));  // keep the row part a scalar base, not refactored
 #pragma unroll
     for (int j = 0; j < (G::ROWS + NW - 1) / NW; ++j) {
       const int row = wave + j * NW;
       if (row < G::ROWS) {
-        const unsigned roff = (unsigned)min(row, b.HR - 1) * rowb;
-        __builtin_amdgcn_global_load_lds((const void *)(kb0 + (roff + coff)),
+        const unsigned roff = (unsigned)min(row, r.HR - 1) * rowb;
+        __builtin_amdgcn_global_load_lds((const void *)((kb0 + roff) + coff),
                                          (lds_void *)(kbuf + row * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(vb0 + (roff + coff)),
+        __builtin_amdgcn_global_load_lds((const void *)((vb0 + roff) + coff),
                                          (lds_void *)(vbuf + row * 1024), 16, 0, 0);
       }
     }
@@ -198,8 +254,8 @@ __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__
         const int pix = slot >> 2, pch = slot & 3;
         const int row = pix / G::HCM, col = pix - row * G::HCM;
         const int lch = pch ^ ((col >> 1) & 3);
-        const unsigned off = (unsigned)min(row, b.HR - 1) * rowb +
-                             (unsigned)min(col, b.cmax) * colb + lch * 16;
+        const unsigned off = (unsigned)min(row, r.HR - 1) * rowb +
+                             (unsigned)min(col, c.cmax) * colb + lch * 16;
         char *dst = (isv ? vbuf : kbuf) + (slot - lane) * 16;
         if (pix < G::PIX)
           __builtin_amdgcn_global_load_lds((const void *)((isv ? vb0 : kb0) + off),
@@ -224,31 +280,32 @@ __device__ __forceinline__ int table_index(int e) {
                                                                     : -2;
 }
 
-template <int KS> struct TableRegs {
-  static constexpr int N = (Geometry<KS>::NTAB + Geometry<KS>::THREADS - 1) / Geometry<KS>::THREADS;
+template <int KS, int RY> struct TableRegs {
+  static constexpr int N =
+      (Geometry<KS, RY>::NTAB + Geometry<KS, RY>::THREADS - 1) / Geometry<KS, RY>::THREADS;
 };
 
 // Raw rpb values of this thread's entries for head h (loads are unconditional
 // -- margin entries read entry 0 -- so they never need an early wait).
-template <typename T, int KS>
+template <typename T, int KS, int RY>
 __device__ __forceinline__ void load_tables(const T *__restrict__ rpb, int h, int tid,
-                                            T (&reg)[TableRegs<KS>::N]) {
-  using G = Geometry<KS>;
+                                            T (&reg)[TableRegs<KS, RY>::N]) {
+  using G = Geometry<KS, RY>;
   if (rpb == nullptr) return;
 #pragma unroll
-  for (int it = 0; it < TableRegs<KS>::N; ++it) {
+  for (int it = 0; it < TableRegs<KS, RY>::N; ++it) {
     const int e = min(tid + it * G::THREADS, G::NTAB - 1);
     const int idx = max(table_index<KS>(e), 0);
     reg[it] = rpb[(int64_t)h * G::SIDE * G::SIDE + idx];
   }
 }
 
-template <typename T, int KS>
+template <typename T, int KS, int RY>
 __device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
-                                             const T (&reg)[TableRegs<KS>::N]) {
-  using G = Geometry<KS>;
+                                             const T (&reg)[TableRegs<KS, RY>::N]) {
+  using G = Geometry<KS, RY>;
 #pragma unroll
-  for (int it = 0; it < TableRegs<KS>::N; ++it) {
+  for (int it = 0; it < TableRegs<KS, RY>::N; ++it) {
     const int e = tid + it * G::THREADS;
     if (e < G::NTAB) {
       const int idx = table_index<KS>(e);
@@ -259,69 +316,118 @@ __device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
   }
 }
 
-// In-plane pixel index of this lane's query in block b: block row lr, block
-// column lc, clamped into a ragged block (such lanes recompute a real query
-// and store nothing).  Planes hold fewer than 2^24 pixels, so 24-bit
-// multiplies suffice.
-__device__ __forceinline__ int query_pixel(const Block &b, const Shape &s, int lr, int lc) {
-  const int ci = b.rc0 + min(lr, b.rc1 - 1 - b.rc0);
-  const int cj = b.cc0 + min(lc, b.cc1 - 1 - b.cc0);
-  return b.org + (int)__umul24((unsigned)ci, (unsigned)(s.dil * s.W)) +
-         (int)__umul24((unsigned)cj, (unsigned)s.dil);
-}
-
-// The 16-byte Q slice (channels 8g..8g+7) of the query at pixel pix.
+// The 16-byte Q slice (channels 8g..8g+7) of the query at in-plane pixel pix.
 template <typename T>
-__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, const Block &b, int64_t pstride,
-                                        int pix, int g) {
-  const char *qp = (const char *)(q + b.plane * pstride);
+__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, int64_t pofs, int pix, int g) {
+  const char *qp = (const char *)(q + pofs);
   return *(const u32x4 *)(qp + ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 16u));
 }
 
-// One 16-query tile of block b (this wave's), from one LDS buffer.
-// One 16-query tile of block b (this wave's), from one LDS buffer; the
-// query of this lane sits at in-plane pixel pix.
+// A lane's share of a tile's output: channels 4g..4g+3 and 16+4g..16+4g+3
+// of its query, rounded; ok is false for queries outside a ragged block.
+struct TileOut {
+  u32x4 val;
+  bool ok;
+};
+
+// Unnormalised softmax weights over the query's k*k keys, in place (the 4
+// lane groups hold disjoint keys; the denominator comes from the PV step).
+template <int KS>
+__device__ __forceinline__ void softmax_weights(f32x4 (&sc)[Geometry<KS>::NB]) {
+  constexpr int NB = Geometry<KS>::NB;
+  const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
+  mx = group_max(mx);
+  const float mc = mx * c2;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+}
+
+// 16-bit P^T operand of key rows 2j and 2j+1.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::vec p_operand(const f32x4 &s0, const f32x4 &s1) {
+  typename Mma<T>::vec pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pb[i] = static_cast<T>(s0[i]);
+    pb[4 + i] = static_cast<T>(s1[i]);
+  }
+  return pb;
+}
+
+// Accumulators of one tile's PV product: channels 4g.. (o0) and 16+4g..
+// (o1) of query ql, and the softmax denominator (o2, a product with ones).
+struct PVAcc {
+  f32x4 o0, o1, o2;
+};
+
+template <typename T>
+__device__ __forceinline__ void pv_step(PVAcc &acc, typename Mma<T>::vec w0,
+                                        typename Mma<T>::vec w1, typename Mma<T>::vec p) {
+  typename Mma<T>::vec ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
+  acc.o0 = Mma<T>::run(w0, p, acc.o0);
+  acc.o1 = Mma<T>::run(w1, p, acc.o1);
+  acc.o2 = Mma<T>::run(ones, p, acc.o2);
+}
+
+template <typename T>
+__device__ __forceinline__ TileOut finish(const PVAcc &acc, bool ok) {
+  const float inv = __builtin_amdgcn_rcpf(acc.o2[0]);
+  typedef __attribute__((ext_vector_type(4))) T vec4;
+  vec4 r0, r1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r0[i] = static_cast<T>(acc.o0[i] * inv);
+    r1[i] = static_cast<T>(acc.o1[i] * inv);
+  }
+  const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+  return TileOut{{w0[0], w0[1], w1[0], w1[1]}, ok};
+}
+
+// One 16-query tile of a block (this wave's), from one LDS buffer.
 template <typename T, int KS>
-__device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b, const Shape &s,
-                                             int64_t pstride, int pix, const char *kbuf,
-                                             const char *vbuf, const float *tab, u32x4 qraw,
-                                             int wave, int lane) {
+__device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart &c,
+                                                const char *kbuf, const char *vbuf,
+                                                const float *tab, u32x4 qraw, int lane) {
   using G = Geometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, HCM = G::HCM;
-  constexpr int R = KS / 2;
   const int ql = lane & 15, g = lane >> 4;
   const int qy = ql / TX, qx = ql % TX;
-  const int ty = wave / G::NTX, tx = wave % G::NTX;
-  const int tci0 = b.rc0 + ty * TY, tcj0 = b.cc0 + tx * TX;
-  if (tci0 >= b.rc1 || tcj0 >= b.cc1) return;  // tile outside a ragged block
-  const int Y0 = window_start(tci0, b.Ly, KS), X0 = window_start(tcj0, b.Lx, KS);
-  const int lrow0 = Y0 - b.hy0, lcol0 = X0 - b.hx0;
+  const int tci0 = r.tci0, tcj0 = c.tcj0;
+  if (tci0 >= r.rc1 || tcj0 >= c.cc1) return TileOut{{0u, 0u, 0u, 0u}, false};  // outside
+  const int Y0 = r.Y0, X0 = c.X0;
+  const int lrow0 = Y0 - r.hy0, lcol0 = X0 - c.hx0;
   const vec qv = __builtin_bit_cast(vec, qraw);
-  const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
 
   // S^T rows: key (Y0 + a, X0 + 4g + i) against query ql, i = 0..3.
   const int kcol = lcol0 + ql;
   const u32x4 *kb =
       (const u32x4 *)(kbuf + (lrow0 * HCM + kcol) * 64) + (g ^ ((kcol >> 1) & 3));
   f32x4 sc[NB];
-  const bool interior = tci0 - R >= 0 && tci0 + TY - 1 + R <= b.Ly - 1 && tcj0 - R >= 0 &&
-                        tcj0 + TX - 1 + R <= b.Lx - 1;
-  if (interior) {
+  if (r.inner && c.inner) {
     const float *tb = tab + (TY - 1 - qy) * G::IW + (TX + 4 * g - qx);
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
-      f32x4 c;
+      f32x4 cin;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = tb[a * G::IW + i];
-      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
+      for (int i = 0; i < 4; ++i) cin[i] = tb[a * G::IW + i];
+      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, cin);
     }
   } else {
     // The query's window starts sy, sx lie TY-1 resp. TX-1 at most past the
     // tile's Y0, X0, so key rows TY-1..k-1 of the key block are inside every
     // lane's row window: only the first and last TY-1 rows need a row test.
-    const int ci = min(tci0 + qy, b.rc1 - 1), cj = min(tcj0 + qx, b.cc1 - 1);
-    const int sy = window_start(ci, b.Ly, KS), sx = window_start(cj, b.Lx, KS);
+    const int ci = min(tci0 + qy, r.rc1 - 1), cj = min(tcj0 + qx, c.cc1 - 1);
+    const int sy = window_start(ci, r.Ly, KS), sx = window_start(cj, c.Lx, KS);
     const int rowrel = Y0 - sy, colrel = X0 + 4 * g - sx;
     int bidx = G::BOFF + (Y0 - ci + KS - 1) * SIDE + (X0 + 4 * g - cj + KS - 1);
     asm volatile("" : "+v"(bidx));  // one base register; the reads use immediate offsets
@@ -339,48 +445,29 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
       const bool rtest = !(a >= TY - 1 && a <= KS - 1);
       float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
       if (rtest) asm volatile("" : "+v"(rcap));
-      f32x4 c;
+      f32x4 cin;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        c[i] = rtest ? fminf(fminf(bb[a * SIDE + i], ccap[i]), rcap)
-                     : fminf(bb[a * SIDE + i], ccap[i]);
-      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, c);
+        cin[i] = rtest ? fminf(fminf(bb[a * SIDE + i], ccap[i]), rcap)
+                       : fminf(bb[a * SIDE + i], ccap[i]);
+      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, cin);
     }
   }
 
-  // softmax over the query's k*k keys: the 4 lane groups hold disjoint keys
-  float mx = -INFINITY;
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
-  mx = group_max(mx);
-  const float mc = mx * c2;
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+  softmax_weights<KS>(sc);
 
   // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA).  As a source
   // of the transposing read, lane (g, 4k + qd) reads channels 4qd..4qd+3
   // (+16 for the second channel block) of key column X0 + 4g + k.
   const int vcol = lcol0 + 4 * g + (ql >> 2), qd = ql & 3, vs = (vcol >> 1) & 3;
-  const char *vrow = vbuf + (lrow0 * HCM + vcol) * 64 + 8 * (qd & 1);
+  const char *vrow = vbuf + (lrow0 * G::HCM + vcol) * 64 + 8 * (qd & 1);
   const char *va0 = vrow + 16 * ((qd >> 1) ^ vs);
   const char *va1 = vrow + 16 * (((qd >> 1) | 2) ^ vs);
-  vec ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
+  PVAcc acc{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int j = 0; j < NB / 2; ++j) {
-    vec pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = static_cast<T>(sc[2 * j][i]);
-      pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
-    }
-    constexpr int RB = HCM * 64;  // bytes per staged row
+    const vec pb = p_operand<T>(sc[2 * j], sc[2 * j + 1]);
+    constexpr int RB = G::HCM * 64;  // bytes per staged row
     const u32x2 a0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (lds_s16x4 *)(va0 + (2 * j) * RB)));
     const u32x2 a1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -389,36 +476,29 @@ __device__ __forceinline__ void compute_tile(T *__restrict__ out, const Block &b
                                                    (lds_s16x4 *)(va1 + (2 * j) * RB)));
     const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                    (lds_s16x4 *)(va1 + (2 * j + 1) * RB)));
-    const u32x4 w0 = {a0[0], a0[1], a1[0], a1[1]};
-    const u32x4 w1 = {b0[0], b0[1], b1[0], b1[1]};
-    o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
-    o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
-    o2 = Mma<T>::run(ones, pb, o2);
+    pv_step<T>(acc, __builtin_bit_cast(vec, u32x4{a0[0], a0[1], a1[0], a1[1]}),
+               __builtin_bit_cast(vec, u32x4{b0[0], b0[1], b1[0], b1[1]}), pb);
   }
+  return finish<T>(acc, tci0 + qy < r.rc1 && tcj0 + qx < c.cc1);
+}
 
-  // lane holds channels 4g..4g+3 (o0) and 16+4g..16+4g+3 (o1) of query ql
-  if (tci0 + qy < b.rc1 && tcj0 + qx < b.cc1) {
-    const float inv = __builtin_amdgcn_rcpf(o2[0]);
-    typedef __attribute__((ext_vector_type(4))) T vec4;
-    vec4 r0, r1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r0[i] = static_cast<T>(o0[i] * inv);
-      r1[i] = static_cast<T>(o1[i] * inv);
-    }
-    char *o = (char *)(out + b.plane * pstride) +
-              ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u);
-    *(u32x2 *)o = __builtin_bit_cast(u32x2, r0);
-    *(u32x2 *)(o + 16 * sizeof(T)) = __builtin_bit_cast(u32x2, r1);
+// Writes a lane's TileOut to the query at in-plane pixel pix.
+template <typename T>
+__device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, int pix, int g,
+                                          const TileOut &t) {
+  if (t.ok) {
+    char *o = (char *)(out + pofs) + ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u);
+    *(u32x2 *)o = u32x2{t.val[0], t.val[1]};
+    *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{t.val[2], t.val[3]};
   }
 }
 
-template <typename T, int KS>
-__global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
+template <typename T, int KS, int RY>
+__global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fdil, FastDiv fnbx,
     FastDiv fnby, FastDiv fheads, int nblocks) {
-  using G = Geometry<KS>;
+  using G = Geometry<KS, RY>;
   __shared__ __attribute__((aligned(16))) char kbuf0[G::PIX * 64], vbuf0[G::PIX * 64];
   __shared__ __attribute__((aligned(16))) char kbuf1[G::PIX * 64], vbuf1[G::PIX * 64];
   __shared__ float tab0[G::NTAB], tab1[G::NTAB];
@@ -434,70 +514,66 @@ __global__ __launch_bounds__(Geometry<KS>::THREADS) void fused_mfma_kernel(
   if (b0 >= b1) return;
   const bool has_rpb = rpb != nullptr;
   const int64_t pstride = (int64_t)s.H * s.W * kHeadDim;  // elements per plane
-  // this lane's query position within a block
-  const int lr = (wave / G::NTX) * G::TY + ql / G::TX, lc = (wave % G::NTX) * G::TX + ql % G::TX;
+  // this wave's tile and this lane's query position within a block
+  const int ty = wave / G::NTX, tx = wave % G::NTX;
+  const int lr = ty * G::TY + ql / G::TX, lc = tx * G::TX + ql % G::TX;
+  const int nbx = fnbx.div, nby = fnby.div;
 
   // Prefetch order for block n+1 while block n computes: its Q slice (and,
   // when the head changes, its bias-table values) first, then the K/V DMA;
   // nothing consumes them before the end-of-block barrier, so the loads
   // overlap the whole compute of block n.
-  T treg[TableRegs<KS>::N];
+  T treg[TableRegs<KS, RY>::N];
   BlockCursor cc = cursor_at(b0, s.dil, fdil, fnbx, fnby, fheads);
-  Block cur = block_of<KS>(cc, s, fdil);
-  int pcur = query_pixel(cur, s, lr, lc);
-  u32x4 qcur = load_q<T>(q, cur, pstride, pcur, g);
-  load_tables<T, KS>(rpb, cur.h, tid, treg);
-  if (cur.valid) stage_block<T, KS>(k, v, cur, s, pstride, kbuf0, vbuf0, wave, lane);
-  store_tables<T, KS>(tab0, tid, has_rpb, treg);
-  int tab_h0 = cur.h, tab_h1 = -1;  // head whose tables each buffer holds
+  RowPart rcur = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
+  ColPart ccur = col_part<T, KS>(cc, s, fdil, tx, lc);
+  int pcur = query_pixel(rcur, ccur, s, lr, lc);
+  u32x4 qcur = load_q<T>(q, rcur.pofs, pcur, g);
+  load_tables<T, KS, RY>(rpb, rcur.h, tid, treg);
+  if (rcur.ok && ccur.ok) stage_block<T, KS, RY>(k, v, rcur, ccur, s, kbuf0, vbuf0, wave, lane);
+  store_tables<T, KS, RY>(tab0, tid, has_rpb, treg);
+  int tab_h0 = rcur.h, tab_h1 = -1;  // head whose tables each buffer holds
   __syncthreads();
-  const int nbx = fnbx.div, nby = fnby.div;
 
+  TileOut res;
+  // One block: compute the current one from buffer (kc, vc, tc) while block
+  // n+1 is staged into (kn, vn, tn).  Called with fixed arrays, so that the
+  // compiler can tell the DMA target from the buffer being read.
+  auto step = [&](const char *kc, const char *vc, const float *tc, char *kn, char *vn, float *tn,
+                  int &tab_hn, bool more) {
+    RowPart rnxt = rcur;
+    if (more && cursor_step(cc, s.dil, nbx, nby, s.heads))
+      rnxt = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
+    const ColPart cnxt = col_part<T, KS>(cc, s, fdil, tx, lc);
+    const int pnxt = query_pixel(rnxt, cnxt, s, lr, lc);
+    const u32x4 qnxt = load_q<T>(q, rnxt.pofs, pnxt, g);
+    const bool newtab = more && rnxt.h != tab_hn;
+    if (newtab) load_tables<T, KS, RY>(rpb, rnxt.h, tid, treg);
+    if (more && rnxt.ok && cnxt.ok) stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, kn, vn, wave, lane);
+    res = TileOut{{0u, 0u, 0u, 0u}, false};
+    if (rcur.ok && ccur.ok) res = compute_tile<T, KS>(rcur, ccur, kc, vc, tc, qcur, lane);
+    if (!more) return;
+    if (newtab) {
+      store_tables<T, KS, RY>(tn, tid, has_rpb, treg);
+      tab_hn = rnxt.h;
+    }
+    __syncthreads();  // also waits for the DMA (workgroup fence)
+    // the block's results leave after the barrier, so that its wait covers
+    // the next block's loads but not these stores
+    store_out<T>(out, rcur.pofs, pcur, g, res);
+    rcur = rnxt;
+    ccur = cnxt;
+    pcur = pnxt;
+    qcur = qnxt;
+  };
   // Two blocks per iteration so that each buffer is a fixed LDS array.
   for (int bi = b0; bi < b1; bi += 2) {
-    {  // block bi from buffer 0; block bi+1 into buffer 1
-      const bool more = bi + 1 < b1;
-      if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
-      const Block nxt = block_of<KS>(cc, s, fdil);
-      const int pnxt = query_pixel(nxt, s, lr, lc);
-      const u32x4 qnxt = load_q<T>(q, nxt, pstride, pnxt, g);
-      const bool newtab = more && nxt.h != tab_h1;
-      if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
-      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, pstride, kbuf1, vbuf1, wave, lane);
-      if (cur.valid)
-        compute_tile<T, KS>(out, cur, s, pstride, pcur, kbuf0, vbuf0, tab0, qcur, wave, lane);
-      if (!more) break;
-      if (newtab) {
-        store_tables<T, KS>(tab1, tid, has_rpb, treg);
-        tab_h1 = nxt.h;
-      }
-      __syncthreads();  // also waits for the DMA (workgroup fence)
-      cur = nxt;
-      pcur = pnxt;
-      qcur = qnxt;
-    }
-    {  // block bi+1 from buffer 1; block bi+2 into buffer 0
-      const bool more = bi + 2 < b1;
-      if (more) cursor_step(cc, s.dil, nbx, nby, s.heads);
-      const Block nxt = block_of<KS>(cc, s, fdil);
-      const int pnxt = query_pixel(nxt, s, lr, lc);
-      const u32x4 qnxt = load_q<T>(q, nxt, pstride, pnxt, g);
-      const bool newtab = more && nxt.h != tab_h0;
-      if (newtab) load_tables<T, KS>(rpb, nxt.h, tid, treg);
-      if (more && nxt.valid) stage_block<T, KS>(k, v, nxt, s, pstride, kbuf0, vbuf0, wave, lane);
-      if (cur.valid)
-        compute_tile<T, KS>(out, cur, s, pstride, pcur, kbuf1, vbuf1, tab1, qcur, wave, lane);
-      if (!more) break;
-      if (newtab) {
-        store_tables<T, KS>(tab0, tid, has_rpb, treg);
-        tab_h0 = nxt.h;
-      }
-      __syncthreads();
-      cur = nxt;
-      pcur = pnxt;
-      qcur = qnxt;
-    }
+    const bool more0 = bi + 1 < b1;
+    step(kbuf0, vbuf0, tab0, kbuf1, vbuf1, tab1, tab_h1, more0);
+    if (!more0) break;
+    step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < b1);
   }
+  store_out<T>(out, rcur.pofs, pcur, g, res);  // the last block
 }
 
 // Compute units of the current device (queried once per device).
@@ -514,21 +590,32 @@ int device_cus() {
   return cache[dev];
 }
 
-template <typename T, int KS>
+template <typename T, int KS, int RY>
 hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb, void *out,
                     const Shape &s, hipStream_t st) {
-  using G = Geometry<KS>;
+  using G = Geometry<KS, RY>;
   const int Lymax = class_len(s.H, 0, s.dil), Lxmax = class_len(s.W, 0, s.dil);
   const int nby = (Lymax + G::RY - 1) / G::RY, nbx = (Lxmax + G::RX - 1) / G::RX;
   const int64_t nblocks = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
   // one persistent workgroup per compute unit (its LDS holds two blocks)
   const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
-  fused_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
+  fused_mfma_kernel<T, KS, RY><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
       make_fastdiv((uint32_t)s.heads), (int)nblocks);
   return hipGetLastError();
+}
+
+// k <= 7: blocks of 32 rows (16 waves) or 28 rows (14 waves), whichever
+// covers the tallest residue class with fewer blocks (28 on a tie: less work
+// per block for the same count).
+template <typename T, int KS>
+hipError_t launch_small(const void *q, const void *k, const void *v, const void *rpb, void *out,
+                        const Shape &s, hipStream_t st) {
+  const int L = class_len(s.H, 0, s.dil);
+  if ((L + 27) / 28 <= (L + 31) / 32) return launch_t<T, KS, 28>(q, k, v, rpb, out, s, st);
+  return launch_t<T, KS, 32>(q, k, v, rpb, out, s, st);
 }
 
 template <typename T>
@@ -540,13 +627,13 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
     return hipSuccess;
   }
   switch (s.ks) {
-    case 1: return launch_t<T, 1>(q, k, v, rpb, out, s, st);
-    case 3: return launch_t<T, 3>(q, k, v, rpb, out, s, st);
-    case 5: return launch_t<T, 5>(q, k, v, rpb, out, s, st);
-    case 7: return launch_t<T, 7>(q, k, v, rpb, out, s, st);
-    case 9: return launch_t<T, 9>(q, k, v, rpb, out, s, st);
-    case 11: return launch_t<T, 11>(q, k, v, rpb, out, s, st);
-    case 13: return launch_t<T, 13>(q, k, v, rpb, out, s, st);
+    case 1: return launch_small<T, 1>(q, k, v, rpb, out, s, st);
+    case 3: return launch_small<T, 3>(q, k, v, rpb, out, s, st);
+    case 5: return launch_small<T, 5>(q, k, v, rpb, out, s, st);
+    case 7: return launch_small<T, 7>(q, k, v, rpb, out, s, st);
+    case 9: return launch_t<T, 9, default_rows(9)>(q, k, v, rpb, out, s, st);
+    case 11: return launch_t<T, 11, default_rows(11)>(q, k, v, rpb, out, s, st);
+    case 13: return launch_t<T, 13, default_rows(13)>(q, k, v, rpb, out, s, st);
   }
   *supported = false;
   return hipSuccess;
