@@ -183,3 +183,20 @@ def test_many_planes_large_grid():
     cpu, g = gpu_inputs(p, seed=10)
     note("large grid %s" % p.describe())
     compare(p, run_path("auto", p, g), cpu, idx=sample_indices(p, 60_000))
+
+
+# Whole-class maps (H == W == k*d, d a power of two) take the dense kernel.
+# These shapes give it several blocks per workgroup, blocks that end a head
+# with fewer classes than a block holds, and head changes inside one
+# workgroup's run of blocks.
+DENSE = [Problem(129, 5, 14, 14, 32, 7, 2, "bf16"), Problem(67, 5, 10, 10, 32, 5, 2, "f16"),
+         Problem(131, 7, 6, 6, 32, 3, 2, "bf16"), Problem(300, 3, 7, 7, 32, 7, 1, "f16"),
+         Problem(5, 9, 56, 56, 32, 7, 8, "bf16")]
+
+
+@pytest.mark.parametrize("p", DENSE, ids=lambda p: p.describe().replace(" ", "_"))
+def test_whole_class_maps(p):
+    cpu, g = gpu_inputs(p, seed=11)
+    for path in ("auto", "mfma"):
+        note("%s path=%s" % (p.describe(), path))
+        compare(p, run_path(path, p, g), cpu, idx=sample_indices(p, 200_000))

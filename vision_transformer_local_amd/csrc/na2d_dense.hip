@@ -10,239 +10,345 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ---------------------------------------------------------------------------
-// Whole-sub-grid windows: H == k*d and W == k*d (d a power of two).
+// Whole-class windows: H == k*d and W == k*d (d a power of two).
 //
 // Then every residue class is exactly k x k and every query's clamped window
-// is its entire class, so the operator is dense attention with bias inside
+// is its entire class, so the operator is dense attention with a bias inside
 // each class (the NAT README's self-attention equivalence, applied per
-// class).  The class is flattened: its N = k*k queries form ceil(N/16)
-// tiles and its N keys NKB blocks of 16 (padded with zero pixels, masked
-// with -inf).  The accumulator input (bias * sqrt(D), -inf on padding) of a
-// (tile, key block) pair is the same for every class of a head, so each wave
-// computes it once for the tiles it owns.
+// class).  A class is flattened: its N = k*k queries form NT tiles of 16 and
+// its N keys NKB blocks of 16; key slots past N hold copies of the last key
+// and get -inf, query slots past N recompute the last query and store
+// nothing.  The MFMA accumulator input of a (tile, key block) pair -- bias *
+// sqrt(D), -inf on padding -- is the same for every class of a head: it sits
+// in an LDS table, one 16-byte entry per lane, rebuilt when the head changes.
 //
-// A workgroup owns SG consecutive classes of one head, ordered (b, ry, rx)
-// with rx fastest, so for d > 1 the classes of one workgroup read whole
-// pixel rows.
+// Work decomposition: classes are numbered head-major, (h, b, ry, rx) with
+// rx fastest, and cut into blocks of SG classes that never straddle two
+// heads.  Workgroups are persistent (one per compute unit), walk a contiguous
+// run of blocks and keep two LDS buffers: while the 16 waves compute block i
+// (TPW tiles each) from one buffer, the direct global->LDS path fills the
+// other with block i+1.  K and V are staged as [class][key slot] 64-byte
+// pixels, the 16-byte chunks XOR-swizzled by slot; the PV product reads V^T
+// with ds_read_b64_tr_b16 as in the general kernel.
 template <int KS> struct DenseGeometry {
   static constexpr int N = KS * KS;
-  static constexpr int NT = (N + 15) / 16;             // query tiles per class
-  static constexpr int NKB = ((N + 15) / 16 + 1) & ~1; // key blocks (even)
-  static constexpr int NK = NKB * 16;                  // padded keys per class
-  static constexpr int SG = 8;                         // classes per workgroup
-  static constexpr int NTW = (NT + kWaves - 1) / kWaves;  // tiles per wave
-  static constexpr int VSTR = NK + 2;  // V^T channel stride (elements): odd dword count
+  static constexpr int NT = (N + 15) / 16;              // query tiles per class
+  static constexpr int NKB = ((N + 15) / 16 + 1) & ~1;  // key blocks (even: PV pairs)
+  static constexpr int NK = NKB * 16;                   // key slots per class
+  static constexpr int WAVES = 16, THREADS = WAVES * 64;
+  static constexpr int TPW = KS == 3 ? 1 : 2;           // tiles per wave
+  static constexpr int SG = WAVES * TPW / NT;           // classes per block
+  static constexpr int CB = NK * 64;                    // bytes per class and tensor
+  static constexpr int DPT = SG * NK / 16;              // DMA instructions per tensor
+  static constexpr int DPW = 2 * DPT / WAVES;           // ... per wave
+  static constexpr int NCT = NT * NKB * 64 * 4;         // accumulator-table floats
   static constexpr int SIDE = 2 * KS - 1;
+  static_assert(SG * NT == WAVES * TPW, "blocks hold whole classes");
+  static_assert(DPW * WAVES == 2 * DPT, "DMA instructions spread evenly");
+  static_assert(2 * 2 * SG * CB + NCT * 4 <= 160 * 1024, "LDS");
 };
 
+// Byte offset of pixel (0, 0) of class jh (numbered (b, ry, rx), rx fastest)
+// of head h.
+__device__ __forceinline__ int64_t class_base(int h, int jh, const Shape &s, int log2d,
+                                              int64_t plane_bytes, unsigned pixel_bytes) {
+  const int d = s.dil;
+  const int rx = jh & (d - 1), ry = (jh >> log2d) & (d - 1), b = jh >> (2 * log2d);
+  const int64_t plane = (int64_t)b * s.heads + h;
+  return plane * plane_bytes + (int64_t)(ry * s.W + rx) * pixel_bytes;
+}
+
+// Block id -> (head, first class within the head, classes in the block).
+struct DenseBlock {
+  int h, j0, n;
+};
+
+template <int KS>
+__device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &fbph, int per_head) {
+  using G = DenseGeometry<KS>;
+  DenseBlock b;
+  b.h = (int)fast_div((uint32_t)id, fbph);
+  b.j0 = (id - b.h * (int)fbph.div) * G::SG;
+  b.n = min(G::SG, per_head - b.j0);
+  return b;
+}
+
 template <typename T, int KS>
-__global__ __launch_bounds__(kThreads) void dense_mfma_kernel(
+__global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fitems, int total,
-    int log2d) {
+    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fbph, int per_head,
+    int nblocks, int log2d) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
-  constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, SG = G::SG, NTW = G::NTW;
-  constexpr int VSTR = G::VSTR, SIDE = G::SIDE;
-  constexpr int D = kHeadDim;
-  constexpr int VCLS = D * VSTR / 2;  // dwords of V^T per class
+  constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, TPW = G::TPW, SG = G::SG;
+  constexpr int CB = G::CB, DPT = G::DPT, DPW = G::DPW, SIDE = G::SIDE;
+  constexpr int WAVES = G::WAVES, THREADS = G::THREADS;
+  constexpr unsigned PB = kHeadDim * sizeof(T);  // bytes per pixel
+  __shared__ __attribute__((aligned(16))) char kbuf0[SG * CB], vbuf0[SG * CB];
+  __shared__ __attribute__((aligned(16))) char kbuf1[SG * CB], vbuf1[SG * CB];
+  __shared__ __attribute__((aligned(16))) float ctab[G::NCT];  // [tile][key block][lane][4]
 
-  __shared__ u32x4 k_lds[SG * NK * 4];         // [class][key][chunk ^ swz]
-  __shared__ unsigned int vt_lds[SG * VCLS];   // [class][channel][key pair]
-  __shared__ float b_lds[SIDE * SIDE];         // bias * sqrt(D)
-
-  const int tid = threadIdx.x;
-  const int dil = s.dil;
-  const uint32_t id = xcd_contiguous_id(blockIdx.x, total);
-  const int h = fast_div(id, fitems);
-  const int per_head = s.B << (2 * log2d);  // classes of one head
-  const int c0 = (id - h * fitems.div) * SG;
-  const int ncls = min(SG, per_head - c0);
-  const int64_t hw = (int64_t)s.H * s.W;
-
-  // class c of this workgroup -> (plane, ry, rx)
-  // (dilation is a power of two here, so the decode is shifts and masks)
-  auto class_pos = [&](int c, int64_t &plane, int &ry, int &rx) {
-    const int j = c0 + c;
-    rx = j & (dil - 1);
-    ry = (j >> log2d) & (dil - 1);
-    plane = (int64_t)(j >> (2 * log2d)) * s.heads + h;
-  };
-
-  // ---- stage: all loads first (unconditional, clamped), then LDS writes --
-  // A thread owns one (key, 16-byte chunk) slot of a class and visits the
-  // workgroup's classes; a load address is a uniform per-class base plus the
-  // thread's fixed 32-bit byte offset.
-  constexpr int KPC = NK * 4, KCPP = kThreads / KPC;        // K items per class, classes/pass
-  constexpr int VPC = (NK / 2) * 4, VCPP = kThreads / VPC;  // V items per class, classes/pass
-  static_assert(KCPP * KPC == kThreads && VCPP * VPC == kThreads, "class items must tile 256");
-  constexpr int KIT = SG / KCPP, VIT = SG / VCPP;
-  const unsigned rowb = (unsigned)dil * (unsigned)s.W * (unsigned)(D * sizeof(T));
-  const unsigned colb = (unsigned)dil * (unsigned)(D * sizeof(T));
-  // byte offset of pixel (0, 0) of class c (clamped to the workgroup's classes)
-  auto cls_off = [&](int c) -> int64_t {
-    const int j = c0 + min(c, ncls - 1);
-    const int rxx = j & (dil - 1), ryy = (j >> log2d) & (dil - 1);
-    const int64_t pl = (int64_t)(j >> (2 * log2d)) * s.heads + h;
-    return ((pl * hw + (int64_t)ryy * s.W + rxx) * D) * (int64_t)sizeof(T);
-  };
-  auto pick = [&](int it, int cpp, int sub) -> int64_t {
-    int64_t o = cls_off(it * cpp);
-#pragma unroll
-    for (int u = 1; u < 4; ++u)
-      if (u < cpp && sub == u) o = cls_off(it * cpp + u);
-    return o;
-  };
-
-  const int ksub = tid / KPC, kkey = (tid % KPC) >> 2, kch = tid & 3;
-  const int kkc = min(kkey, N - 1);
-  const unsigned koff = (unsigned)(kkc / KS) * rowb + (unsigned)(kkc % KS) * colb + kch * 16;
-  u32x4 kreg[KIT];
-#pragma unroll
-  for (int it = 0; it < KIT; ++it)
-    kreg[it] = *(const u32x4 *)((const char *)k + pick(it, KCPP, ksub) + koff);
-
-  const int vsub = tid / VPC, vpr = (tid % VPC) >> 2, vch = tid & 3;
-  const int vk0 = min(2 * vpr, N - 1), vk1 = min(2 * vpr + 1, N - 1);
-  const unsigned voff0 = (unsigned)(vk0 / KS) * rowb + (unsigned)(vk0 % KS) * colb + vch * 16;
-  const unsigned voff1 = (unsigned)(vk1 / KS) * rowb + (unsigned)(vk1 % KS) * colb + vch * 16;
-  u32x4 va[VIT], vb2[VIT];
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const char *base = (const char *)v + pick(it, VCPP, vsub);
-    va[it] = *(const u32x4 *)(base + voff0);
-    vb2[it] = *(const u32x4 *)(base + voff1);
-  }
-  for (int e = tid; e < SIDE * SIDE; e += kThreads)
-    b_lds[e] = rpb != nullptr ? Elem<T>::to_f(rpb[(int64_t)h * SIDE * SIDE + e]) * kSqrtD : 0.f;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  {
-    // padding keys must hold finite values: zeros
-    u32x4 *dst = k_lds + (ksub * NK + kkey) * 4 + (kch ^ ((kkey >> 1) & 3));
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) dst[it * KCPP * NK * 4] = kkey < N ? kreg[it] : zero4;
-  }
-  {
-    unsigned int *dst = vt_lds + vsub * VCLS + (vch * 8) * (VSTR / 2) + vpr;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const u32x4 a = 2 * vpr < N ? va[it] : zero4, b = 2 * vpr + 1 < N ? vb2[it] : zero4;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dst[it * VCPP * VCLS + (2 * w) * (VSTR / 2)] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-        dst[it * VCPP * VCLS + (2 * w + 1) * (VSTR / 2)] =
-            __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
-      }
-    }
-  }
-  __syncthreads();
-
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
+  const int wg = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int b0 = (int)((int64_t)nblocks * wg / gridDim.x);
+  const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
+  if (b0 >= b1) return;
+  const int d = s.dil;
+  const int64_t plane_bytes = (int64_t)s.H * s.W * PB;
+  const unsigned rowb = (unsigned)d * (unsigned)s.W * PB, colb = (unsigned)d * PB;
+
+  // ---- per-lane constants: DMA slots, query positions ----
+  // DMA instruction i = wave + WAVES * m covers 16 key slots (4 lanes each)
+  // of one class of one tensor; lane l lands at slot kg*16 + l/4, 16-byte
+  // position l&3, which holds logical chunk (l&3) ^ swz(slot).
+  unsigned doff[DPW];
+#pragma unroll
+  for (int m = 0; m < DPW; ++m) {
+    const int i = wave + WAVES * m, it = i % DPT;
+    const int kg = it % (NK / 16);
+    const int slot = kg * 16 + (lane >> 2), key = min(slot, N - 1);
+    const int lch = (lane & 3) ^ ((slot >> 1) & 3);
+    doff[m] = (unsigned)(key / KS) * rowb + (unsigned)(key % KS) * colb + lch * 16u;
+  }
+  // this wave's tiles: tile t = wave*TPW + u of the block is tile t % NT of
+  // class t / NT; lane query slot tt*16 + ql (clamped to the last query)
+  unsigned qoff[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tt = (wave * TPW + u) % NT;
+    const int nq = min(tt * 16 + ql, N - 1);
+    qoff[u] = (unsigned)(nq / KS) * rowb + (unsigned)(nq % KS) * colb;
+  }
+
+  // accumulator table for head h: entry (tt, kb, lane, i) = bias * sqrt(D)
+  // of key slot kb*16 + 4g + i against query slot tt*16 + ql, -inf on
+  // padding keys
+  constexpr int CPT = (G::NCT + THREADS - 1) / THREADS;  // entries per thread
+  auto ctab_src = [&](int e) -> int {  // rpb index of entry e, or -1 for -inf
+    const int i = e & 3, l = (e >> 2) & 63, kb = (e >> 8) % NKB, tt = (e >> 8) / NKB;
+    const int nk = kb * 16 + 4 * (l >> 4) + i;
+    const int nq = min(tt * 16 + (l & 15), N - 1);
+    if (nk >= N) return -1;
+    return (nk / KS - nq / KS + KS - 1) * SIDE + (nk % KS - nq % KS + KS - 1);
+  };
+  T craw[CPT];
+  auto load_ctab = [&](int h) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int e = min(tid + m * THREADS, G::NCT - 1);
+      craw[m] = rpb != nullptr ? rpb[(int64_t)h * SIDE * SIDE + max(ctab_src(e), 0)]
+                               : static_cast<T>(0.0f);
+    }
+  };
+  auto store_ctab = [&]() {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int e = tid + m * THREADS;
+      if (e < G::NCT) ctab[e] = ctab_src(e) < 0 ? -INFINITY : Elem<T>::to_f(craw[m]) * kSqrtD;
+    }
+  };
+
+  // ---- staging of one block into a buffer (uniform per-class bases) ----
+  auto stage = [&](const DenseBlock &bk, char *kb, char *vb) {
+#pragma unroll
+    for (int m = 0; m < DPW; ++m) {
+      const int i = wave + WAVES * m;
+      const bool isv = i >= DPT;
+      const int it = i % DPT, c = it / (NK / 16), kg = it % (NK / 16);
+      const int64_t base = class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, plane_bytes, PB);
+      const char *src = (const char *)(isv ? v : k) + base;
+      char *dst = (isv ? vb : kb) + c * CB + kg * 1024;
+      __builtin_amdgcn_global_load_lds((const void *)(src + doff[m]), (lds_void *)dst, 16, 0, 0);
+    }
+  };
+  // byte offset of this wave's tile u query pixel in block bk
+  auto tile_base = [&](const DenseBlock &bk, int u) -> int64_t {
+    const int c = (wave * TPW + u) / NT;
+    return class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, plane_bytes, PB);
+  };
+  auto load_q = [&](const DenseBlock &bk, int u) -> u32x4 {
+    return *(const u32x4 *)((const char *)q + tile_base(bk, u) + qoff[u] + g * 16u);
+  };
+
   const float c2 = kLog2e / kSqrtD;
-  const int chA = 8 * (ql >> 2) + (ql & 3);
   vec ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
 
-  // accumulator inputs of this wave's tiles
-  f32x4 cint[NTW][NKB];
+  // LDS byte offsets are formed as one integer per lane and kept opaque, so
+  // that every read is (array + offset) + constant: the compiler then still
+  // knows which array it reads and does not wait for the DMA into the other
+  // buffer before it.
+  auto opaque = [](int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  // one tile: returns the lane's 8 output channels, rounded
+  auto tile = [&](const char *kb, const char *vb, int u, u32x4 qraw) -> u32x4 {
+    const int t = wave * TPW + u, c = t / NT, tt = t % NT;
+    const vec qv = __builtin_bit_cast(vec, qraw);
+    // key slot kbk*16 + ql, logical chunk g (the swizzle does not depend on kbk)
+    const char *kp = kb + opaque(c * CB + ql * 64 + 16 * (g ^ ((ql >> 1) & 3)));
+    const f32x4 *ct = (const f32x4 *)((const char *)ctab + opaque(((tt * NKB) * 64 + lane) * 16));
+    f32x4 sc[NKB];
 #pragma unroll
-  for (int tw = 0; tw < NTW; ++tw) {
-    const int nq = min((wave + tw * kWaves) * 16 + ql, N - 1);
-    const int qa = nq / KS, qb = nq % KS;
+    for (int kbk = 0; kbk < NKB; ++kbk) {
+      const u32x4 kv = *(const u32x4 *)(kp + kbk * 1024);
+      sc[kbk] = Mma<T>::run(__builtin_bit_cast(vec, kv), qv, ct[kbk * 64]);
+    }
+    float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kbk][i]);
+    mx = group_max(mx);
+    const float mc = mx * c2;
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[kbk][i] = __builtin_amdgcn_exp2f(fmaf(sc[kbk][i], c2, -mc));
+    // out^T = V^T . P^T, 32 keys per MFMA: P^T rows 8g'..8g'+7 are key slots
+    // 32j + 4g' + 0..3 and 32j + 16 + 4g' + 0..3.  As a source of the
+    // transposing read, lane (g, 4kk + qd) reads channels 4qd..4qd+3 (+16
+    // for the second channel block) of slot 32j + 4g + kk (+16).
+    // slot 32j + 4g + kk (+16 for the second half); its swizzle does not
+    // depend on j
+    const int qd = ql & 3, kk = ql >> 2, sl = 4 * g + kk, z = (sl >> 1) & 3;
+    const int vrow = c * CB + sl * 64 + 8 * (qd & 1);
+    const char *va = vb + opaque(vrow + 16 * ((qd >> 1) ^ z));
+    const char *vc2 = vb + opaque(vrow + 16 * (((qd >> 1) | 2) ^ z));
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NKB / 2; ++j) {
+      vec pb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int nk = kb * 16 + 4 * g + i;
-        const int ka = nk / KS, kc = nk % KS;
-        cint[tw][kb][i] = nk < N ? b_lds[(ka - qa + KS - 1) * SIDE + (kc - qb + KS - 1)] : -INFINITY;
+        pb[i] = static_cast<T>(sc[2 * j][i]);
+        pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
       }
-  }
-
-  for (int c = 0; c < ncls; ++c) {
-    int64_t plane;
-    int ry, rx;
-    class_pos(c, plane, ry, rx);
-    const u32x4 *kc = k_lds + c * NK * 4;
-    const unsigned int *vc = vt_lds + c * VCLS;
-#pragma unroll
-    for (int tw = 0; tw < NTW; ++tw) {
-      const int t = wave + tw * kWaves;
-      if (t >= NT) break;
-      const int nq0 = t * 16 + ql;
-      const int nq = min(nq0, N - 1);
-      const int64_t qoff =
-          (plane * hw + (int64_t)(ry + (nq / KS) * dil) * s.W + rx + (nq % KS) * dil) * D + g * 8;
-      const vec qv = __builtin_bit_cast(vec, *(const u32x4 *)(q + qoff));
-      f32x4 sc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int key = kb * 16 + ql;
-        sc[kb] = Mma<T>::run(__builtin_bit_cast(vec, kc[key * 4 + (g ^ ((key >> 1) & 3))]), qv,
-                             cint[tw][kb]);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][i]);
-      mx = group_max(mx);
-      const float mc = mx * c2;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[kb][i] = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c2, -mc));
-      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f}, o2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < NKB / 2; ++j) {
-        vec pb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = static_cast<T>(sc[2 * j][i]);
-          pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
-        }
-        // keys 32j + 4g .. +3 and 32j + 16 + 4g .. +3 of channel chA (+4)
-        const unsigned int *r = vc + chA * (VSTR / 2) + 16 * j + 2 * g;
-        constexpr int C4 = 4 * (VSTR / 2);
-        const u32x4 w0 = {r[0], r[1], r[8], r[9]};
-        const u32x4 w1 = {r[C4], r[C4 + 1], r[C4 + 8], r[C4 + 9]};
-        o0 = Mma<T>::run(__builtin_bit_cast(vec, w0), pb, o0);
-        o1 = Mma<T>::run(__builtin_bit_cast(vec, w1), pb, o1);
-        o2 = Mma<T>::run(ones, pb, o2);
-      }
-      if (nq0 < N) {
-        const float inv = __builtin_amdgcn_rcpf(o2[0]);
-        vec res;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          res[i] = static_cast<T>(o0[i] * inv);
-          res[4 + i] = static_cast<T>(o1[i] * inv);
-        }
-        *(u32x4 *)(out + qoff) = __builtin_bit_cast(u32x4, res);
-      }
+      const u32x2 a0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va + 2048 * j)));
+      const u32x2 a1 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va + 2048 * j + 1024)));
+      const u32x2 c0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vc2 + 2048 * j)));
+      const u32x2 c1 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vc2 + 2048 * j + 1024)));
+      o0 = Mma<T>::run(__builtin_bit_cast(vec, u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, o0);
+      o1 = Mma<T>::run(__builtin_bit_cast(vec, u32x4{c0[0], c0[1], c1[0], c1[1]}), pb, o1);
+      o2 = Mma<T>::run(ones, pb, o2);
     }
+    const float inv = __builtin_amdgcn_rcpf(o2[0]);
+    typedef __attribute__((ext_vector_type(4))) T vec4;
+    vec4 r0, r1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r0[i] = static_cast<T>(o0[i] * inv);
+      r1[i] = static_cast<T>(o1[i] * inv);
+    }
+    const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+    return u32x4{w0[0], w0[1], w1[0], w1[1]};
+  };
+  // whether this lane's query of tile u exists in block bk
+  auto tile_ok = [&](const DenseBlock &bk, int u) -> bool {
+    const int t = wave * TPW + u, c = t / NT, tt = t % NT;
+    return c < bk.n && tt * 16 + ql < N;
+  };
+  auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok) {
+    if (ok) {
+      char *o = (char *)out + tile_base(bk, u) + qoff[u] + g * 8u;
+      *(u32x2 *)o = u32x2{val[0], val[1]};
+      *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{val[2], val[3]};
+    }
+  };
+
+  // ---- prologue ----
+  DenseBlock cur = dense_block<KS>(b0, fbph, per_head);
+  u32x4 qcur[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) qcur[u] = load_q(cur, u);
+  load_ctab(cur.h);
+  stage(cur, kbuf0, vbuf0);
+  store_ctab();
+  int ctab_h = cur.h;
+  __syncthreads();
+
+  u32x4 res[TPW];
+  bool rok[TPW];
+  // One block from (kc, vc) while the next is staged into (kn, vn); called
+  // with fixed arrays so that the compiler can tell the DMA target from the
+  // buffer being read.
+  auto step = [&](int bi, const char *kc, const char *vc, char *kn, char *vn) {
+    const bool more = bi + 1 < b1;
+    const DenseBlock nxt = dense_block<KS>(more ? bi + 1 : bi, fbph, per_head);
+    u32x4 qnxt[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) qnxt[u] = load_q(nxt, u);
+    const bool newtab = more && nxt.h != ctab_h;
+    if (newtab) load_ctab(nxt.h);
+    if (more) stage(nxt, kn, vn);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      rok[u] = tile_ok(cur, u);
+      res[u] = (wave * TPW + u) / NT < cur.n ? tile(kc, vc, u, qcur[u]) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (!more) return;
+    if (newtab) {
+      __syncthreads();  // every wave is done with the old table
+      store_ctab();
+      ctab_h = nxt.h;
+    }
+    __syncthreads();  // also waits for the DMA (workgroup fence)
+    // results leave after the barrier, whose wait then covers only the loads
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u]);
+    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) qcur[u] = qnxt[u];
+  };
+  for (int bi = b0; bi < b1; bi += 2) {
+    step(bi, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (bi + 1 >= b1) break;
+    step(bi + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u]);  // the last block
+}
+
+int dense_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <typename T, int KS>
 hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, hipStream_t st) {
   using G = DenseGeometry<KS>;
-  const int64_t per_head = (int64_t)s.B * s.dil * s.dil;
-  const int64_t items_per_head = (per_head + G::SG - 1) / G::SG;
-  const int64_t total = items_per_head * s.heads;
-  if (total > INT_MAX || per_head > INT_MAX) return hipErrorInvalidConfiguration;
+  const int64_t per_head = (int64_t)s.B * s.dil * s.dil;  // classes of one head
+  const int64_t bph = (per_head + G::SG - 1) / G::SG;      // blocks per head
+  const int64_t nblocks = bph * s.heads;
+  if (nblocks > INT_MAX || per_head > INT_MAX) return hipErrorInvalidConfiguration;
   int log2d = 0;
   while ((1 << log2d) < s.dil) ++log2d;
-  dense_mfma_kernel<T, KS><<<dim3((unsigned)total), kThreads, 0, st>>>(
+  const int64_t grid = nblocks < dense_cus() ? nblocks : dense_cus();
+  dense_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
-      make_fastdiv((uint32_t)items_per_head), (int)total, log2d);
+      make_fastdiv((uint32_t)bph), (int)per_head, (int)nblocks, log2d);
   return hipGetLastError();
 }
 
@@ -254,7 +360,8 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
   *supported = true;
   const bool pow2_dil = (s.dil & (s.dil - 1)) == 0;
   if ((int64_t)s.ks * s.dil != s.H || (int64_t)s.ks * s.dil != s.W || !pow2_dil ||
-      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32) {
+      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32 ||
+      (int64_t)s.H * s.W >= kMaxPlanePixels) {
     *supported = false;
     return hipSuccess;
   }
