@@ -42,7 +42,7 @@ template <int KS> struct DenseGeometry {
   static constexpr int NKB = ((N + 15) / 16 + 1) & ~1;  // key blocks (even: PV pairs)
   static constexpr int NK = NKB * 16;                   // key slots per class
   static constexpr int WAVES = 16, THREADS = WAVES * 64;
-  static constexpr int TPW = KS == 3 ? 1 : 2;           // tiles per wave
+  static constexpr int TPW = 1;                         // tiles per wave
   static constexpr int SG = WAVES * TPW / NT;           // classes per block
   static constexpr int CB = NK * 64;                    // bytes per class and tensor
   static constexpr int DPT = SG * NK / 16;              // DMA instructions per tensor

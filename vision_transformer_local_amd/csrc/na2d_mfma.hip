@@ -317,10 +317,16 @@ __device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
 }
 
 // The 16-byte Q slice (channels 8g..8g+7) of the query at in-plane pixel pix.
-template <typename T>
+// Without dilation Q is read once and out written once, in whole cache
+// lines: both then bypass cache retention (non-temporal), leaving the caches
+// to the K/V halo rows that neighbouring blocks share.  With dilation the
+// classes rx and rx + 1, visited one after the other, share the lines.
+template <typename T, bool STREAM>
 __device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, int64_t pofs, int pix, int g) {
-  const char *qp = (const char *)(q + pofs);
-  return *(const u32x4 *)(qp + ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 16u));
+  const u32x4 *p = (const u32x4 *)((const char *)(q + pofs) +
+                                   ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 16u));
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
 }
 
 // A lane's share of a tile's output: channels 4g..4g+3 and 16+4g..16+4g+3
@@ -483,17 +489,24 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
 }
 
 // Writes a lane's TileOut to the query at in-plane pixel pix.
-template <typename T>
+template <typename T, bool STREAM>
 __device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, int pix, int g,
                                           const TileOut &t) {
   if (t.ok) {
-    char *o = (char *)(out + pofs) + ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u);
-    *(u32x2 *)o = u32x2{t.val[0], t.val[1]};
-    *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{t.val[2], t.val[3]};
+    u32x2 *o = (u32x2 *)((char *)(out + pofs) +
+                         ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u));
+    if constexpr (STREAM) {
+      __builtin_nontemporal_store(u32x2{t.val[0], t.val[1]}, o);
+      __builtin_nontemporal_store(u32x2{t.val[2], t.val[3]}, o + 2 * sizeof(T));
+    } else {
+      o[0] = u32x2{t.val[0], t.val[1]};
+      o[2 * sizeof(T)] = u32x2{t.val[2], t.val[3]};
+    }
   }
 }
 
-template <typename T, int KS, int RY>
+// STREAM: Q and out accesses are non-temporal (maps without dilation).
+template <typename T, int KS, int RY, bool STREAM>
 __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fdil, FastDiv fnbx,
@@ -528,7 +541,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   RowPart rcur = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
   ColPart ccur = col_part<T, KS>(cc, s, fdil, tx, lc);
   int pcur = query_pixel(rcur, ccur, s, lr, lc);
-  u32x4 qcur = load_q<T>(q, rcur.pofs, pcur, g);
+  u32x4 qcur = load_q<T, STREAM>(q, rcur.pofs, pcur, g);
   load_tables<T, KS, RY>(rpb, rcur.h, tid, treg);
   if (rcur.ok && ccur.ok) stage_block<T, KS, RY>(k, v, rcur, ccur, s, kbuf0, vbuf0, wave, lane);
   store_tables<T, KS, RY>(tab0, tid, has_rpb, treg);
@@ -546,7 +559,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
       rnxt = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
     const ColPart cnxt = col_part<T, KS>(cc, s, fdil, tx, lc);
     const int pnxt = query_pixel(rnxt, cnxt, s, lr, lc);
-    const u32x4 qnxt = load_q<T>(q, rnxt.pofs, pnxt, g);
+    const u32x4 qnxt = load_q<T, STREAM>(q, rnxt.pofs, pnxt, g);
     const bool newtab = more && rnxt.h != tab_hn;
     if (newtab) load_tables<T, KS, RY>(rpb, rnxt.h, tid, treg);
     if (more && rnxt.ok && cnxt.ok) stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, kn, vn, wave, lane);
@@ -560,7 +573,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // the block's results leave after the barrier, so that its wait covers
     // the next block's loads but not these stores
-    store_out<T>(out, rcur.pofs, pcur, g, res);
+    store_out<T, STREAM>(out, rcur.pofs, pcur, g, res);
     rcur = rnxt;
     ccur = cnxt;
     pcur = pnxt;
@@ -573,7 +586,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     if (!more0) break;
     step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < b1);
   }
-  store_out<T>(out, rcur.pofs, pcur, g, res);  // the last block
+  store_out<T, STREAM>(out, rcur.pofs, pcur, g, res);  // the last block
 }
 
 // Compute units of the current device (queried once per device).
@@ -600,7 +613,8 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
   // one persistent workgroup per compute unit (its LDS holds two blocks)
   const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
-  fused_mfma_kernel<T, KS, RY><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
+  auto kernel = s.dil == 1 ? fused_mfma_kernel<T, KS, RY, true> : fused_mfma_kernel<T, KS, RY, false>;
+  kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
       make_fastdiv((uint32_t)s.heads), (int)nblocks);
