@@ -1,0 +1,73 @@
+"""Properties of the gfx950 code the matrix-core kernels compile to (CPU only:
+hipcc cross-compiles to assembly, nothing runs).
+
+* No wait for all outstanding vector-memory operations right next to an LDS
+  read.  The kernels read one LDS buffer while the direct global->LDS copy of
+  the next block fills the other; when the compiler cannot tell the two
+  buffers apart (it loses track once an address is derived through too many
+  steps), it makes the read wait for that copy, which stalls every tile on
+  the next block's loads.
+* No vector-register spills and no scratch memory (scalar registers may
+  spill into vector-register lanes, which costs no memory traffic).
+* No LDS access through flat (generic) addresses.
+* No packed-FP32 arithmetic (the build disables it).
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from vision_transformer_local_amd import build as B
+
+SOURCES = ["na2d_mfma.hip", "na2d_dense.hip"]
+KERNEL = re.compile(r"^(_ZN4na2d12_GLOBAL__N_1\d+\w*mfma_kernel\S*):", re.M)
+
+
+def _asm(src, tmp_path):
+    if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path / (os.path.basename(src) + ".s")
+    cmd = [B.HIPCC] + [f for f in B.COMMON if f not in ("-fPIC",)] + [
+        "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernels(asm):
+    for m in KERNEL.finditer(asm):
+        end = asm.index(".Lfunc_end", m.end())
+        yield m.group(1), asm[m.end():end].split("\n")
+
+
+def _metadata(asm, name):
+    meta = asm[asm.index(".amdgpu_metadata"):]
+    for block in meta.split("- .agpr_count")[1:]:
+        if name in block:
+            return block
+    raise AssertionError("no metadata for " + name)
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_kernel_code_properties(src, tmp_path):
+    asm = _asm(src, tmp_path)
+    kernels = list(_kernels(asm))
+    assert kernels, "no kernels found in " + src
+    for name, body in kernels:
+        ops = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
+        for i, op in enumerate(ops):
+            if re.fullmatch(r"s_waitcnt vmcnt\(0\)", op):
+                near = [o.split()[0] for o in ops[max(0, i - 2):i + 3]]
+                assert not any(o.startswith("ds_read") for o in near), (
+                    "%s: full vector-memory wait next to an LDS read: %s" % (name, near))
+            mnem = op.split()[0]
+            assert not mnem.startswith("flat_"), "%s: flat access %s" % (name, op)
+            assert mnem not in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"), (
+                "%s: packed fp32 %s" % (name, op))
+        meta = _metadata(asm, name)
+        for key in (".vgpr_spill_count", ".private_segment_fixed_size"):
+            m = re.search(re.escape(key) + r":\s+(\d+)", meta)
+            assert m is not None, key
+            assert int(m.group(1)) == 0, "%s: %s = %s" % (name, key, m.group(1))
