@@ -92,20 +92,43 @@ def measured_traffic(workload: str, path: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(p, cpu_inputs, repeats=3):
+def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500):
+    """The float64 oracle on the host cores: whole-workload passes repeated
+    until about budget_s seconds of CPU work, median pass time."""
     import oracle
     threads = oracle.default_threads()
     arrs = [t.to(torch.float64).numpy() for t in cpu_inputs]
     times = []
-    for _ in range(repeats):
+    start = time.perf_counter()
+    while len(times) < min_runs or (time.perf_counter() - start < budget_s
+                                    and len(times) < max_runs):
         t0 = time.perf_counter()
         oracle.forward(*arrs, p.kernel_size, p.dilation, threads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": p.n_query_heads / t, "unit": "queries*heads/s", "cores": threads,
             "kind": "oracle",
-            "sample": "whole workload (%d query-heads), median of %d runs, float64"
-                      % (p.n_query_heads, repeats)}
+            "sample": "whole workload (%d query-heads) run %d times in %.1f s, median pass, "
+                      "float64" % (p.n_query_heads, len(times), time.perf_counter() - start)}
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Read+write GB/s of a plain device copy (torch) of nbytes: the
+    bandwidth a simple streaming kernel attains on this GPU."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps / 1e3
+    del src, dst
+    return 2 * nbytes / t / 1e9
 
 
 def main(argv=None):
@@ -117,6 +140,8 @@ def main(argv=None):
     ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-reference", action="store_true",
+                    help="skip the device-copy bandwidth measurement")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
@@ -262,6 +287,10 @@ def main(argv=None):
         "sample_max_abs_err": max_err,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if not args.no_copy_reference:
+        copy_gbs = copy_bandwidth(dev)
+        rec["copy_reference"] = {"copy_gbs": copy_gbs, "achieved_over_copy": achieved / copy_gbs,
+                                 "what": "torch device copy of 1 GiB, read+write bytes"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(p, cpu)
     print(json.dumps(rec), flush=True)
