@@ -1,4 +1,5 @@
-"""CPU oracle for the 2D (dilated) Neighborhood Attention forward pass.
+"""CPU oracle for the 2D (dilated) Neighborhood Attention forward and backward
+passes.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP
@@ -51,6 +52,12 @@ def _load():
             ctypes.c_int, ctypes.c_int,
             i64p, ctypes.c_int64,
             dp, dp, dp, i32p, i32p, ctypes.c_int]
+        lib.na2d_oracle_backward.restype = ctypes.c_int
+        lib.na2d_oracle_backward.argtypes = [
+            dp, dp, dp, dp, dp,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int,
+            dp, dp, dp, dp, ctypes.c_int]
         lib.na2d_oracle_valid.restype = ctypes.c_int
         lib.na2d_oracle_valid.argtypes = [ctypes.c_int] * 4
         _lib = lib
@@ -141,3 +148,39 @@ def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
     if argmax:
         res["argmax"] = am
     return res
+
+
+def backward(q, k, v, rpb, dout, kernel_size: int, dilation: int, *,
+             threads: int | None = None):
+    """Oracle backward pass: gradients of sum(out * dout) with respect to q,
+    k, v and the bias table.
+
+    q, k, v, dout: [B, heads, H, W, D]; rpb: [heads, 2k-1, 2k-1] or None.
+    Returns a dict with ``dq``, ``dk``, ``dv`` ([B, heads, H, W, D]) and
+    ``drpb`` ([heads, 2k-1, 2k-1], also when rpb is None).
+    """
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if q.ndim != 5 or k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout must share one [B, heads, H, W, D] shape")
+    B, heads, H, W, D = q.shape
+    ks, dil = int(kernel_size), int(dilation)
+    side = 2 * ks - 1
+    if rpb is not None:
+        rpb = _f64(rpb)
+        if rpb.shape != (heads, side, side):
+            raise ValueError("rpb must be [heads, 2k-1, 2k-1]")
+    dq = np.empty_like(q)
+    dk = np.empty_like(q)
+    dv = np.empty_like(q)
+    drpb = np.empty((heads, side, side), dtype=np.float64)
+    rc = lib.na2d_oracle_backward(
+        _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+        _ptr(rpb, ctypes.c_double), _ptr(dout, ctypes.c_double),
+        B, heads, H, W, D, ks, dil,
+        _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double),
+        _ptr(drpb, ctypes.c_double),
+        threads if threads else default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the problem (status %d)" % rc)
+    return {"dq": dq, "dk": dk, "dv": dv, "drpb": drpb}

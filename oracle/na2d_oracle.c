@@ -1,6 +1,6 @@
 /*
  * na2d_oracle.c -- plain, slow, obviously-correct CPU oracle for the forward
- * pass of 2D (dilated) Neighborhood Attention.
+ * and backward passes of 2D (dilated) Neighborhood Attention.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
  * the CPU-baseline leg of the benchmark may load this code.  It shares no
@@ -236,6 +236,173 @@ int na2d_oracle_forward(const double *q, const double *k, const double *v, const
         if (rc)
             failed = 1;
     }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * Backward pass: the chain rule through the four steps above, in double.
+ * With L = sum over all outputs of out * dout (dout given), for every query
+ * with window keys n and probabilities P[n] (recomputed as in the forward):
+ *
+ *   dP[n]   = sum_e dout[e] * value_n[e]
+ *   Dq      = sum_n P[n] * dP[n]               (softmax Jacobian, one row)
+ *   dS[n]   = P[n] * (dP[n] - Dq)
+ *   dq[e]   = sum_n dS[n] * key_n[e] / sqrt(D)
+ *   dk_n[e] += dS[n] * q[e] / sqrt(D)          for every query whose window holds n
+ *   dv_n[e] += P[n] * dout[e]                  likewise
+ *   drpb[h][dy_n + k-1][dx_n + k-1] += dS[n]
+ *
+ * Threads own whole (batch, head) planes, so the scatter into dk and dv never
+ * races; each thread sums its bias gradient into its own table and the tables
+ * are added in thread order at the end (deterministic).
+ */
+typedef struct {
+    const double *q, *k, *v, *rpb, *dout;
+    int B, heads, H, W, D, ks, dil;
+    int64_t plane0, plane1;
+    double *dq, *dk, *dv, *drpb; /* drpb: this thread's own table */
+} oracle_bwd_job;
+
+static void *oracle_bwd_worker(void *arg)
+{
+    const oracle_bwd_job *jb = (const oracle_bwd_job *)arg;
+    const int H = jb->H, W = jb->W, D = jb->D, ks = jb->ks, d = jb->dil;
+    const int nk = ks * ks, side = 2 * ks - 1;
+    const int64_t hw = (int64_t)H * W;
+    const double scale = 1.0 / sqrt((double)D);
+    double *s = (double *)malloc(sizeof(double) * nk);
+    double *p = (double *)malloc(sizeof(double) * nk);
+    double *dp = (double *)malloc(sizeof(double) * nk);
+    int64_t *nb = (int64_t *)malloc(sizeof(int64_t) * nk);
+    int *boff = (int *)malloc(sizeof(int) * nk);
+    if (!s || !p || !dp || !nb || !boff) {
+        free(s); free(p); free(dp); free(nb); free(boff);
+        return (void *)1;
+    }
+    for (int64_t plane = jb->plane0; plane < jb->plane1; ++plane) {
+        const int h = (int)(plane % jb->heads);
+        const int64_t base = plane * hw * D;
+        for (int i = 0; i < H; ++i) {
+            for (int j = 0; j < W; ++j) {
+                const int ry = i % d, ci = i / d, Ly = (H - ry + d - 1) / d;
+                const int rx = j % d, cj = j / d, Lx = (W - rx + d - 1) / d;
+                const int sy = oracle_window_start(ci, Ly, ks);
+                const int sx = oracle_window_start(cj, Lx, ks);
+                const double *qrow = jb->q + base + ((int64_t)i * W + j) * D;
+                const double *grow = jb->dout + base + ((int64_t)i * W + j) * D;
+                double smax = -INFINITY;
+                for (int a = 0; a < ks; ++a)
+                    for (int c = 0; c < ks; ++c) {
+                        const int n = a * ks + c;
+                        const int ni = ry + (sy + a) * d, nj = rx + (sx + c) * d;
+                        nb[n] = base + ((int64_t)ni * W + nj) * D;
+                        boff[n] = ((sy + a) - ci + ks - 1) * side + ((sx + c) - cj + ks - 1);
+                        double dot = 0.0;
+                        for (int e = 0; e < D; ++e)
+                            dot += qrow[e] * jb->k[nb[n] + e];
+                        s[n] = dot * scale + (jb->rpb ? jb->rpb[(int64_t)h * side * side + boff[n]] : 0.0);
+                        if (s[n] > smax)
+                            smax = s[n];
+                    }
+                double sum = 0.0;
+                for (int n = 0; n < nk; ++n) {
+                    p[n] = exp(s[n] - smax);
+                    sum += p[n];
+                }
+                double dq_dot = 0.0; /* Dq */
+                for (int n = 0; n < nk; ++n) {
+                    p[n] /= sum;
+                    double g = 0.0;
+                    for (int e = 0; e < D; ++e)
+                        g += grow[e] * jb->v[nb[n] + e];
+                    dp[n] = g;
+                    dq_dot += p[n] * g;
+                }
+                double *dqrow = jb->dq + base + ((int64_t)i * W + j) * D;
+                for (int e = 0; e < D; ++e)
+                    dqrow[e] = 0.0;
+                for (int n = 0; n < nk; ++n) {
+                    const double ds = p[n] * (dp[n] - dq_dot);
+                    for (int e = 0; e < D; ++e) {
+                        dqrow[e] += ds * jb->k[nb[n] + e] * scale;
+                        jb->dk[nb[n] + e] += ds * qrow[e] * scale;
+                        jb->dv[nb[n] + e] += p[n] * grow[e];
+                    }
+                    jb->drpb[(int64_t)h * side * side + boff[n]] += ds;
+                }
+            }
+        }
+    }
+    free(s); free(p); free(dp); free(nb); free(boff);
+    return NULL;
+}
+
+/*
+ * q, k, v, dout: [B, heads, H, W, D] doubles, contiguous; rpb as in the
+ * forward (NULL = zero bias).  Writes dq, dk, dv ([B, heads, H, W, D]) and
+ * drpb ([heads, 2k-1, 2k-1], the gradient of the bias table; written also
+ * when rpb is NULL).
+ */
+int na2d_oracle_backward(const double *q, const double *k, const double *v, const double *rpb,
+                         const double *dout, int B, int heads, int H, int W, int D, int ks,
+                         int dil, double *dq, double *dk, double *dv, double *drpb,
+                         int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !drpb || B < 1 || heads < 1 ||
+        H < 1 || W < 1 || D < 1 || ks < 1 || (ks % 2) == 0 || dil < 1 || H < ks * dil ||
+        W < ks * dil)
+        return ORACLE_BAD_ARGS;
+    const int64_t planes = (int64_t)B * heads;
+    const int64_t n = planes * H * W * D;
+    const int side = 2 * ks - 1;
+    const int64_t nb = (int64_t)heads * side * side;
+    memset(dk, 0, sizeof(double) * n);
+    memset(dv, 0, sizeof(double) * n);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (planes < nthreads)
+        nthreads = (int)planes;
+    double *tables = (double *)calloc((size_t)nthreads * nb, sizeof(double));
+    if (!tables)
+        return ORACLE_NO_MEMORY;
+    oracle_bwd_job jobs[256];
+    pthread_t tids[256];
+    int created[256];
+    const int64_t chunk = (planes + nthreads - 1) / nthreads;
+    int failed = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_bwd_job *jb = &jobs[t];
+        jb->q = q; jb->k = k; jb->v = v; jb->rpb = rpb; jb->dout = dout;
+        jb->B = B; jb->heads = heads; jb->H = H; jb->W = W; jb->D = D;
+        jb->ks = ks; jb->dil = dil;
+        jb->plane0 = (int64_t)t * chunk;
+        jb->plane1 = jb->plane0 + chunk < planes ? jb->plane0 + chunk : planes;
+        jb->dq = dq; jb->dk = dk; jb->dv = dv; jb->drpb = tables + (int64_t)t * nb;
+        created[t] = 0;
+        if (jb->plane0 >= jb->plane1)
+            continue;
+        if (pthread_create(&tids[t], NULL, oracle_bwd_worker, jb) == 0)
+            created[t] = 1;
+        else if (oracle_bwd_worker(jb))
+            failed = 1;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        if (!created[t])
+            continue;
+        void *rc = NULL;
+        pthread_join(tids[t], &rc);
+        if (rc)
+            failed = 1;
+    }
+    for (int64_t e = 0; e < nb; ++e) {
+        double acc = 0.0;
+        for (int t = 0; t < nthreads; ++t)
+            acc += tables[(int64_t)t * nb + e];
+        drpb[e] = acc;
+    }
+    free(tables);
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
