@@ -115,6 +115,38 @@ na2d_status_t na2d_av(const float *attn, const void *v, void *out, int B, int he
                       int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
                       hipStream_t stream);
 
+/*
+ * Backward pass: gradients of sum(out * dout) with respect to q, k, v and the
+ * bias table, for the operator na2d_forward computes (the chain rule through
+ * the DiNAT module's natten2dqkrpb -> softmax -> natten2dav; DiNAT
+ * walk-through blog, "What is DiNAT").
+ *
+ *   q, k, v, rpb  the forward inputs (rpb may be NULL: zero bias); the
+ *                 probabilities are recomputed from them
+ *   dout          gradient of the loss with respect to the forward output
+ *   dq, dk, dv    written, [B, heads, H, W, D] in `dtype`, rounded once (RNE)
+ *   drpb          written when not NULL: fp32 [heads, 2k-1, 2k-1], the bias
+ *                 table's gradient summed over batch and pixels; NULL skips it
+ *   workspace     caller-owned device memory of at least
+ *                 na2d_backward_workspace_size(...) bytes, 16-byte aligned;
+ *                 its contents are scratch (nothing needs to be zeroed)
+ *
+ * All accumulation is fp32 and every sum runs in a fixed order: repeated
+ * calls give identical results.  Layouts, dtypes and status codes are those
+ * of na2d_forward; outputs must not overlap each other, the inputs or the
+ * workspace.  Work is enqueued on `stream`.
+ */
+na2d_status_t na2d_backward(const void *q, const void *k, const void *v, const void *rpb,
+                            const void *dout, void *dq, void *dk, void *dv, float *drpb,
+                            void *workspace, size_t workspace_bytes, int B, int heads, int H,
+                            int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
+                            hipStream_t stream);
+
+/* Workspace bytes na2d_backward needs (with_bias_grad: drpb != NULL); 0 for
+ * an invalid or unsupported problem. */
+size_t na2d_backward_workspace_size(int B, int heads, int H, int W, int D, int kernel_size,
+                                    int dilation, int with_bias_grad);
+
 /* Static, NUL-terminated description of a status code. */
 const char *na2d_status_string(na2d_status_t status);
 

@@ -163,3 +163,60 @@ def test_header_declares_extern_c_and_no_torch_types():
     assert 'extern "C"' in text
     for banned in ("at::", "torch::", "c10::", "#include <torch", "#include <ATen"):
         assert banned not in text
+
+
+# -- backward -------------------------------------------------------------
+# pointers: q k v rpb dout dq dk dv drpb workspace (fake, 256 MB apart)
+BP = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(10)]
+BIG = ctypes.c_size_t(1 << 40)
+
+
+def _backward(L, ptrs, args, ws_bytes=BIG):
+    B, h, H, W, D, ks, d, dt = args
+    return L.na2d_backward(*ptrs[:10], ws_bytes, B, h, H, W, D, ks, d, dt, S)
+
+
+@pytest.mark.parametrize("args,expect", FORWARD_CASES)
+def test_backward_validation(args, expect):
+    L = na2d.lib()
+    assert _backward(L, BP, args) == expect
+    B, h, H, W, D, ks, d, dt = args
+    if dt in (F32, BF16, F16):  # the size does not depend on the dtype
+        assert L.na2d_backward_workspace_size(B, h, H, W, D, ks, d, 1) == 0
+
+
+def test_backward_workspace_size():
+    L = na2d.lib()
+    B, h, H, W, D, ks, d, _ = VALID
+    with_bias = L.na2d_backward_workspace_size(B, h, H, W, D, ks, d, 1)
+    without = L.na2d_backward_workspace_size(B, h, H, W, D, ks, d, 0)
+    assert without == B * h * H * W * 8  # log-sum-exp and dout.out per query, fp32
+    assert with_bias > without
+    # one workspace byte short is rejected
+    assert _backward(L, BP, VALID, ctypes.c_size_t(with_bias - 1)) == INVALID
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 4, 5, 6, 7, 9])
+def test_backward_null_pointers(slot):
+    L = na2d.lib()
+    ptrs = list(BP)
+    ptrs[slot] = NULL
+    assert _backward(L, ptrs, VALID) == INVALID
+
+
+@pytest.mark.parametrize("slot", range(10))
+def test_backward_misaligned_pointers(slot):
+    L = na2d.lib()
+    ptrs = list(BP)
+    ptrs[slot] = ctypes.c_void_p(ptrs[slot].value + 4)
+    assert _backward(L, ptrs, VALID) == INVALID
+
+
+@pytest.mark.parametrize("a,b", [(5, 0), (5, 6), (6, 7), (7, 4), (8, 3), (9, 5), (9, 1),
+                                 (5, 3), (8, 9)])
+def test_backward_rejects_overlaps(a, b):
+    """An output (or the workspace) placed on top of another buffer."""
+    L = na2d.lib()
+    ptrs = list(BP)
+    ptrs[a] = ctypes.c_void_p(ptrs[b].value + 16)
+    assert _backward(L, ptrs, VALID) == INVALID

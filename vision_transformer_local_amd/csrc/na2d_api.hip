@@ -152,6 +152,52 @@ na2d_status_t na2d_av(const float *attn, const void *v, void *out, int B, int he
   return from_hip(na2d::launch_av(attn, v, out, s, dtype, stream));
 }
 
+size_t na2d_backward_workspace_size(int B, int heads, int H, int W, int D, int kernel_size,
+                                    int dilation, int with_bias_grad) {
+  na2d::Shape s;
+  if (check_shape(B, heads, H, W, D, kernel_size, dilation, &s) != NA2D_SUCCESS) return 0;
+  return na2d::backward_workspace_bytes(s, with_bias_grad != 0);
+}
+
+na2d_status_t na2d_backward(const void *q, const void *k, const void *v, const void *rpb,
+                            const void *dout, void *dq, void *dk, void *dv, float *drpb,
+                            void *workspace, size_t workspace_bytes, int B, int heads, int H,
+                            int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
+                            hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  const void *ins[] = {q, k, v, dout};
+  void *outs[] = {dq, dk, dv};
+  for (const void *p : ins)
+    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
+  for (void *p : outs)
+    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
+  if ((rpb && !aligned16(rpb)) || (drpb && !aligned16(drpb))) return NA2D_ERROR_INVALID_VALUE;
+  if (!workspace || !aligned16(workspace)) return NA2D_ERROR_INVALID_VALUE;
+  const size_t need = na2d::backward_workspace_bytes(s, drpb != nullptr);
+  if (workspace_bytes < need) return NA2D_ERROR_INVALID_VALUE;
+  const int64_t tbytes = s.n_query * D * elem_bytes(dtype);
+  const int64_t side = 2 * kernel_size - 1;
+  const int64_t bbytes = heads * side * side * 4;
+  const int64_t rbytes = heads * side * side * elem_bytes(dtype);
+  // outputs (and the workspace) must not overlap each other or any input
+  struct Span { const void *p; int64_t n; };
+  const Span written[] = {{dq, tbytes}, {dk, tbytes}, {dv, tbytes}, {drpb, bbytes},
+                          {workspace, (int64_t)need}};
+  const Span read[] = {{q, tbytes}, {k, tbytes}, {v, tbytes}, {dout, tbytes}, {rpb, rbytes}};
+  for (int a = 0; a < 5; ++a) {
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(written[a].p, written[a].n, written[b].p, written[b].n))
+        return NA2D_ERROR_INVALID_VALUE;
+    for (const Span &r : read)
+      if (overlaps(written[a].p, written[a].n, r.p, r.n)) return NA2D_ERROR_INVALID_VALUE;
+  }
+  return from_hip(na2d::launch_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, workspace, s, dtype,
+                                        stream));
+}
+
 const char *na2d_status_string(na2d_status_t status) {
   switch (status) {
     case NA2D_SUCCESS: return "NA2D_SUCCESS: no error";

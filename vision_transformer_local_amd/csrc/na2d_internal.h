@@ -103,6 +103,11 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);
+// Backward pass (three kernels); ws holds backward_workspace_bytes(s, drpb).
+size_t backward_workspace_bytes(const Shape &s, bool with_bias);
+hipError_t launch_backward(const void *q, const void *k, const void *v, const void *rpb,
+                           const void *dout, void *dq, void *dk, void *dv, float *drpb, void *ws,
+                           const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s,
                      na2d_dtype_t dt, hipStream_t st);
 

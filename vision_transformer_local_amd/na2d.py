@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.na2d_softmax.argtypes = [vp] * 2 + [i] * 5 + [vp]
         L.na2d_av.restype = i
         L.na2d_av.argtypes = [vp] * 3 + [i] * 8 + [vp]
+        L.na2d_backward.restype = i
+        L.na2d_backward.argtypes = [vp] * 10 + [ctypes.c_size_t] + [i] * 8 + [vp]
+        L.na2d_backward_workspace_size.restype = ctypes.c_size_t
+        L.na2d_backward_workspace_size.argtypes = [i] * 8
         L.na2d_status_string.restype = ctypes.c_char_p
         L.na2d_status_string.argtypes = [i]
         L.na2d_version.restype = i
@@ -173,6 +177,34 @@ def na2d_av(attn, v, out, kernel_size: int, dilation: int):
     return out
 
 
+def na2d_backward_workspace_size(B, heads, H, W, D, kernel_size: int, dilation: int,
+                                 with_bias_grad: bool) -> int:
+    return int(lib().na2d_backward_workspace_size(B, heads, H, W, D, int(kernel_size),
+                                                  int(dilation), int(bool(with_bias_grad))))
+
+
+def na2d_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, workspace, kernel_size: int,
+                  dilation: int):
+    """Backward pass into dq, dk, dv (and drpb, fp32, unless None); the
+    workspace is a uint8 GPU tensor of at least na2d_backward_workspace_size
+    bytes."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        _need(t, n, q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    side = 2 * kernel_size - 1
+    if drpb is not None:
+        _need(drpb, "drpb", torch.float32, (heads, side, side))
+    _need(workspace, "workspace", torch.uint8)
+    st = lib().na2d_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(dout),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drpb), _ptr(workspace),
+                             workspace.numel(), B, heads, H, W, D, int(kernel_size),
+                             int(dilation), _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_backward")
+    return dq, dk, dv, drpb
+
+
 # -- allocating conveniences (torch allocates the outputs; nothing else) ----
 
 def forward(q, k, v, rpb, kernel_size: int, dilation: int, algo: str = "auto"):
@@ -189,3 +221,17 @@ def forward_unfused(q, k, v, rpb, kernel_size: int, dilation: int):
     out = torch.empty_like(v)
     na2d_av(attn, v, out, kernel_size, dilation)
     return out
+
+
+def backward(q, k, v, rpb, dout, kernel_size: int, dilation: int, bias_grad: bool = True):
+    """Allocating backward: returns (dq, dk, dv, drpb or None)."""
+    B, heads, H, W, D = _qkv_shape(q)
+    n = na2d_backward_workspace_size(B, heads, H, W, D, kernel_size, dilation, bias_grad)
+    if n == 0:
+        raise Na2dError(INVALID_VALUE, "na2d_backward_workspace_size: invalid problem")
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    side = 2 * kernel_size - 1
+    drpb = (torch.empty((heads, side, side), dtype=torch.float32, device=q.device)
+            if bias_grad else None)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    return na2d_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, kernel_size, dilation)
