@@ -2,9 +2,12 @@
 """Throughput of the fused 2D Neighborhood Attention forward pass on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--pass forward|backward]
 
 One step = one full forward pass (neighbourhood map, QK + bias, softmax, AV,
 store) over one batch of the workload, on inputs already resident in HBM.
+With --pass backward, one step is one backward pass instead (dq, dk, dv and
+the bias gradient from q, k, v, the bias table and dout).
 The default workload is the NAT-Tiny stage-1 layer: B=64, heads=2, 56x56,
 D=32, k=7, d=1, bf16 (fp32 accumulation), seeded synthetic N(0,1) data.
 
@@ -52,6 +55,8 @@ WORKLOADS = {
     "det_k13_d8_bf16": I.DETECTION[6], "det_k13_d8_f16": I.DETECTION[7],
     "tiny_f32": I.TINY,
 }
+BACKWARD_SOURCES = ["vision_transformer_local_amd/csrc/na2d_backward.hip",
+                    "vision_transformer_local_amd/csrc/na2d_internal.h"]
 KERNEL_SOURCES = ["vision_transformer_local_amd/csrc/na2d_mfma.hip",
                   "vision_transformer_local_amd/csrc/na2d_dense.hip",
                   "vision_transformer_local_amd/csrc/na2d_mfma_common.h",
@@ -71,9 +76,17 @@ def algorithmic_bytes(p) -> int:
     return 4 * p.D * s * p.n_query_heads + p.heads * side * side * s
 
 
-def kernel_source_hash() -> str:
+def backward_algorithmic_bytes(p) -> int:
+    """Bytes the backward pass must move: q, k, v and dout read once, dq, dk
+    and dv written once, the bias table read and its fp32 gradient written."""
+    s = elem_size(p.dtype)
+    side = 2 * p.kernel_size - 1
+    return 7 * p.D * s * p.n_query_heads + p.heads * side * side * (s + 4)
+
+
+def kernel_source_hash(which: str = "forward") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in BACKWARD_SOURCES if which == "backward" else KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -87,23 +100,25 @@ def measured_traffic(workload: str, path: str):
         return None
     with open(fn) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(
+            "backward" if path == "backward" else "forward"):
         return None  # kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500):
+def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500, backward=False):
     """The float64 oracle on the host cores: whole-workload passes repeated
     until about budget_s seconds of CPU work, median pass time."""
     import oracle
     threads = oracle.default_threads()
     arrs = [t.to(torch.float64).numpy() for t in cpu_inputs]
+    fn = oracle.backward if backward else oracle.forward
     times = []
     start = time.perf_counter()
     while len(times) < min_runs or (time.perf_counter() - start < budget_s
                                     and len(times) < max_runs):
         t0 = time.perf_counter()
-        oracle.forward(*arrs, p.kernel_size, p.dilation, threads=threads)
+        fn(*arrs, p.kernel_size, p.dilation, threads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": p.n_query_heads / t, "unit": "queries*heads/s", "cores": threads,
@@ -138,6 +153,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="nat_tiny_s1", choices=sorted(WORKLOADS))
     ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-reference", action="store_true",
@@ -174,6 +190,8 @@ def main(argv=None):
         return 0
     p = WORKLOADS[args.workload]
     L = na2d.lib()
+    if args.which == "backward":
+        return bench_backward(args, p, dev, L)
 
     cpu = I.make_inputs(p, seed=0)
     q0, k0, v0, rpb0 = cpu
@@ -210,10 +228,8 @@ def main(argv=None):
         if r != 0:
             raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
 
-    stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
-        launch(i, stream.cuda_stream)
-    torch.cuda.synchronize()
+    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+    K = args.steps
 
     # sanity: a sample of the first replica's output against the oracle
     import numpy as np
@@ -224,37 +240,6 @@ def main(argv=None):
     got = reps[0][3].reshape(-1, D)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
     max_err = float(np.abs(got - ref).max())
 
-    K = args.steps
-    graph = None
-    if args.mode == "graph":
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                cap = torch.cuda.current_stream(dev).cuda_stream
-                for i in range(K):
-                    launch(i, cap)
-        torch.cuda.synchronize()
-        graph.replay()  # one untimed replay: first-replay setup stays out of the timing
-        torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(K):
-            launch(i, stream.cuda_stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    ms_per_step = (t1 - t0) * 1e3 / K
-    kernel_ms = ev0.elapsed_time(ev1) / K
     value = p.n_query_heads / (ms_per_step / 1e3)
     abytes = algorithmic_bytes(p)
     if args.path == "unfused":
@@ -293,6 +278,118 @@ def main(argv=None):
                                  "what": "torch device copy of 1 GiB, read+write bytes"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(p, cpu)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def time_steps(args, launch, dev):
+    """Warm up, capture K launches in a graph (or not), time them: returns
+    (wall ms per step, event ms per step)."""
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        launch(i, stream.cuda_stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    graph = None
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                cap = torch.cuda.current_stream(dev).cuda_stream
+                for i in range(K):
+                    launch(i, cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            launch(i, stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+
+
+def bench_backward(args, p, dev, L):
+    """One step = one backward pass (three kernel launches) over the workload."""
+    import numpy as np
+    B, heads, H, W, D = p.shape
+    ks, dil = p.kernel_size, p.dilation
+    q0, k0, v0, rpb0 = I.make_inputs(p, seed=0)
+    gen = torch.Generator("cpu").manual_seed(1000)
+    d0 = torch.randn(q0.shape, generator=gen, dtype=torch.float32).to(q0.dtype)
+    tbytes = q0.numel() * q0.element_size()
+    wsb = na2d.na2d_backward_workspace_size(B, heads, H, W, D, ks, dil, True)
+    R = max(2, math.ceil(args.rotate_bytes / (7 * tbytes + wsb)))
+    rpb = rpb0.to(dev)
+    side = 2 * ks - 1
+    drpb = torch.empty((heads, side, side), dtype=torch.float32, device=dev)
+    reps = []
+    for _ in range(R):
+        ins = [t.to(dev) for t in (q0, k0, v0, d0)]
+        outs = [torch.empty_like(ins[0]) for _ in range(3)]
+        reps.append((ins, outs, torch.empty(wsb, dtype=torch.uint8, device=dev)))
+    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
+
+    def launch(i, stream):
+        (q, k, v, dout), (dq, dk, dv), ws = reps[i % R]
+        r = L.na2d_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            drpb.data_ptr(), ws.data_ptr(), wsb, B, heads, H, W, D, ks, dil,
+                            dt_code, ctypes.c_void_p(stream))
+        if r != 0:
+            raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
+
+    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+
+    # sanity: the first replica's gradients against the oracle (skipped on the
+    # largest maps, where the parity tests cover them)
+    max_err = None
+    if p.n_query_heads * ks * ks <= 64 * 2 * 56 * 56 * 49:
+        import oracle
+        ref = oracle.backward(q0, k0, v0, rpb0, d0, ks, dil)
+        got = [t.double().cpu().numpy() for t in reps[0][1]]
+        max_err = max(float(np.abs(g - ref[n]).max()) for g, n in zip(got, ("dq", "dk", "dv")))
+        max_err = max(max_err, float(np.abs(drpb.double().cpu().numpy() - ref["drpb"]).max()))
+
+    abytes = backward_algorithmic_bytes(p)
+    achieved = abytes / (kernel_ms / 1e3) / 1e9
+    rec = {
+        "metric": "NA2D bwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
+        "value": p.n_query_heads / (ms_per_step / 1e3),
+        "unit": "queries*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v/dout, 0.02*N(0,1) bias)",
+        "config": {"workload": "%s backward: %s" % (args.workload, p.describe()),
+                   "B": B, "heads": heads, "H": H, "W": W, "D": D,
+                   "kernel_size": ks, "dilation": dil, "path": "backward",
+                   "timing": args.mode, "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload, "backward")},
+        "kernel_ms": kernel_ms,
+        "algorithmic_bytes_per_step": abytes,
+        "sample_max_abs_err": max_err,
+        "kernel_source_hash": kernel_source_hash("backward"),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(p, (q0, k0, v0, rpb0, d0), backward=True)
     print(json.dumps(rec), flush=True)
     return 0
 

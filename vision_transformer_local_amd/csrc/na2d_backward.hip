@@ -303,6 +303,8 @@ hipError_t launch_bwd_dtype(const void *q, const void *k, const void *v, const v
 
 }  // namespace
 
+// Large enough for either family of kernels (the size does not depend on
+// the data type, which picks the family).
 size_t backward_workspace_bytes(const Shape &s, bool with_bias) {
   const int side = 2 * s.ks - 1;
   const int tq = s.ks <= 5 ? QueryGroup<5>::THREADS
@@ -310,12 +312,15 @@ size_t backward_workspace_bytes(const Shape &s, bool with_bias) {
   const int64_t chunks = ((int64_t)s.H * s.W + tq - 1) / tq;
   size_t n = (size_t)s.n_query * 2 * sizeof(float);
   if (with_bias) n += (size_t)s.B * s.heads * chunks * side * side * sizeof(float);
-  return n;
+  const size_t m = backward_mfma_workspace_bytes(s, with_bias);
+  return n > m ? n : m;
 }
 
 hipError_t launch_backward(const void *q, const void *k, const void *v, const void *rpb,
                            const void *dout, void *dq, void *dk, void *dv, float *drpb, void *ws,
                            const Shape &s, na2d_dtype_t dt, hipStream_t st) {
+  if (backward_mfma_supported(s, dt))
+    return launch_backward_mfma(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, s, dt, st);
   switch (dt) {
     case NA2D_DTYPE_F32:
       return launch_bwd_dtype<float>(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, s, st);

@@ -104,7 +104,14 @@ hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *at
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);
 // Backward pass (three kernels); ws holds backward_workspace_bytes(s, drpb).
+// The matrix-core kernels take bf16/fp16 with 3 <= k <= 13, the per-lane
+// kernels everything else.
 size_t backward_workspace_bytes(const Shape &s, bool with_bias);
+bool backward_mfma_supported(const Shape &s, na2d_dtype_t dt);
+size_t backward_mfma_workspace_bytes(const Shape &s, bool with_bias);
+hipError_t launch_backward_mfma(const void *q, const void *k, const void *v, const void *rpb,
+                                const void *dout, void *dq, void *dk, void *dv, float *drpb,
+                                void *ws, const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_backward(const void *q, const void *k, const void *v, const void *rpb,
                            const void *dout, void *dq, void *dk, void *dv, float *drpb, void *ws,
                            const Shape &s, na2d_dtype_t dt, hipStream_t st);
