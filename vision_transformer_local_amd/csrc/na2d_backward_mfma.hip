@@ -31,11 +31,14 @@
 //     Near the borders the set of queries reaching a key is larger than
 //     the k x k interior one; the tile loops over exactly its rows and
 //     16-column chunks.
-//   * The bias gradient: each wave adds its tile's dS into its own LDS table
-//     with one 16-lane group at a time (its lanes hold distinct queries, so
-//     no two lanes of one add meet at an entry holding a nonzero term), the
-//     block sums its waves' tables in wave order, and a last kernel sums the
-//     blocks of each head in a fixed tree.  The pass is deterministic.
+//   * The bias gradient: after the tile's products, each wave parks its dS
+//     rows (by query, in window coordinates) in the freed halo LDS and every
+//     lane sums one window slot over the tile's queries in a fixed order into
+//     the wave's own table (distinct lanes, distinct entries: no atomics);
+//     the block sums its waves' tables in wave order, and a last kernel sums
+//     the blocks of each head in a fixed tree.  The pass is deterministic.
+//   * Each wave's Q/dout (query kernel) or K/V (key kernel) operands are
+//     loaded while the block's halo copy is in flight.
 #include "na2d_mfma_common.h"
 
 #include <limits.h>
@@ -72,9 +75,11 @@ constexpr int max_inv_span(int ks, int n) {
   return best;
 }
 
-template <int KS> struct BG {
+// Block height: 16 rows, or 8 when the residue classes are at most 8 rows
+// long (large dilations), so that no wave of a block idles.
+template <int KS, int RYV = 16> struct BG {
   static constexpr int TY = KS <= 9 ? 2 : 4, TX = 16 / TY;  // tile: TY x TX pixels
-  static constexpr int RY = 16, RX = 8;                       // block: RY x RX pixels
+  static constexpr int RY = RYV, RX = 8;                      // block: RY x RX pixels
   static constexpr int NTX = RX / TX, WAVES = (RY / TY) * NTX, THREADS = 64 * WAVES;
   static constexpr int NB = TY + KS - 1;  // key rows reached by a query tile
   static constexpr int SIDE = 2 * KS - 1, NT = SIDE * SIDE;
@@ -85,6 +90,16 @@ template <int KS> struct BG {
   // key kernel: Q/dout halo of a key block, plus one row for the second row
   // of a tile's last (odd) pair
   static constexpr int QR = max_inv_span(KS, RY) + 1, QC = max_inv_span(KS, RX);
+  // Bias tables (times sqrt(D)) laid out so that a lane reads its entries at
+  // one base plus immediate offsets, margins included (no clamping):
+  //   query kernel, interior tiles: [a - qy + TY-1][c - qx + TX-1] with the
+  //     window mask baked in (-inf outside); edge tiles: [key - query row +
+  //     k-1 + TY-1][key - query column + k-1 + TX-1], zero margins;
+  //   key kernel: the same two kinds indexed by query - key (+ k-1 and the
+  //     margins TY-1, TX-1).
+  static constexpr int IH = NB + TY - 1, IW = 16 + TX - 1;
+  static constexpr int EH = NB + KS + TY - 2, EW = TX + KS + 14;
+  static constexpr int FH = 2 * TY + 2 * KS - 2, FW = 2 * TX + 2 * KS + 12;
 };
 
 constexpr float kInvSqrtD = 0.17677669529663687f;  // 1 / sqrt(32)
@@ -107,18 +122,27 @@ struct Block {
   bool ok;  // false when the class is too short to reach this block
 };
 
-__device__ __forceinline__ Block block_at(int id, const Shape &s, int nby, int nbx, int RY,
+// Divisors of the block numbering, fixed per launch.
+struct BlockDivs {
+  FastDiv nbx, nby, dil, heads;
+};
+
+__device__ __forceinline__ Block block_at(int id, const Shape &s, const BlockDivs &dv, int RY,
                                           int RX) {
   Block b;
-  const int bx = id % nbx;
-  id /= nbx;
-  const int by = id % nby;
-  id /= nby;
-  b.rx = id % s.dil;
-  id /= s.dil;
-  b.ry = id % s.dil;
-  b.plane = id / s.dil;
-  b.h = (int)(b.plane % s.heads);
+  uint32_t u = (uint32_t)id, t = fast_div(u, dv.nbx);
+  const int bx = (int)(u - t * dv.nbx.div);
+  u = t;
+  t = fast_div(u, dv.nby);
+  const int by = (int)(u - t * dv.nby.div);
+  u = t;
+  t = fast_div(u, dv.dil);
+  b.rx = (int)(u - t * dv.dil.div);
+  u = t;
+  t = fast_div(u, dv.dil);
+  b.ry = (int)(u - t * dv.dil.div);
+  b.plane = t;
+  b.h = (int)(t - fast_div(t, dv.heads) * dv.heads.div);
   b.Ly = class_len(s.H, b.ry, s.dil);
   b.Lx = class_len(s.W, b.rx, s.dil);
   b.y0 = by * RY;
@@ -226,30 +250,43 @@ __device__ __forceinline__ typename Mma<T>::vec load_operand(const T *pixel, int
   return __builtin_bit_cast(typename Mma<T>::vec, *(const u32x4 *)(pixel + 8 * g));
 }
 
-// Bias table of head h, times sqrt(D) (accumulator units of the score MFMA).
-template <typename T, int NT>
-__device__ __forceinline__ void load_bias(const T *__restrict__ rpb, int h, float *tab, int tid,
-                                          int nthreads) {
-  for (int e = tid; e < NT; e += nthreads)
-    tab[e] = rpb != nullptr ? Elem<T>::to_f(rpb[(int64_t)h * NT + e]) * kSqrtD : 0.f;
+// Fills an H x W table: entry (u, w) holds sqrt(D) * rpb[h][ry][rx] for the
+// bias index (ry, rx) = map(u, w) when that lies in the (2k-1)^2 table, else
+// `outside` (0 for margins, -inf for a baked-in window mask); `inside`
+// additionally restricts the valid entries.
+template <typename T, int KS, typename Map>
+__device__ __forceinline__ void fill_table(const T *__restrict__ rpb, int h, float *tab, int H,
+                                           int W, int tid, int nthreads, float outside,
+                                           Map map) {
+  constexpr int SIDE = 2 * KS - 1;
+  for (int e = tid; e < H * W; e += nthreads) {
+    const int u = e / W, w = e - u * W;
+    int by, bx;
+    const bool in = map(u, w, by, bx);
+    float x = outside;
+    if (in && (unsigned)by < (unsigned)SIDE && (unsigned)bx < (unsigned)SIDE)
+      x = rpb != nullptr ? Elem<T>::to_f(rpb[((int64_t)h * SIDE + by) * SIDE + bx]) * kSqrtD : 0.f;
+    tab[e] = x;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Query kernel.
-template <typename T, int KS>
-__global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
+template <typename T, int KS, int RY>
+__global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, const T *__restrict__ dout, T *__restrict__ dq,
     float *__restrict__ lse, float *__restrict__ dqdot, float *__restrict__ bias_part, Shape s,
-    int nby, int nbx) {
-  using G = BG<KS>;
-  constexpr int NB = G::NB, SIDE = G::SIDE, NT = G::NT, HC = G::HC;
+    BlockDivs dv) {
+  using G = BG<KS, RY>;
+  constexpr int NB = G::NB, SIDE = G::SIDE, NT = G::NT, HC = G::HC, TY = G::TY, TX = G::TX;
+  constexpr int R = KS / 2;
   constexpr int HALO = G::HR * HC * 64;  // bytes per staged tensor
   // K then V halo; afterwards the waves' parking space for dS (bias gradient)
   __shared__ __attribute__((aligned(16))) char halo[2 * HALO];
-  __shared__ float btab[NT];
+  __shared__ float tabI[G::IH * G::IW], tabE[G::EH * G::EW];
   __shared__ float dtab[G::WAVES][NT];
-  constexpr int PARK = G::TX * KS * 16;  // floats per wave: [query column][window row][16]
+  constexpr int PARK = TX * KS * 16;  // floats per wave: [query column][window row][16]
   static_assert(G::WAVES * PARK * 4 <= 2 * HALO, "dS parking exceeds the halo buffers");
   char *const kbuf = halo, *const vbuf = halo + HALO;
 
@@ -257,7 +294,7 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
   const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const Block b = block_at(id, s, nby, nbx, G::RY, G::RX);
+  const Block b = block_at(id, s, dv, G::RY, G::RX);
   const bool bias = bias_part != nullptr;
   if (!b.ok) {
     if (bias)
@@ -270,45 +307,74 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
   const int hx0 = window_start(b.x0, Lx, KS), hx1 = window_start(x1, Lx, KS) + KS - 1;
   stage_halo<T, G::HR, HC>(k, s, b, hy0, hy1, hx0, hx1, kbuf, wave, lane, G::WAVES);
   stage_halo<T, G::HR, HC>(v, s, b, hy0, hy1, hx0, hx1, vbuf, wave, lane, G::WAVES);
-  load_bias<T, NT>(rpb, b.h, btab, tid, G::THREADS);
+  // this wave's tile; its Q / dout operands load while the halo copy runs
+  const int64_t pofs = b.plane * (int64_t)s.H * s.W * kHeadDim;
+  const int tci0 = b.y0 + (wave / G::NTX) * TY, tcj0 = b.x0 + (wave % G::NTX) * TX;
+  const bool tile_ok = tci0 < Ly && tcj0 < Lx;
+  const int qy = ql / TX, qx = ql % TX;
+  const int ci = min(tci0 + qy, Ly - 1), cj = min(tcj0 + qx, Lx - 1);
+  const unsigned qpix = pixel_of(s, b, ci, cj);
+  const typename Mma<T>::vec qv = load_operand(q + pofs + (size_t)qpix * kHeadDim, g);
+  const typename Mma<T>::vec gv = load_operand(dout + pofs + (size_t)qpix * kHeadDim, g);
+  fill_table<T, KS>(rpb, b.h, tabI, G::IH, G::IW, tid, G::THREADS, -INFINITY,
+                    [](int u, int w, int &by, int &bx) {
+                      const int oy = u - (TY - 1), ox = w - (TX - 1);  // window slot
+                      by = oy + R;
+                      bx = ox + R;
+                      return (unsigned)oy < (unsigned)KS && (unsigned)ox < (unsigned)KS;
+                    });
+  fill_table<T, KS>(rpb, b.h, tabE, G::EH, G::EW, tid, G::THREADS, 0.f,
+                    [](int u, int w, int &by, int &bx) {
+                      by = u - (TY - 1);
+                      bx = w - (TX - 1);
+                      return true;
+                    });
   if (bias)
     for (int e = lane; e < NT; e += 64) dtab[wave][e] = 0.f;
   __syncthreads();  // also completes the LDS copies
 
-  const int64_t pofs = b.plane * (int64_t)s.H * s.W * kHeadDim;
-  const int tci0 = b.y0 + (wave / G::NTX) * G::TY, tcj0 = b.x0 + (wave % G::NTX) * G::TX;
-  const bool tile_ok = tci0 < Ly && tcj0 < Lx;
-  const int qy = ql / G::TX, qx = ql % G::TX;
-  const int ci = min(tci0 + qy, Ly - 1), cj = min(tcj0 + qx, Lx - 1);
-  const int Y0 = window_start(min(tci0, Ly - 1), Ly, KS), X0 = window_start(min(tcj0, Lx - 1), Lx, KS);
+  const int Y0 = window_start(min(tci0, Ly - 1), Ly, KS);
+  const int X0 = window_start(min(tcj0, Lx - 1), Lx, KS);
   const int sy = window_start(ci, Ly, KS), sx = window_start(cj, Lx, KS);
   f32x4 dp[NB];  // dP, then dS
   if (tile_ok) {
     const bool qok = tci0 + qy < Ly && tcj0 + qx < Lx;
-    const unsigned qpix = pixel_of(s, b, ci, cj);
-    const typename Mma<T>::vec qv = load_operand(q + pofs + (size_t)qpix * kHeadDim, g);
-    const typename Mma<T>::vec gv = load_operand(dout + pofs + (size_t)qpix * kHeadDim, g);
     const int lr0 = Y0 - hy0, lc0 = X0 - hx0;
-    float capx[4];
-    int colp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int xx = X0 + 4 * g + i;
-      capx[i] = (unsigned)(xx - sx) < (unsigned)KS ? INFINITY : -INFINITY;
-      colp[i] = clampi(xx - cj + KS - 1, 0, SIDE - 1);
-    }
     f32x4 sc[NB];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // every query of the tile has an unclamped window (and the tile is whole)
+    const bool inner = tci0 >= R && tci0 + TY - 1 + R <= Ly - 1 && tcj0 >= R &&
+                       tcj0 + TX - 1 + R <= Lx - 1;
+    const char *kb = kbuf + (lr0 * HC + lc0 + ql) * 64 + 16 * (g ^ (((lc0 + ql) >> 1) & 3));
+    const char *vb = vbuf + (kb - kbuf);
+    if (inner) {
+      const float *tb = tabI + (TY - 1 - qy) * G::IW + (4 * g - qx + TX - 1);
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const int yy = Y0 + a;
-      const float capy = (unsigned)(yy - sy) < (unsigned)KS ? INFINITY : -INFINITY;
-      const int rowp = clampi(yy - ci + KS - 1, 0, SIDE - 1) * SIDE;
-      f32x4 cin;
+      for (int a = 0; a < NB; ++a) {
+        f32x4 cin;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cin[i] = fminf(fminf(btab[rowp + colp[i]], capx[i]), capy);
-      sc[a] = Mma<T>::run(halo_vec<T, HC>(kbuf, lr0 + a, lc0 + ql, g), qv, cin);
-      dp[a] = Mma<T>::run(halo_vec<T, HC>(vbuf, lr0 + a, lc0 + ql, g), gv, zero);
+        for (int i = 0; i < 4; ++i) cin[i] = tb[a * G::IW + i];
+        sc[a] = Mma<T>::run(*(const typename Mma<T>::vec *)(kb + a * HC * 64), qv, cin);
+        dp[a] = Mma<T>::run(*(const typename Mma<T>::vec *)(vb + a * HC * 64), gv, zero);
+      }
+    } else {
+      // +inf inside the query's window, -inf outside: one min per bound
+      float capx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        capx[i] = (unsigned)(X0 + 4 * g + i - sx) < (unsigned)KS ? INFINITY : -INFINITY;
+      int be = (Y0 - ci + KS - 1 + TY - 1) * G::EW + (X0 + 4 * g - cj + KS - 1 + TX - 1);
+      asm volatile("" : "+v"(be));  // one base register; the reads use immediate offsets
+      const float *tb = tabE + be;
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        const float capy = (unsigned)(Y0 + a - sy) < (unsigned)KS ? INFINITY : -INFINITY;
+        f32x4 cin;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cin[i] = fminf(fminf(tb[a * G::EW + i], capx[i]), capy);
+        sc[a] = Mma<T>::run(*(const typename Mma<T>::vec *)(kb + a * HC * 64), qv, cin);
+        dp[a] = Mma<T>::run(*(const typename Mma<T>::vec *)(vb + a * HC * 64), gv, zero);
+      }
     }
     // softmax over the window (masked entries are -inf), in log2 units of z
     const float c2 = kLog2e * kInvSqrtD;
@@ -319,29 +385,25 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
     mx = group_max(mx);
     const float mc = mx * c2;
-    float l = 0.f;
+    float l = 0.f, pd = 0.f;
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+        sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));  // unnormalised p
         l += sc[a][i];
+        pd = fmaf(sc[a][i], dp[a][i], pd);
       }
     l = group_sum(l);
+    pd = group_sum(pd);
     const float inv = 1.0f / l;
-    float dqd = 0.f;
+    const float dqd = pd * inv;  // Dq = sum P dP
+    const float ninvd = -inv * dqd;
+    // dS = P (dP - Dq) = p (inv dP - inv Dq)
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[a][i] *= inv;
-        dqd = fmaf(sc[a][i], dp[a][i], dqd);
-      }
-    dqd = group_sum(dqd);
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dp[a][i] = sc[a][i] * (dp[a][i] - dqd);  // dS
+      for (int i = 0; i < 4; ++i) dp[a][i] = sc[a][i] * fmaf(dp[a][i], inv, ninvd);
     // dq^T = K^T . dS^T over pairs of key rows
     f32x4 o0 = zero, o1 = zero;
     const int tc = lc0 + 4 * g + (ql >> 2);
@@ -371,7 +433,16 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
   if (tile_ok) {
     float *park = (float *)halo + wave * PARK;
     float *wt = dtab[wave];
-    for (int h = 0; h < G::TY; ++h) {
+    constexpr int NS = (KS * KS + 63) / 64;  // window slots per lane
+    int pslot[NS], eslot[NS];                // slot's parking / table offsets
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int slot = min(u * 64 + lane, KS * KS - 1);
+      const int wa = slot / KS, wc = slot - wa * KS;
+      pslot[u] = wa * 16 + wc;
+      eslot[u] = wa * SIDE + wc;
+    }
+    for (int h = 0; h < TY; ++h) {
       const int qi = tci0 + h;
       if (qi >= Ly) break;
       if (qy == h) {
@@ -382,30 +453,31 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
         }
       }
       __builtin_amdgcn_wave_barrier();
-      const int syq = window_start(qi, Ly, KS);
-      for (int s0 = 0; s0 < KS * KS; s0 += 64) {
-        const int slot = s0 + lane;
-        if (slot < KS * KS) {
-          const int wa = slot / KS, wc = slot - wa * KS;
-          const int erow = (wa + syq - qi + KS - 1) * SIDE;
-          float run = 0.f;
-          int re = -1;  // table entry the running sum belongs to
-          for (int x = 0; x < G::TX; ++x) {
-            const int qj = tcj0 + x;
-            if (qj >= Lx) break;
-            const int sxq = window_start(qj, Lx, KS);
-            const float val = park[(x * KS + wa) * 16 + wc + sxq - X0];
-            const int e = erow + wc + sxq - qj + KS - 1;
-            if (e != re) {
-              if (re >= 0) wt[re] += run;
-              run = val;
-              re = e;
-            } else {
-              run += val;
-            }
+      // the row's queries in column order; the table offset of a slot
+      // depends on the query only through its window start (uniform), so
+      // consecutive queries with the same start share one running sum
+      const int rowcls = (window_start(qi, Ly, KS) - qi + KS - 1) * SIDE;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const bool active = u * 64 + lane < KS * KS;
+        float run = 0.f;
+        int rc = -1;  // table offset (uniform) of the running sum
+#pragma unroll
+        for (int x = 0; x < TX; ++x) {
+          const int qj = tcj0 + x;
+          if (qj >= Lx) break;
+          const int sxq = window_start(qj, Lx, KS);
+          const int cls = rowcls + sxq - qj + KS - 1;
+          const float val = park[x * KS * 16 + (sxq - X0) + pslot[u]];
+          if (cls != rc) {
+            if (rc >= 0 && active) wt[eslot[u] + rc] += run;
+            run = val;
+            rc = cls;
+          } else {
+            run += val;
           }
-          if (re >= 0) wt[re] += run;
         }
+        if (active) wt[eslot[u] + rc] += run;
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -421,23 +493,24 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_query_mfma(
 
 // ---------------------------------------------------------------------------
 // Key kernel.
-template <typename T, int KS>
-__global__ __launch_bounds__(BG<KS>::THREADS) void bwd_key_mfma(
+template <typename T, int KS, int RY>
+__global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_key_mfma(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, const T *__restrict__ dout, const float *__restrict__ lse,
-    const float *__restrict__ dqdot, T *__restrict__ dk, T *__restrict__ dv, Shape s, int nby,
-    int nbx) {
-  using G = BG<KS>;
-  constexpr int SIDE = G::SIDE, NT = G::NT, QR = G::QR, QC = G::QC;
+    const float *__restrict__ dqdot, T *__restrict__ dk, T *__restrict__ dv, Shape s,
+    BlockDivs dvs) {
+  using G = BG<KS, RY>;
+  constexpr int QR = G::QR, QC = G::QC, TY = G::TY, TX = G::TX, FW = G::FW;
+  constexpr int R = KS / 2;
   __shared__ __attribute__((aligned(16))) char qbuf[QR * QC * 64], gbuf[QR * QC * 64];
   __shared__ f32x2 lbuf[QR * QC];  // (log-sum-exp, Dq) of the halo queries
-  __shared__ float btab[NT];
+  __shared__ float tabI[G::FH * FW], tabE[G::FH * FW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
   const int id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const Block b = block_at(id, s, nby, nbx, G::RY, G::RX);
+  const Block b = block_at(id, s, dvs, G::RY, G::RX);
   if (!b.ok) return;
   const int Ly = b.Ly, Lx = b.Lx;
   const int y1 = min(b.y0 + G::RY, Ly) - 1, x1 = min(b.x0 + G::RX, Lx) - 1;
@@ -447,70 +520,107 @@ __global__ __launch_bounds__(BG<KS>::THREADS) void bwd_key_mfma(
   stage_halo<T, QR, QC>(dout, s, b, hq0, hq1, hc0, hc1, gbuf, wave, lane, G::WAVES);
   const int64_t pofs = b.plane * (int64_t)s.H * s.W * kHeadDim;
   const int64_t qbase = pofs / kHeadDim;
-  for (int p = tid; p < QR * QC; p += G::THREADS) {
-    const int row = p / QC, col = p - row * QC;
-    const int64_t qi = qbase + pixel_of(s, b, min(hq0 + row, hq1), min(hc0 + col, hc1));
-    lbuf[p] = f32x2{lse[qi], dqdot[qi]};
-  }
-  load_bias<T, NT>(rpb, b.h, btab, tid, G::THREADS);
-  __syncthreads();  // also completes the LDS copies
-
-  const int t0 = b.y0 + (wave / G::NTX) * G::TY, tx0 = b.x0 + (wave % G::NTX) * G::TX;
-  if (t0 >= Ly || tx0 >= Lx) return;
-  const int kyl = t0 + ql / G::TX, kxl = tx0 + ql % G::TX;
+  // this wave's key tile; its K / V operands load while the halo copy runs
+  const int t0 = b.y0 + (wave / G::NTX) * TY, tx0 = b.x0 + (wave % G::NTX) * TX;
+  const int kyl = t0 + ql / TX, kxl = tx0 + ql % TX;
   const bool kok = kyl < Ly && kxl < Lx;
   const int ky = min(kyl, Ly - 1), kx = min(kxl, Lx - 1);
   const unsigned kpix = pixel_of(s, b, ky, kx);
   const typename Mma<T>::vec kv = load_operand(k + pofs + (size_t)kpix * kHeadDim, g);
   const typename Mma<T>::vec vv = load_operand(v + pofs + (size_t)kpix * kHeadDim, g);
-  const int rlo = inv_lo(t0, KS), rhi = inv_hi(min(t0 + G::TY, Ly) - 1, Ly, KS);
-  const int clo = inv_lo(tx0, KS), chi = inv_hi(min(tx0 + G::TX, Lx) - 1, Lx, KS);
+  for (int p = tid; p < QR * QC; p += G::THREADS) {
+    const int row = p / QC, col = p - row * QC;
+    const int64_t qi = qbase + pixel_of(s, b, min(hq0 + row, hq1), min(hc0 + col, hc1));
+    lbuf[p] = f32x2{lse[qi], dqdot[qi]};
+  }
+  // entry (u, w): query - key offset (u - (TY-1) - (k-1), w - (TX-1) - (k-1))
+  fill_table<T, KS>(rpb, b.h, tabI, G::FH, FW, tid, G::THREADS, -INFINITY,
+                    [](int u, int w, int &by, int &bx) {
+                      const int oy = u - (TY - 1) - (KS - 1), ox = w - (TX - 1) - (KS - 1);
+                      by = KS - 1 - oy;
+                      bx = KS - 1 - ox;
+                      return oy >= -R && oy <= R && ox >= -R && ox <= R;
+                    });
+  fill_table<T, KS>(rpb, b.h, tabE, G::FH, FW, tid, G::THREADS, 0.f,
+                    [](int u, int w, int &by, int &bx) {
+                      by = KS - 1 - (u - (TY - 1) - (KS - 1));
+                      bx = KS - 1 - (w - (TX - 1) - (KS - 1));
+                      return true;
+                    });
+  __syncthreads();  // also completes the LDS copies
+  if (t0 >= Ly || tx0 >= Lx) return;
+  const int t1 = min(t0 + TY, Ly) - 1, tx1 = min(tx0 + TX, Lx) - 1;
+  const int rlo = inv_lo(t0, KS), rhi = inv_hi(t1, Ly, KS);
+  const int clo = inv_lo(tx0, KS), chi = inv_hi(tx1, Lx, KS);
+  // every query reaching the tile has an unclamped window (and the tile is
+  // whole): the window mask is the table's
+  const bool inner = t0 + TY - 1 < Ly && tx0 + TX - 1 < Lx && rlo >= R && rhi <= Ly - 1 - R &&
+                     clo >= R && chi <= Lx - 1 - R;
   const float c2 = kLog2e * kInvSqrtD;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 k0 = zero, k1 = zero, v0 = zero, v1 = zero;
+  // one row pair (r, r+1) of one 16-column chunk starting at c0
+  auto pair = [&](const float *tb, int r, int acol, int tc, const int (&lcol)[4],
+                  const float (&capx)[4], bool edge) {
+    f32x4 P[2], dS[2];
+    const int lrow0 = r - hq0;  // r + 1 - hq0 <= QR - 1: the staged rows cover the pair
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qr = r + u, lrow = lrow0 + u;
+      f32x4 cin;
+      if (edge) {
+        const int syq = window_start(min(qr, Ly - 1), Ly, KS);
+        const float capy = qr < Ly && (unsigned)(ky - syq) < (unsigned)KS ? INFINITY : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cin[i] = fminf(fminf(tb[u * FW + i], capx[i]), capy);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cin[i] = tb[u * FW + i];
+      }
+      const f32x4 sv = Mma<T>::run(halo_vec<T, QC>(qbuf, lrow, acol, g), kv, cin);
+      const f32x4 dpv = Mma<T>::run(halo_vec<T, QC>(gbuf, lrow, acol, g), vv, zero);
+      const f32x2 *lr = lbuf + lrow * QC;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x2 ld = lr[lcol[i]];
+        P[u][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ld[0]));
+        dS[u][i] = P[u][i] * (dpv[i] - ld[1]);
+      }
+    }
+    typename Mma<T>::vec phi, plo, shi, slo;
+    split_operand<T>(P[0], P[1], phi, plo);
+    split_operand<T>(dS[0], dS[1], shi, slo);
+    v0 = mma2<T>(halo_tr<T, QC>(gbuf, lrow0, tc, ql, 0), phi, plo, v0);
+    v1 = mma2<T>(halo_tr<T, QC>(gbuf, lrow0, tc, ql, 1), phi, plo, v1);
+    k0 = mma2<T>(halo_tr<T, QC>(qbuf, lrow0, tc, ql, 0), shi, slo, k0);
+    k1 = mma2<T>(halo_tr<T, QC>(qbuf, lrow0, tc, ql, 1), shi, slo, k1);
+  };
   for (int c0 = clo; c0 <= chi; c0 += 16) {
-    // this lane's 4 query columns c0 + 4g + i: window test, bias column and
-    // LDS column (clamped: columns past the halo are masked)
+    // this lane's 4 query columns c0 + 4g + i: window test and LDS column
+    // (clamped: columns past the halo are masked)
     float capx[4];
-    int colp[4], lcol[4];
+    int lcol[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qc = c0 + 4 * g + i;
-      const bool in = qc < Lx && (unsigned)(kx - window_start(min(qc, Lx - 1), Lx, KS)) < (unsigned)KS;
+      const bool in =
+          qc < Lx && (unsigned)(kx - window_start(min(qc, Lx - 1), Lx, KS)) < (unsigned)KS;
       capx[i] = in ? INFINITY : -INFINITY;
-      colp[i] = clampi(kx - qc + KS - 1, 0, SIDE - 1);
       lcol[i] = min(qc - hc0, QC - 1);
     }
     const int acol = min(c0 + ql - hc0, QC - 1);
     const int tc = min(c0 + 4 * g + (ql >> 2) - hc0, QC - 1);
-    for (int r = rlo; r <= rhi; r += 2) {
-      f32x4 P[2], dS[2];
-      const int lrow0 = r - hq0;  // r + 1 - hq0 <= QR - 1: the staged rows cover the pair
+    // table entry of (query row r, column c0 + 4g) against this lane's key
+    int bt = (rlo - ky + KS - 1 + TY - 1) * FW + (c0 + 4 * g - kx + KS - 1 + TX - 1);
+    asm volatile("" : "+v"(bt));
+    if (inner) {
+      const float *tb = tabI + bt;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qr = r + u, lrow = lrow0 + u;
-        const int syq = window_start(min(qr, Ly - 1), Ly, KS);
-        const float capy = qr < Ly && (unsigned)(ky - syq) < (unsigned)KS ? INFINITY : -INFINITY;
-        const int rowp = clampi(ky - qr + KS - 1, 0, SIDE - 1) * SIDE;
-        f32x4 cin;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cin[i] = fminf(fminf(btab[rowp + colp[i]], capx[i]), capy);
-        const f32x4 sv = Mma<T>::run(halo_vec<T, QC>(qbuf, lrow, acol, g), kv, cin);
-        const f32x4 dpv = Mma<T>::run(halo_vec<T, QC>(gbuf, lrow, acol, g), vv, zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x2 ld = lbuf[lrow * QC + lcol[i]];
-          P[u][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ld[0]));
-          dS[u][i] = P[u][i] * (dpv[i] - ld[1]);
-        }
-      }
-      typename Mma<T>::vec phi, plo, shi, slo;
-      split_operand<T>(P[0], P[1], phi, plo);
-      split_operand<T>(dS[0], dS[1], shi, slo);
-      v0 = mma2<T>(halo_tr<T, QC>(gbuf, lrow0, tc, ql, 0), phi, plo, v0);
-      v1 = mma2<T>(halo_tr<T, QC>(gbuf, lrow0, tc, ql, 1), phi, plo, v1);
-      k0 = mma2<T>(halo_tr<T, QC>(qbuf, lrow0, tc, ql, 0), shi, slo, k0);
-      k1 = mma2<T>(halo_tr<T, QC>(qbuf, lrow0, tc, ql, 1), shi, slo, k1);
+      for (int j = 0; j < (TY + KS - 1) / 2; ++j)
+        pair(tb + 2 * j * FW, rlo + 2 * j, acol, tc, lcol, capx, false);
+    } else {
+      const float *tb = tabE + bt;
+      for (int r = rlo; r <= rhi; r += 2, tb += 2 * FW) pair(tb, r, acol, tc, lcol, capx, true);
     }
   }
   if (kok) {
@@ -546,42 +656,61 @@ __global__ __launch_bounds__(kSumThreads) void bwd_bias_sum(const float *__restr
 struct Grid {
   int nby, nbx;
   int64_t bpp, nblocks;
+  BlockDivs divs;
 };
 
-template <int KS>
+template <int KS, int RY>
 Grid grid_of(const Shape &s) {
-  using G = BG<KS>;
+  using G = BG<KS, RY>;
   Grid r;
   r.nby = (class_len(s.H, 0, s.dil) + G::RY - 1) / G::RY;
   r.nbx = (class_len(s.W, 0, s.dil) + G::RX - 1) / G::RX;
   r.bpp = (int64_t)s.dil * s.dil * r.nby * r.nbx;
   r.nblocks = (int64_t)s.B * s.heads * r.bpp;
+  r.divs = BlockDivs{make_fastdiv((uint32_t)r.nbx), make_fastdiv((uint32_t)r.nby),
+                     make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)s.heads)};
   return r;
+}
+
+// Short residue classes take 8-row blocks (k <= 9; longer windows need
+// longer classes).
+inline bool short_classes(const Shape &s, int ks) {
+  return ks <= 9 && class_len(s.H, 0, s.dil) <= 8;
+}
+
+template <typename T, int KS, int RY>
+hipError_t launch_rt(const void *q, const void *k, const void *v, const void *rpb,
+                     const void *dout, void *dq, void *dk, void *dv, float *drpb, void *ws,
+                     const Shape &s, hipStream_t st) {
+  using G = BG<KS, RY>;
+  const Grid gr = grid_of<KS, RY>(s);
+  if (gr.nblocks > INT_MAX) return hipErrorInvalidConfiguration;
+  float *lse = (float *)ws;
+  float *dqdot = lse + s.n_query;
+  float *part = drpb != nullptr ? dqdot + s.n_query : nullptr;
+  bwd_query_mfma<T, KS, RY><<<dim3((unsigned)gr.nblocks), G::THREADS, 0, st>>>(
+      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (const T *)dout, (T *)dq, lse,
+      dqdot, part, s, gr.divs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_key_mfma<T, KS, RY><<<dim3((unsigned)gr.nblocks), G::THREADS, 0, st>>>(
+      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (const T *)dout, lse, dqdot,
+      (T *)dk, (T *)dv, s, gr.divs);
+  e = hipGetLastError();
+  if (e != hipSuccess || drpb == nullptr) return e;
+  bwd_bias_sum<<<dim3(G::NT, s.heads), kSumThreads, 0, st>>>(part, drpb, s.B, s.heads,
+                                                             (int)gr.bpp, G::NT);
+  return hipGetLastError();
 }
 
 template <typename T, int KS>
 hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb,
                     const void *dout, void *dq, void *dk, void *dv, float *drpb, void *ws,
                     const Shape &s, hipStream_t st) {
-  using G = BG<KS>;
-  const Grid gr = grid_of<KS>(s);
-  if (gr.nblocks > INT_MAX) return hipErrorInvalidConfiguration;
-  float *lse = (float *)ws;
-  float *dqdot = lse + s.n_query;
-  float *part = drpb != nullptr ? dqdot + s.n_query : nullptr;
-  bwd_query_mfma<T, KS><<<dim3((unsigned)gr.nblocks), G::THREADS, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (const T *)dout, (T *)dq, lse,
-      dqdot, part, s, gr.nby, gr.nbx);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  bwd_key_mfma<T, KS><<<dim3((unsigned)gr.nblocks), G::THREADS, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (const T *)dout, lse, dqdot,
-      (T *)dk, (T *)dv, s, gr.nby, gr.nbx);
-  e = hipGetLastError();
-  if (e != hipSuccess || drpb == nullptr) return e;
-  bwd_bias_sum<<<dim3(G::NT, s.heads), kSumThreads, 0, st>>>(part, drpb, s.B, s.heads,
-                                                             (int)gr.bpp, G::NT);
-  return hipGetLastError();
+  if constexpr (KS <= 9)
+    if (short_classes(s, KS))
+      return launch_rt<T, KS, 8>(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, s, st);
+  return launch_rt<T, KS, 16>(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, s, st);
 }
 
 template <typename T>
@@ -601,7 +730,9 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 
 template <int KS>
 int64_t blocks_of(const Shape &s) {
-  return grid_of<KS>(s).nblocks;
+  if constexpr (KS <= 9)
+    if (short_classes(s, KS)) return grid_of<KS, 8>(s).nblocks;
+  return grid_of<KS, 16>(s).nblocks;
 }
 
 }  // namespace
