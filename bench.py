@@ -154,6 +154,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="nat_tiny_s1", choices=sorted(WORKLOADS))
     ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
+    ap.add_argument("--layout", default="dense", choices=["dense", "channels_last"],
+                    help="forward I/O layout: dense [B, heads, H, W, D], or channels-last "
+                         "[B, H, W, heads*D] through na2d_forward_strided")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-reference", action="store_true",
@@ -195,22 +198,40 @@ def main(argv=None):
 
     cpu = I.make_inputs(p, seed=0)
     q0, k0, v0, rpb0 = cpu
+    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
+    algo = {"fused": 0, "fma": 1}.get(args.path, 0)
+    B, heads, H, W, D = p.shape
+    ks, dil = p.kernel_size, p.dilation
+    cl = args.layout == "channels_last"
+    if cl and args.path != "fused":
+        print("--layout channels_last takes the fused path only", file=sys.stderr)
+        return 2
     tbytes = q0.numel() * q0.element_size()
     attn_bytes = p.n_query_heads * p.kernel_size ** 2 * 4 if args.path == "unfused" else 0
     per_replica = 4 * tbytes + attn_bytes
     R = max(2, math.ceil(args.rotate_bytes / per_replica))
     rpb = rpb0.to(dev)
     reps = []
+
+    def relayout(t):
+        # [B, heads, H, W, D] -> channels-last [B, H, W, heads*D], viewed per head
+        x = t.permute(0, 2, 3, 1, 4).reshape(t.shape[0], t.shape[2], t.shape[3], -1)
+        return na2d.heads_view(x.contiguous().to(dev), t.shape[1])
+
     for _ in range(R):
-        q, k, v = (t.to(dev) for t in (q0, k0, v0))
-        out = torch.empty_like(q)
+        if cl:
+            q, k, v = (relayout(t) for t in (q0, k0, v0))
+            out = na2d.heads_view(torch.empty((B, H, W, heads * D), dtype=q.dtype, device=dev),
+                                  heads)
+        else:
+            q, k, v = (t.to(dev) for t in (q0, k0, v0))
+            out = torch.empty_like(q)
         attn = (torch.empty(p.shape[:4] + (p.kernel_size ** 2,), dtype=torch.float32,
                             device=dev) if args.path == "unfused" else None)
         reps.append((q, k, v, out, attn))
-    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
-    algo = {"fused": 0, "fma": 1}.get(args.path, 0)
-    B, heads, H, W, D = p.shape
-    ks, dil = p.kernel_size, p.dilation
+
+    si = (ctypes.c_int64 * 4)(*reps[0][0].stride()[:4])
+    so = (ctypes.c_int64 * 4)(*reps[0][3].stride()[:4])
 
     def launch(i, stream):
         q, k, v, out, attn = reps[i % R]
@@ -221,6 +242,10 @@ def main(argv=None):
             r = r or L.na2d_softmax(attn.data_ptr(), attn.data_ptr(), B, heads, H, W, ks, st)
             r = r or L.na2d_av(attn.data_ptr(), v.data_ptr(), out.data_ptr(),
                                B, heads, H, W, D, ks, dil, dt_code, st)
+        elif cl:
+            r = L.na2d_forward_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                       out.data_ptr(), B, heads, H, W, D, ks, dil, si, so,
+                                       dt_code, st)
         else:
             r = L.na2d_forward_algo(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
                                     out.data_ptr(), B, heads, H, W, D, ks, dil, dt_code,
@@ -237,7 +262,8 @@ def main(argv=None):
     idx = np.random.default_rng(0).choice(p.n_query_heads, size=min(4096, p.n_query_heads),
                                           replace=False)
     ref = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx)["out"]
-    got = reps[0][3].reshape(-1, D)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+    got = reps[0][3].contiguous().reshape(-1, D)[torch.from_numpy(idx).to(dev)]
+    got = got.double().cpu().numpy()
     max_err = float(np.abs(got - ref).max())
 
     value = p.n_query_heads / (ms_per_step / 1e3)
@@ -245,7 +271,7 @@ def main(argv=None):
     if args.path == "unfused":
         abytes += 4 * p.n_query_heads * p.kernel_size ** 2 * 4  # fp32 attn w, r, w, r
     achieved = abytes / (kernel_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload, args.path)
+    traffic = measured_traffic(args.workload, args.path if not cl else "strided")
 
     rec = {
         "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
@@ -263,6 +289,7 @@ def main(argv=None):
         "config": {"workload": "%s: %s" % (args.workload, p.describe()),
                    "B": B, "heads": heads, "H": H, "W": W, "D": D,
                    "kernel_size": ks, "dilation": dil, "path": args.path,
+                   "layout": args.layout,
                    "timing": args.mode, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -47,6 +47,7 @@
 #define NA2D_H
 
 #include <hip/hip_runtime_api.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -83,13 +84,41 @@ na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const vo
                            hipStream_t stream);
 
 /* na2d_forward with an explicit kernel family.  NA2D_ALGO_MFMA returns
- * NA2D_ERROR_NOT_SUPPORTED for fp32 data and for (batch, head) planes of
- * 2^24 pixels or more (H*W >= 16777216); NA2D_ALGO_AUTO sends such planes to
- * the FMA kernel. */
+ * NA2D_ERROR_NOT_SUPPORTED for fp32 data and for (batch, head) planes that
+ * span more than 2^31 bytes (H*W > 2^25 pixels at 16 bits); NA2D_ALGO_AUTO
+ * sends such planes to the FMA kernel. */
 na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, const void *rpb,
                                 void *out, int B, int heads, int H, int W, int D,
                                 int kernel_size, int dilation, na2d_dtype_t dtype,
                                 na2d_algo_t algo, hipStream_t stream);
+
+/*
+ * na2d_forward on strided views: the same operator, with q, k, v and out
+ * addressed as [B, heads, H, W, D] views whose element (b, h, i, j, e) sits
+ * at  b*s[0] + h*s[1] + i*s[2] + j*s[3] + e  (D channels contiguous).  This
+ * reads channels-last hidden states as the NAT/DiNAT encoders keep them
+ * ([B, H, W, heads*D]: s = {H*W*heads*D, D, W*heads*D, heads*D}; DiNAT
+ * walk-through blog, encoder section, and the blog's attention module, which
+ * splits the channels into heads) and writes out in that layout, with no
+ * permute around the call; a fused QKV buffer [B, H, W, 3*heads*D] passes
+ * q, k, v as three base pointers with shared strides.
+ *
+ *   in_strides   4 element strides (batch, head, row, column) shared by q,
+ *                k and v; host memory, read during the call only
+ *   out_strides  4 element strides of out; host memory
+ *
+ * Strides must be >= 0 with every stride times the element size a multiple
+ * of 16 bytes; out's strides must not map two elements to one address; out's
+ * footprint (first to last element it touches) must not overlap q's, k's,
+ * v's or rpb's.  Violations return NA2D_ERROR_INVALID_VALUE before any HIP
+ * call.  Kernel family as NA2D_ALGO_AUTO; dense strides take exactly the
+ * na2d_forward path.  Other conventions as na2d_forward.
+ */
+na2d_status_t na2d_forward_strided(const void *q, const void *k, const void *v,
+                                   const void *rpb, void *out, int B, int heads, int H, int W,
+                                   int D, int kernel_size, int dilation,
+                                   const int64_t *in_strides, const int64_t *out_strides,
+                                   na2d_dtype_t dtype, hipStream_t stream);
 
 /*
  * Unfused step 1 (the blog's natten2dqkrpb): attn[b,h,i,j,n] =

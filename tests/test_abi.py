@@ -220,3 +220,84 @@ def test_backward_rejects_overlaps(a, b):
     ptrs = list(BP)
     ptrs[a] = ctypes.c_void_p(ptrs[b].value + 16)
     assert _backward(L, ptrs, VALID) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# na2d_forward_strided: same shape rules, plus the stride rules.
+def _strides(*vals):
+    return (ctypes.c_int64 * 4)(*vals)
+
+
+def _planar(B, h, H, W, D=32):
+    return (h * H * W * D, H * W * D, W * D, D)
+
+
+@pytest.mark.parametrize("args,expect", FORWARD_CASES)
+def test_strided_forward_shape_validation(args, expect):
+    L = na2d.lib()
+    B, h, H, W, D, ks, d, dt = args
+    st = _strides(*_planar(1, 1, 14, 14))  # valid strides; the shape decides
+    assert L.na2d_forward_strided(P[0], P[1], P[2], P[3], P[4], B, h, H, W, D, ks, d, st, st,
+                                  dt, S) == expect
+
+
+# channels-last hidden states [B, H, W, heads*D] seen as [B, heads, H, W, D]
+def _channels_last(B, h, H, W, D=32):
+    return (H * W * h * D, D, W * h * D, h * D)
+
+
+CL = _channels_last(2, 2, 14, 14)
+STRIDE_CASES = [
+    ((-32, 32, 28 * 32, 64), CL, INVALID),            # negative stride
+    (CL, (896 * 14 * 2, 32, 896, -64), INVALID),
+    ((CL[0], CL[1], CL[2], 36), CL, INVALID),         # 72-byte pixel steps: not 16-byte multiples
+    (CL, (CL[0], 36, CL[2], CL[3]), INVALID),
+    (CL, (CL[0], CL[1], CL[2], 16), INVALID),         # out pixels overlap (step < D)
+    (CL, (CL[0], 0, CL[2], CL[3]), INVALID),          # both heads on the same out elements
+    (CL, (CL[0], CL[1], 32, CL[3]), INVALID),         # rows collide with columns
+    (CL, (0, CL[1], CL[2], CL[3]), INVALID),          # both batch items on the same out
+    ((1 << 58, CL[1], CL[2], CL[3]), CL, INVALID),    # footprint overflow
+]
+
+
+@pytest.mark.parametrize("si,so,expect", STRIDE_CASES)
+def test_strided_forward_stride_rules(si, so, expect):
+    L = na2d.lib()
+    B, h, H, W, D, ks, d = 2, 2, 14, 14, 32, 7, 1
+    # q, k, v, out far apart so that only the stride rule can fail
+    ptrs = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]
+    assert L.na2d_forward_strided(*ptrs, B, h, H, W, D, ks, d, _strides(*si), _strides(*so),
+                                  BF16, S) == expect
+
+
+def test_strided_forward_null_strides_and_pointers():
+    L = na2d.lib()
+    st = _strides(*CL)
+    args = (2, 2, 14, 14, 32, 7, 1)
+    ptrs = [ctypes.c_void_p((1 << 40) * (i + 1)) for i in range(5)]
+    assert L.na2d_forward_strided(*ptrs, *args, None, st, BF16, S) == INVALID
+    assert L.na2d_forward_strided(*ptrs, *args, st, None, BF16, S) == INVALID
+    for slot in (0, 1, 2, 4):
+        p = list(ptrs)
+        p[slot] = NULL
+        assert L.na2d_forward_strided(*p, *args, st, st, BF16, S) == INVALID
+        p[slot] = ctypes.c_void_p(ptrs[slot].value + 8)
+        assert L.na2d_forward_strided(*p, *args, st, st, BF16, S) == INVALID
+
+
+def test_strided_forward_rejects_out_overlapping_an_input():
+    L = na2d.lib()
+    st = _strides(*CL)
+    args = (2, 2, 14, 14, 32, 7, 1)
+    base = 1 << 40
+    # a fused QKV buffer (q, k, v at channel offsets 0, 64, 128 of 192-channel
+    # pixels) with out written into the same buffer's last channels
+    qkv = (14 * 14 * 192, 32, 14 * 192, 192)
+    q, k, v = (ctypes.c_void_p(base + off * 2) for off in (0, 64, 128))
+    out = ctypes.c_void_p(base + 128 * 2 + 64)
+    assert L.na2d_forward_strided(q, k, v, NULL, out, *args, _strides(*qkv), st, BF16,
+                                  S) == INVALID
+    # out starting inside v's footprint
+    far = [ctypes.c_void_p((1 << 41) * (i + 1)) for i in range(3)]
+    inside = ctypes.c_void_p(far[2].value + 4096)
+    assert L.na2d_forward_strided(*far, NULL, inside, *args, st, st, BF16, S) == INVALID

@@ -8,7 +8,8 @@
 
 namespace {
 
-constexpr int64_t kMaxElems = (int64_t)1 << 60;  // keeps byte counts (x4) in int64
+constexpr int64_t kMaxElems = (int64_t)1 << 60;   // keeps byte counts (x4) in int64
+constexpr int64_t kMaxStride = (int64_t)1 << 58;  // per dimension, stride * (extent - 1)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,6 +53,51 @@ na2d_status_t from_hip(hipError_t e) {
   return e == hipErrorInvalidConfiguration ? NA2D_ERROR_NOT_SUPPORTED : NA2D_ERROR_LAUNCH_FAILURE;
 }
 
+// Bytes from the first to one past the last element a [B, heads, H, W, D]
+// view with these (non-negative) strides touches.
+int64_t footprint(const na2d::Strides &t, const na2d::Shape &s, int64_t elem) {
+  return ((int64_t)(s.B - 1) * t.b + (int64_t)(s.heads - 1) * t.h + (int64_t)(s.H - 1) * t.y +
+          (int64_t)(s.W - 1) * t.x + na2d::kHeadDim) *
+         elem;
+}
+
+// True when no two elements of the view share an address: with the
+// dimensions ordered by stride, each stride must step past everything the
+// smaller dimensions span (size-1 dimensions impose nothing).
+bool injective(const na2d::Strides &t, const na2d::Shape &s) {
+  int64_t st[4] = {t.b, t.h, t.y, t.x}, ex[4] = {s.B, s.heads, s.H, s.W};
+  for (int i = 0; i < 4; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      int64_t a = st[j]; st[j] = st[j - 1]; st[j - 1] = a;
+      a = ex[j]; ex[j] = ex[j - 1]; ex[j - 1] = a;
+    }
+  int64_t span = na2d::kHeadDim;  // elements covered by the smaller dimensions
+  for (int i = 0; i < 4; ++i) {
+    if (ex[i] == 1) continue;
+    if (st[i] < span) return false;
+    span += (ex[i] - 1) * st[i];
+  }
+  return true;
+}
+
+// The forward pass for checked shapes, pointers and strides.
+na2d_status_t forward_checked(const void *q, const void *k, const void *v, const void *rpb,
+                              void *out, const na2d::Shape &s, const na2d::Strides &in,
+                              const na2d::Strides &os, na2d_dtype_t dtype, na2d_algo_t algo,
+                              hipStream_t stream) {
+  const bool automatic = algo == NA2D_ALGO_AUTO;
+  if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
+  if (algo == NA2D_ALGO_MFMA) {
+    if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
+    bool supported = true;
+    hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, dtype, stream, &supported);
+    if (supported) return from_hip(e);
+    if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
+    // planes too large for 32-bit in-plane offsets: the FMA kernel handles them
+  }
+  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, dtype, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,17 +125,44 @@ na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, con
     if (overlaps(out, tbytes, rpb, heads * side * side * elem_bytes(dtype)))
       return NA2D_ERROR_INVALID_VALUE;
   }
-  const bool automatic = algo == NA2D_ALGO_AUTO;
-  if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
-  if (algo == NA2D_ALGO_MFMA) {
-    if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
-    bool supported = true;
-    hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, dtype, stream, &supported);
-    if (supported) return from_hip(e);
-    if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
-    // planes of 2^24 pixels or more: the general kernel handles them
+  const na2d::Strides pl = na2d::planar_strides(s);
+  return forward_checked(q, k, v, rpb, out, s, pl, pl, dtype, algo, stream);
+}
+
+na2d_status_t na2d_forward_strided(const void *q, const void *k, const void *v,
+                                   const void *rpb, void *out, int B, int heads, int H, int W,
+                                   int D, int kernel_size, int dilation,
+                                   const int64_t *in_strides, const int64_t *out_strides,
+                                   na2d_dtype_t dtype, hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!q || !k || !v || !out || !in_strides || !out_strides) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (rpb && !aligned16(rpb)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const na2d::Strides in{in_strides[0], in_strides[1], in_strides[2], in_strides[3]};
+  const na2d::Strides os{out_strides[0], out_strides[1], out_strides[2], out_strides[3]};
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t all[8] = {in.b, in.h, in.y, in.x, os.b, os.h, os.y, os.x};
+  const int64_t ext[4] = {B, heads, H, W};
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = all[i], e = ext[i % 4];
+    // bounded so that footprints stay far inside int64; every pixel's D
+    // channels start on a 16-byte boundary
+    if (t < 0 || t > kMaxStride || (e > 1 && t > kMaxStride / (e - 1)) || (t * eb) % 16 != 0)
+      return NA2D_ERROR_INVALID_VALUE;
   }
-  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, dtype, stream));
+  if (!injective(os, s)) return NA2D_ERROR_INVALID_VALUE;  // out elements must not alias
+  const int64_t ib = footprint(in, s, eb), ob = footprint(os, s, eb);
+  if (overlaps(out, ob, q, ib) || overlaps(out, ob, k, ib) || overlaps(out, ob, v, ib))
+    return NA2D_ERROR_INVALID_VALUE;
+  if (rpb) {
+    const int64_t side = 2 * kernel_size - 1;
+    if (overlaps(out, ob, rpb, heads * side * side * eb)) return NA2D_ERROR_INVALID_VALUE;
+  }
+  return forward_checked(q, k, v, rpb, out, s, in, os, dtype, NA2D_ALGO_AUTO, stream);
 }
 
 na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const void *rpb,

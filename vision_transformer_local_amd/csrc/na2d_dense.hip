@@ -55,13 +55,12 @@ template <int KS> struct DenseGeometry {
 };
 
 // Byte offset of pixel (0, 0) of class jh (numbered (b, ry, rx), rx fastest)
-// of head h.
+// of head h, for a view with byte strides st.
 __device__ __forceinline__ int64_t class_base(int h, int jh, const Shape &s, int log2d,
-                                              int64_t plane_bytes, unsigned pixel_bytes) {
+                                              const ByteStrides &st) {
   const int d = s.dil;
   const int rx = jh & (d - 1), ry = (jh >> log2d) & (d - 1), b = jh >> (2 * log2d);
-  const int64_t plane = (int64_t)b * s.heads + h;
-  return plane * plane_bytes + (int64_t)(ry * s.W + rx) * pixel_bytes;
+  return b * st.b + h * st.h + (int64_t)(ry * st.y + rx * st.x);
 }
 
 // Block id -> (head, first class within the head, classes in the block).
@@ -82,14 +81,13 @@ __device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &fbph, i
 template <typename T, int KS>
 __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fbph, int per_head,
-    int nblocks, int log2d) {
+    const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
+    FastDiv fbph, int per_head, int nblocks, int log2d) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, TPW = G::TPW, SG = G::SG;
   constexpr int CB = G::CB, DPT = G::DPT, DPW = G::DPW, SIDE = G::SIDE;
   constexpr int WAVES = G::WAVES, THREADS = G::THREADS;
-  constexpr unsigned PB = kHeadDim * sizeof(T);  // bytes per pixel
   __shared__ __attribute__((aligned(16))) char kbuf0[SG * CB], vbuf0[SG * CB];
   __shared__ __attribute__((aligned(16))) char kbuf1[SG * CB], vbuf1[SG * CB];
   __shared__ __attribute__((aligned(16))) float ctab[G::NCT];  // [tile][key block][lane][4]
@@ -101,8 +99,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
   if (b0 >= b1) return;
   const int d = s.dil;
-  const int64_t plane_bytes = (int64_t)s.H * s.W * PB;
-  const unsigned rowb = (unsigned)d * (unsigned)s.W * PB, colb = (unsigned)d * PB;
+  const unsigned rowb = (unsigned)d * si.y, colb = (unsigned)d * si.x;
 
   // ---- per-lane constants: DMA slots, query positions ----
   // DMA instruction i = wave + WAVES * m covers 16 key slots (4 lanes each)
@@ -119,12 +116,13 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   }
   // this wave's tiles: tile t = wave*TPW + u of the block is tile t % NT of
   // class t / NT; lane query slot tt*16 + ql (clamped to the last query)
-  unsigned qoff[TPW];
+  unsigned qoff[TPW], ooff[TPW];  // in q and in out
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tt = (wave * TPW + u) % NT;
     const int nq = min(tt * 16 + ql, N - 1);
     qoff[u] = (unsigned)(nq / KS) * rowb + (unsigned)(nq % KS) * colb;
+    ooff[u] = (unsigned)(nq / KS) * ((unsigned)d * so.y) + (unsigned)(nq % KS) * ((unsigned)d * so.x);
   }
 
   // accumulator table for head h: entry (tt, kb, lane, i) = bias * sqrt(D)
@@ -162,19 +160,19 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
       const int i = wave + WAVES * m;
       const bool isv = i >= DPT;
       const int it = i % DPT, c = it / (NK / 16), kg = it % (NK / 16);
-      const int64_t base = class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, plane_bytes, PB);
+      const int64_t base = class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, si);
       const char *src = (const char *)(isv ? v : k) + base;
       char *dst = (isv ? vb : kb) + c * CB + kg * 1024;
       __builtin_amdgcn_global_load_lds((const void *)(src + doff[m]), (lds_void *)dst, 16, 0, 0);
     }
   };
-  // byte offset of this wave's tile u query pixel in block bk
-  auto tile_base = [&](const DenseBlock &bk, int u) -> int64_t {
+  // byte offset of the class of this wave's tile u in block bk (strides st)
+  auto tile_base = [&](const DenseBlock &bk, int u, const ByteStrides &st) -> int64_t {
     const int c = (wave * TPW + u) / NT;
-    return class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, plane_bytes, PB);
+    return class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, st);
   };
   auto load_q = [&](const DenseBlock &bk, int u) -> u32x4 {
-    return *(const u32x4 *)((const char *)q + tile_base(bk, u) + qoff[u] + g * 16u);
+    return *(const u32x4 *)((const char *)q + tile_base(bk, u, si) + qoff[u] + g * 16u);
   };
 
   const float c2 = kLog2e / kSqrtD;
@@ -263,7 +261,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   };
   auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok) {
     if (ok) {
-      char *o = (char *)out + tile_base(bk, u) + qoff[u] + g * 8u;
+      char *o = (char *)out + tile_base(bk, u, so) + ooff[u] + g * 8u;
       *(u32x2 *)o = u32x2{val[0], val[1]};
       *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{val[2], val[3]};
     }
@@ -337,7 +335,8 @@ int dense_cus() {
 
 template <typename T, int KS>
 hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
-                        const Shape &s, hipStream_t st) {
+                        const Shape &s, const ByteStrides &si, const ByteStrides &so,
+                        hipStream_t st) {
   using G = DenseGeometry<KS>;
   const int64_t per_head = (int64_t)s.B * s.dil * s.dil;  // classes of one head
   const int64_t bph = (per_head + G::SG - 1) / G::SG;      // blocks per head
@@ -347,7 +346,7 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   while ((1 << log2d) < s.dil) ++log2d;
   const int64_t grid = nblocks < dense_cus() ? nblocks : dense_cus();
   dense_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
+      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, si, so,
       make_fastdiv((uint32_t)bph), (int)per_head, (int)nblocks, log2d);
   return hipGetLastError();
 }
@@ -355,27 +354,27 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
 }  // namespace
 
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
-                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             void *out, const Shape &s, const ByteStrides &si,
+                             const ByteStrides &so, na2d_dtype_t dt, hipStream_t st,
                              bool *supported) {
   *supported = true;
   const bool pow2_dil = (s.dil & (s.dil - 1)) == 0;
   if ((int64_t)s.ks * s.dil != s.H || (int64_t)s.ks * s.dil != s.W || !pow2_dil ||
-      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32 ||
-      (int64_t)s.H * s.W >= kMaxPlanePixels) {
+      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32) {
     *supported = false;
     return hipSuccess;
   }
   if (dt == NA2D_DTYPE_BF16) {
     switch (s.ks) {
-      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, st);
-      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, st);
-      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, st);
+      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, si, so, st);
+      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, si, so, st);
+      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, si, so, st);
     }
   }
   switch (s.ks) {
-    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, st);
-    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, st);
-    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, st);
+    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, si, so, st);
+    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, si, so, st);
+    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, si, so, st);
   }
 }
 

@@ -88,17 +88,42 @@ struct Shape {
   int64_t n_query;  // B * heads * H * W
 };
 
+// Element strides of a tensor seen as [B, heads, H, W, D] with D contiguous:
+// element (b, h, i, j, e) sits at b*b + h*h + i*y + j*x + e.  The dense
+// layout is one choice of strides; channels-last hidden states
+// ([B, H, W, heads*D], DiNAT walk-through blog, encoder section) another.
+struct Strides {
+  int64_t b, h, y, x;
+};
+
+inline Strides planar_strides(const Shape &s) {
+  const int64_t px = kHeadDim, row = (int64_t)s.W * px, plane = (int64_t)s.H * row;
+  return Strides{plane * s.heads, plane, row, px};
+}
+
+inline bool is_planar(const Strides &t, const Shape &s) {
+  const Strides p = planar_strides(s);
+  return t.b == p.b && t.h == p.h && t.y == p.y && t.x == p.x;
+}
+
 // Launchers (one per kernel family); each returns hipSuccess or the launch
-// error.  Argument checking happens before these are reached.
+// error.  Argument checking happens before these are reached.  q, k and v
+// share the strides `in`; out has its own.
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
-                            void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st);
+                            void *out, const Shape &s, const Strides &in, const Strides &out_st,
+                            na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
-                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             void *out, const Shape &s, const Strides &in,
+                             const Strides &out_st, na2d_dtype_t dt, hipStream_t st,
                              bool *supported);
 // Whole-sub-grid kernel (H == W == k*d); sets *supported = false when the
-// problem is not of that kind.
+// problem is not of that kind.  Strides in bytes (mfma::ByteStrides).
+namespace mfma {
+struct ByteStrides;
+}
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
-                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             void *out, const Shape &s, const mfma::ByteStrides &in,
+                             const mfma::ByteStrides &out_st, na2d_dtype_t dt, hipStream_t st,
                              bool *supported);
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);

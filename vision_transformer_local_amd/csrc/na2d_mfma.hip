@@ -92,11 +92,13 @@ template <int KS, int RYV = default_rows(KS)> struct Geometry {
   static_assert((2 * PIX * 128 + 2 * NTAB * 4) <= 160 * 1024, "LDS");
 };
 
-// Block ids enumerate (plane, ry, by, bx, rx) with rx fastest.  A workgroup
-// visits consecutive ids, so it keeps the mixed-radix digits and steps them.
+// Block ids enumerate (batch, head, ry, by, bx, rx) with rx fastest.  A
+// workgroup visits consecutive ids, so it keeps the mixed-radix digits and
+// steps them.  (With channels-last maps the heads of a pixel share its
+// lines; making the head the fastest digit was tried and lost the halo
+// reuse between neighbouring blocks: 2.6x the L2 misses.)
 struct BlockCursor {
-  int64_t plane;
-  int h, ry, by, bx, rx;
+  int b, h, ry, by, bx, rx;
 };
 
 __device__ __forceinline__ BlockCursor cursor_at(uint32_t id, int dil, const FastDiv &fdil,
@@ -114,12 +116,13 @@ __device__ __forceinline__ BlockCursor cursor_at(uint32_t id, int dil, const Fas
   id = t;
   t = fast_div(id, fdil);
   c.ry = id - t * dil;
-  c.plane = t;
-  c.h = (int)(t - fast_div(t, fheads) * fheads.div);
+  const uint32_t bq = fast_div(t, fheads);
+  c.b = (int)bq;
+  c.h = (int)(t - bq * fheads.div);
   return c;
 }
 
-// Steps to the next id; true when (plane, ry, by) changed.
+// Steps to the next id; true when the row part (batch, head, ry, by) changed.
 __device__ __forceinline__ bool cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads) {
   if (++c.rx < dil) return false;
   c.rx = 0;
@@ -129,20 +132,23 @@ __device__ __forceinline__ bool cursor_step(BlockCursor &c, int dil, int nbx, in
   c.by = 0;
   if (++c.ry < dil) return true;
   c.ry = 0;
-  ++c.plane;
-  if (++c.h == heads) c.h = 0;
+  if (++c.h == heads) {
+    c.h = 0;
+    ++c.b;
+  }
   return true;
 }
 
 // A block splits into a row part, which depends on (plane, ry, by) only and
 // is recomputed when those change, and a column part, which depends on
 // (rx, bx).  Both include what this wave's tile and this lane's query need.
-// Byte offsets within a plane fit 32 bits (planes hold < 2^24 pixels).
+// Byte offsets within a plane fit 32 bits.
 struct RowPart {
-  int64_t pofs;    // element offset of the (batch, head) plane
+  int64_t pofs;    // byte offset of the (batch, head) plane of q, k, v
+  int64_t opofs;   // the same for out
   int h, Ly, rc0, rc1, hy0, HR;
   int tci0, Y0;    // first query row of this wave's tile; first key row of its key block
-  unsigned hrow;   // byte offset of the first halo row: (ry + hy0*d) * W * 64
+  unsigned hrow;   // byte offset of the first halo row: (ry + hy0*d) * row stride
   int ry;
   int ok, inner;   // block row exists; the tile's windows are unclamped in y
 };
@@ -150,18 +156,20 @@ struct RowPart {
 struct ColPart {
   int Lx, cc0, cc1, hx0, cmax;
   int tcj0, X0;
-  unsigned hcol;   // byte offset of the first halo column: (rx + hx0*d) * 64
+  unsigned hcol;   // byte offset of the first halo column: (rx + hx0*d) * column stride
   int rx;
   int ok, inner;
 };
 
 template <typename T, int KS, int RY>
 __device__ __forceinline__ RowPart row_part(const BlockCursor &c, const Shape &s,
-                                            const FastDiv &fdil, int64_t pstride, int ty, int lr) {
+                                            const FastDiv &fdil, const ByteStrides &si,
+                                            const ByteStrides &so, int ty, int lr) {
   using G = Geometry<KS, RY>;
   constexpr int R = KS / 2;
   RowPart r;
-  r.pofs = c.plane * pstride;
+  r.pofs = c.b * si.b + c.h * si.h;
+  r.opofs = c.b * so.b + c.h * so.h;
   r.h = c.h;
   // class_len(n, r, d) = (n - r + d - 1) / d
   r.Ly = fast_div((uint32_t)(s.H - c.ry + s.dil - 1), fdil);
@@ -173,14 +181,15 @@ __device__ __forceinline__ RowPart row_part(const BlockCursor &c, const Shape &s
   r.tci0 = r.rc0 + ty * G::TY;
   r.Y0 = window_start(r.tci0, r.Ly, KS);
   r.inner = r.tci0 >= R && r.tci0 + G::TY - 1 + R <= r.Ly - 1;
-  r.hrow = (unsigned)((c.ry + r.hy0 * s.dil) * s.W) * (unsigned)(kHeadDim * sizeof(T));
+  r.hrow = (unsigned)(c.ry + r.hy0 * s.dil) * si.y;
   r.ry = c.ry;
   return r;
 }
 
 template <typename T, int KS>
 __device__ __forceinline__ ColPart col_part(const BlockCursor &c, const Shape &s,
-                                            const FastDiv &fdil, int tx, int lc) {
+                                            const FastDiv &fdil, const ByteStrides &si, int tx,
+                                            int lc) {
   using G = Geometry<KS>;
   constexpr int R = KS / 2;
   ColPart q;
@@ -193,20 +202,26 @@ __device__ __forceinline__ ColPart col_part(const BlockCursor &c, const Shape &s
   q.tcj0 = q.cc0 + tx * G::TX;
   q.X0 = window_start(q.tcj0, q.Lx, KS);
   q.inner = q.tcj0 >= R && q.tcj0 + G::TX - 1 + R <= q.Lx - 1;
-  q.hcol = (unsigned)(c.rx + q.hx0 * s.dil) * (unsigned)(kHeadDim * sizeof(T));
+  q.hcol = (unsigned)(c.rx + q.hx0 * s.dil) * si.x;
   q.rx = c.rx;
   return q;
 }
 
-// In-plane pixel index of this lane's query (block row lr, block column lc),
-// clamped into a ragged block: such lanes recompute a real query and store
-// nothing.
-__device__ __forceinline__ int query_pixel(const RowPart &r, const ColPart &c, const Shape &s,
-                                           int lr, int lc) {
+// In-plane byte offsets of this lane's query (block row lr, block column
+// lc) in q and in out, clamped into a ragged block: such lanes recompute a
+// real query and store nothing.
+struct QueryOffs {
+  unsigned q, o;
+};
+
+__device__ __forceinline__ QueryOffs query_offsets(const RowPart &r, const ColPart &c,
+                                                   const Shape &s, const ByteStrides &si,
+                                                   const ByteStrides &so, int lr, int lc) {
   const int ci = r.rc0 + min(lr, r.rc1 - 1 - r.rc0);
   const int cj = c.cc0 + min(lc, c.cc1 - 1 - c.cc0);
-  return (int)__umul24(r.ry + __umul24((unsigned)ci, (unsigned)s.dil), (unsigned)s.W) + c.rx +
-         (int)__umul24((unsigned)cj, (unsigned)s.dil);
+  const unsigned row = r.ry + __umul24((unsigned)ci, (unsigned)s.dil);
+  const unsigned col = c.rx + __umul24((unsigned)cj, (unsigned)s.dil);
+  return QueryOffs{row * si.y + col * si.x, row * so.y + col * so.x};
 }
 
 // Copy a block's K and V halo into one LDS buffer with the direct
@@ -216,16 +231,16 @@ __device__ __forceinline__ int query_pixel(const RowPart &r, const ColPart &c, c
 template <typename T, int KS, int RY>
 __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__restrict__ v,
                                             const RowPart &r, const ColPart &c, const Shape &s,
-                                            char *kbuf, char *vbuf, int wave, int lane) {
+                                            const ByteStrides &si, char *kbuf, char *vbuf,
+                                            int wave, int lane) {
   using G = Geometry<KS, RY>;
   constexpr int NI = (G::PIX * 4 + 63) / 64;  // instructions per tensor (last one partial)
   constexpr int NW = G::NTILE;
-  constexpr unsigned PB = kHeadDim * sizeof(T);  // bytes per pixel
   const unsigned org = r.hrow + c.hcol;  // halo origin within the plane
-  const char *kb0 = (const char *)(k + r.pofs) + org;
-  const char *vb0 = (const char *)(v + r.pofs) + org;
-  const unsigned rowb = (unsigned)s.dil * (unsigned)s.W * PB;
-  const unsigned colb = (unsigned)s.dil * PB;
+  const char *kb0 = ((const char *)k + r.pofs) + org;
+  const char *vb0 = ((const char *)v + r.pofs) + org;
+  const unsigned rowb = (unsigned)s.dil * si.y;
+  const unsigned colb = (unsigned)s.dil * si.x;
   if constexpr (G::HCM == 16) {
     // one instruction = one staged row of one tensor: the column / chunk part
     // of the address is fixed per lane, the row part is uniform and shared by
@@ -316,15 +331,16 @@ __device__ __forceinline__ void store_tables(float *tab, int tid, bool has_rpb,
   }
 }
 
-// The 16-byte Q slice (channels 8g..8g+7) of the query at in-plane pixel pix.
+// The 16-byte Q slice (channels 8g..8g+7) of the query at in-plane byte
+// offset off.
 // Without dilation Q is read once and out written once, in whole cache
 // lines: both then bypass cache retention (non-temporal), leaving the caches
 // to the K/V halo rows that neighbouring blocks share.  With dilation the
 // classes rx and rx + 1, visited one after the other, share the lines.
 template <typename T, bool STREAM>
-__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, int64_t pofs, int pix, int g) {
-  const u32x4 *p = (const u32x4 *)((const char *)(q + pofs) +
-                                   ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 16u));
+__device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, int64_t pofs, unsigned off,
+                                        int g) {
+  const u32x4 *p = (const u32x4 *)(((const char *)q + pofs) + (off + g * 16u));
   if constexpr (STREAM) return __builtin_nontemporal_load(p);
   return *p;
 }
@@ -488,13 +504,12 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
   return finish<T>(acc, tci0 + qy < r.rc1 && tcj0 + qx < c.cc1);
 }
 
-// Writes a lane's TileOut to the query at in-plane pixel pix.
+// Writes a lane's TileOut to the query at in-plane byte offset off of out.
 template <typename T, bool STREAM>
-__device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, int pix, int g,
+__device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, unsigned off, int g,
                                           const TileOut &t) {
   if (t.ok) {
-    u32x2 *o = (u32x2 *)((char *)(out + pofs) +
-                         ((unsigned)pix * (unsigned)(kHeadDim * sizeof(T)) + g * 8u));
+    u32x2 *o = (u32x2 *)(((char *)out + pofs) + (off + g * 8u));
     if constexpr (STREAM) {
       __builtin_nontemporal_store(u32x2{t.val[0], t.val[1]}, o);
       __builtin_nontemporal_store(u32x2{t.val[2], t.val[3]}, o + 2 * sizeof(T));
@@ -505,12 +520,12 @@ __device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, int
   }
 }
 
-// STREAM: Q and out accesses are non-temporal (maps without dilation).
+// STREAM: Q and out accesses are non-temporal (dense maps without dilation).
 template <typename T, int KS, int RY, bool STREAM>
 __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ rpb, T *__restrict__ out, Shape s, FastDiv fdil, FastDiv fnbx,
-    FastDiv fnby, FastDiv fheads, int nblocks) {
+    const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
+    FastDiv fdil, FastDiv fnbx, FastDiv fnby, FastDiv fheads, int nblocks) {
   using G = Geometry<KS, RY>;
   __shared__ __attribute__((aligned(16))) char kbuf0[G::PIX * 64], vbuf0[G::PIX * 64];
   __shared__ __attribute__((aligned(16))) char kbuf1[G::PIX * 64], vbuf1[G::PIX * 64];
@@ -526,7 +541,6 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
   if (b0 >= b1) return;
   const bool has_rpb = rpb != nullptr;
-  const int64_t pstride = (int64_t)s.H * s.W * kHeadDim;  // elements per plane
   // this wave's tile and this lane's query position within a block
   const int ty = wave / G::NTX, tx = wave % G::NTX;
   const int lr = ty * G::TY + ql / G::TX, lc = tx * G::TX + ql % G::TX;
@@ -538,12 +552,13 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   // overlap the whole compute of block n.
   T treg[TableRegs<KS, RY>::N];
   BlockCursor cc = cursor_at(b0, s.dil, fdil, fnbx, fnby, fheads);
-  RowPart rcur = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
-  ColPart ccur = col_part<T, KS>(cc, s, fdil, tx, lc);
-  int pcur = query_pixel(rcur, ccur, s, lr, lc);
-  u32x4 qcur = load_q<T, STREAM>(q, rcur.pofs, pcur, g);
+  RowPart rcur = row_part<T, KS, RY>(cc, s, fdil, si, so, ty, lr);
+  ColPart ccur = col_part<T, KS>(cc, s, fdil, si, tx, lc);
+  QueryOffs pcur = query_offsets(rcur, ccur, s, si, so, lr, lc);
+  u32x4 qcur = load_q<T, STREAM>(q, rcur.pofs, pcur.q, g);
   load_tables<T, KS, RY>(rpb, rcur.h, tid, treg);
-  if (rcur.ok && ccur.ok) stage_block<T, KS, RY>(k, v, rcur, ccur, s, kbuf0, vbuf0, wave, lane);
+  if (rcur.ok && ccur.ok)
+    stage_block<T, KS, RY>(k, v, rcur, ccur, s, si, kbuf0, vbuf0, wave, lane);
   store_tables<T, KS, RY>(tab0, tid, has_rpb, treg);
   int tab_h0 = rcur.h, tab_h1 = -1;  // head whose tables each buffer holds
   __syncthreads();
@@ -556,13 +571,14 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
                   int &tab_hn, bool more) {
     RowPart rnxt = rcur;
     if (more && cursor_step(cc, s.dil, nbx, nby, s.heads))
-      rnxt = row_part<T, KS, RY>(cc, s, fdil, pstride, ty, lr);
-    const ColPart cnxt = col_part<T, KS>(cc, s, fdil, tx, lc);
-    const int pnxt = query_pixel(rnxt, cnxt, s, lr, lc);
-    const u32x4 qnxt = load_q<T, STREAM>(q, rnxt.pofs, pnxt, g);
+      rnxt = row_part<T, KS, RY>(cc, s, fdil, si, so, ty, lr);
+    const ColPart cnxt = col_part<T, KS>(cc, s, fdil, si, tx, lc);
+    const QueryOffs pnxt = query_offsets(rnxt, cnxt, s, si, so, lr, lc);
+    const u32x4 qnxt = load_q<T, STREAM>(q, rnxt.pofs, pnxt.q, g);
     const bool newtab = more && rnxt.h != tab_hn;
     if (newtab) load_tables<T, KS, RY>(rpb, rnxt.h, tid, treg);
-    if (more && rnxt.ok && cnxt.ok) stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, kn, vn, wave, lane);
+    if (more && rnxt.ok && cnxt.ok)
+      stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, si, kn, vn, wave, lane);
     res = TileOut{{0u, 0u, 0u, 0u}, false};
     if (rcur.ok && ccur.ok) res = compute_tile<T, KS>(rcur, ccur, kc, vc, tc, qcur, lane);
     if (!more) return;
@@ -573,7 +589,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // the block's results leave after the barrier, so that its wait covers
     // the next block's loads but not these stores
-    store_out<T, STREAM>(out, rcur.pofs, pcur, g, res);
+    store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
     rcur = rnxt;
     ccur = cnxt;
     pcur = pnxt;
@@ -586,7 +602,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     if (!more0) break;
     step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < b1);
   }
-  store_out<T, STREAM>(out, rcur.pofs, pcur, g, res);  // the last block
+  store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);  // the last block
 }
 
 // Compute units of the current device (queried once per device).
@@ -603,9 +619,16 @@ int device_cus() {
   return cache[dev];
 }
 
+// Host-side view of the strides of a launch: bytes, and whether q, k, v and
+// out are all dense [B, heads, H, W, D].
+struct Layout {
+  ByteStrides in, out;
+  bool planar;
+};
+
 template <typename T, int KS, int RY>
 hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb, void *out,
-                    const Shape &s, hipStream_t st) {
+                    const Shape &s, const Layout &lay, hipStream_t st) {
   using G = Geometry<KS, RY>;
   const int Lymax = class_len(s.H, 0, s.dil), Lxmax = class_len(s.W, 0, s.dil);
   const int nby = (Lymax + G::RY - 1) / G::RY, nbx = (Lxmax + G::RX - 1) / G::RX;
@@ -613,9 +636,12 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
   // one persistent workgroup per compute unit (its LDS holds two blocks)
   const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
-  auto kernel = s.dil == 1 ? fused_mfma_kernel<T, KS, RY, true> : fused_mfma_kernel<T, KS, RY, false>;
+  // Non-temporal Q/out only when each line belongs to one block: dense maps
+  // without dilation (channels-last maps interleave the heads' channels).
+  auto kernel = s.dil == 1 && lay.planar ? fused_mfma_kernel<T, KS, RY, true>
+                                         : fused_mfma_kernel<T, KS, RY, false>;
   kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
-      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s,
+      (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, lay.in, lay.out,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
       make_fastdiv((uint32_t)s.heads), (int)nblocks);
   return hipGetLastError();
@@ -626,28 +652,23 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
 // per block for the same count).
 template <typename T, int KS>
 hipError_t launch_small(const void *q, const void *k, const void *v, const void *rpb, void *out,
-                        const Shape &s, hipStream_t st) {
+                        const Shape &s, const Layout &lay, hipStream_t st) {
   const int L = class_len(s.H, 0, s.dil);
-  if ((L + 27) / 28 <= (L + 31) / 32) return launch_t<T, KS, 28>(q, k, v, rpb, out, s, st);
-  return launch_t<T, KS, 32>(q, k, v, rpb, out, s, st);
+  if ((L + 27) / 28 <= (L + 31) / 32) return launch_t<T, KS, 28>(q, k, v, rpb, out, s, lay, st);
+  return launch_t<T, KS, 32>(q, k, v, rpb, out, s, lay, st);
 }
 
 template <typename T>
 hipError_t launch_dtype(const void *q, const void *k, const void *v, const void *rpb, void *out,
-                        const Shape &s, hipStream_t st, bool *supported) {
-  // in-plane offsets are 32-bit and pixel products 24-bit
-  if ((int64_t)s.H * s.W >= kMaxPlanePixels) {
-    *supported = false;
-    return hipSuccess;
-  }
+                        const Shape &s, const Layout &lay, hipStream_t st, bool *supported) {
   switch (s.ks) {
-    case 1: return launch_small<T, 1>(q, k, v, rpb, out, s, st);
-    case 3: return launch_small<T, 3>(q, k, v, rpb, out, s, st);
-    case 5: return launch_small<T, 5>(q, k, v, rpb, out, s, st);
-    case 7: return launch_small<T, 7>(q, k, v, rpb, out, s, st);
-    case 9: return launch_t<T, 9, default_rows(9)>(q, k, v, rpb, out, s, st);
-    case 11: return launch_t<T, 11, default_rows(11)>(q, k, v, rpb, out, s, st);
-    case 13: return launch_t<T, 13, default_rows(13)>(q, k, v, rpb, out, s, st);
+    case 1: return launch_small<T, 1>(q, k, v, rpb, out, s, lay, st);
+    case 3: return launch_small<T, 3>(q, k, v, rpb, out, s, lay, st);
+    case 5: return launch_small<T, 5>(q, k, v, rpb, out, s, lay, st);
+    case 7: return launch_small<T, 7>(q, k, v, rpb, out, s, lay, st);
+    case 9: return launch_t<T, 9, default_rows(9)>(q, k, v, rpb, out, s, lay, st);
+    case 11: return launch_t<T, 11, default_rows(11)>(q, k, v, rpb, out, s, lay, st);
+    case 13: return launch_t<T, 13, default_rows(13)>(q, k, v, rpb, out, s, lay, st);
   }
   *supported = false;
   return hipSuccess;
@@ -656,16 +677,27 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 }  // namespace
 
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
-                             void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st,
+                             void *out, const Shape &s, const Strides &in,
+                             const Strides &out_st, na2d_dtype_t dt, hipStream_t st,
                              bool *supported) {
   *supported = true;
-  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, dt, st, supported);
+  if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) {
+    *supported = false;
+    return hipSuccess;
+  }
+  Layout lay;
+  lay.planar = is_planar(in, s) && is_planar(out_st, s);
+  const int64_t elem = 2;
+  if (!mfma::byte_strides(in, s, elem, &lay.in) || !mfma::byte_strides(out_st, s, elem, &lay.out)) {
+    *supported = false;
+    return hipSuccess;
+  }
+  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, dt, st, supported);
   if (*supported) return e;
   *supported = true;
-  if (dt == NA2D_DTYPE_BF16) return launch_dtype<__bf16>(q, k, v, rpb, out, s, st, supported);
-  if (dt == NA2D_DTYPE_F16) return launch_dtype<_Float16>(q, k, v, rpb, out, s, st, supported);
-  *supported = false;
-  return hipSuccess;
+  if (dt == NA2D_DTYPE_BF16)
+    return launch_dtype<__bf16>(q, k, v, rpb, out, s, lay, st, supported);
+  return launch_dtype<_Float16>(q, k, v, rpb, out, s, lay, st, supported);
 }
 
 }  // namespace na2d

@@ -28,6 +28,24 @@ template <> struct Mma<_Float16> {
 
 constexpr float kSqrtD = 5.656854249492380f;  // sqrt(32)
 
+// Byte strides of a q/k/v (or out) view [B, heads, H, W, D]: batch and head
+// as 64-bit offsets, pixel row and column as 32-bit offsets within one
+// (batch, head) plane.
+struct ByteStrides {
+  int64_t b, h;
+  uint32_t y, x;
+};
+
+// Byte strides, or false when a (batch, head) plane's span does not fit the
+// kernels' 32-bit in-plane offsets (or a stride is negative).
+inline bool byte_strides(const Strides &t, const Shape &s, int64_t elem, ByteStrides *out) {
+  if (t.b < 0 || t.h < 0 || t.y < 0 || t.x < 0) return false;
+  const int64_t span = ((int64_t)(s.H - 1) * t.y + (int64_t)(s.W - 1) * t.x + kHeadDim) * elem;
+  if (span > (int64_t(1) << 31)) return false;
+  *out = ByteStrides{t.b * elem, t.h * elem, (uint32_t)(t.y * elem), (uint32_t)(t.x * elem)};
+  return true;
+}
+
 // Maximum over the 4 lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float group_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -60,17 +60,19 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
                                                         const T *__restrict__ k,
                                                         const T *__restrict__ v,
                                                         const T *__restrict__ rpb,
-                                                        T *__restrict__ out, Shape s) {
+                                                        T *__restrict__ out, Shape s,
+                                                        Strides si, Strides so) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= s.n_query) return;
   const QueryPos p = decode_query(t, s);
-  const int64_t hw = (int64_t)s.H * s.W;
-  const T *kp = k + p.plane * hw * D;
-  const T *vp = v + p.plane * hw * D;
+  const int64_t bb = p.plane / s.heads;
+  const int64_t ibase = bb * si.b + p.h * si.h;
+  const T *kp = k + ibase;
+  const T *vp = v + ibase;
   const float scale = 1.0f / sqrtf((float)D);
 
   float qr[D];
-  load_row(q + t * D, qr);
+  load_row(q + ibase + p.i * si.y + p.j * si.x, qr);
   float acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
     const int row = p.ry + (p.sy + a) * s.dil;
     for (int c = 0; c < s.ks; ++c) {
       const int col = p.rx + (p.sx + c) * s.dil;
-      const int64_t off = ((int64_t)row * s.W + col) * D;
+      const int64_t off = row * si.y + col * si.x;
       float kr[D];
       load_row(kp + off, kr);
       float dot = 0.f;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
     }
   }
   const float inv = 1.0f / l;
-  T *o = out + t * D;
+  T *o = out + bb * so.b + p.h * so.h + p.i * so.y + p.j * so.x;
 #pragma unroll
   for (int e = 0; e < D; ++e) o[e] = Elem<T>::from_f(acc[e] * inv);
 }
@@ -202,24 +204,25 @@ bool grid_for(int64_t work, int per_block, dim3 *grid) {
 }  // namespace
 
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
-                            void *out, const Shape &s, na2d_dtype_t dt, hipStream_t st) {
+                            void *out, const Shape &s, const Strides &in, const Strides &out_st,
+                            na2d_dtype_t dt, hipStream_t st) {
   dim3 grid;
   if (!grid_for(s.n_query, 256, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
     case NA2D_DTYPE_F32:
       fused_fma_kernel<float><<<grid, 256, 0, st>>>((const float *)q, (const float *)k,
                                                    (const float *)v, (const float *)rpb,
-                                                   (float *)out, s);
+                                                   (float *)out, s, in, out_st);
       break;
     case NA2D_DTYPE_BF16:
       fused_fma_kernel<__bf16><<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
                                                     (const __bf16 *)v, (const __bf16 *)rpb,
-                                                    (__bf16 *)out, s);
+                                                    (__bf16 *)out, s, in, out_st);
       break;
     case NA2D_DTYPE_F16:
       fused_fma_kernel<_Float16><<<grid, 256, 0, st>>>(
           (const _Float16 *)q, (const _Float16 *)k, (const _Float16 *)v, (const _Float16 *)rpb,
-          (_Float16 *)out, s);
+          (_Float16 *)out, s, in, out_st);
       break;
   }
   return hipGetLastError();

@@ -8,7 +8,10 @@ library has not been built, the first call raises.
 
 Layouts: q, k, v, out are contiguous [B, heads, H, W, D] on the GPU in one of
 float32 / bfloat16 / float16; rpb is [heads, 2k-1, 2k-1] in the same dtype or
-None (zero bias); attn is float32 [B, heads, H, W, k*k].
+None (zero bias); attn is float32 [B, heads, H, W, k*k].  The strided forward
+takes q, k, v, out as [B, heads, H, W, D] views with any strides whose last
+one is 1 (e.g. channels-last hidden states viewed per head, see
+``heads_view``).
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ def lib() -> ctypes.CDLL:
         L.na2d_forward.argtypes = [vp] * 5 + [i] * 8 + [vp]
         L.na2d_forward_algo.restype = i
         L.na2d_forward_algo.argtypes = [vp] * 5 + [i] * 9 + [vp]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.na2d_forward_strided.restype = i
+        L.na2d_forward_strided.argtypes = [vp] * 5 + [i] * 7 + [i64p, i64p, i, vp]
         L.na2d_qkrpb.restype = i
         L.na2d_qkrpb.argtypes = [vp] * 4 + [i] * 8 + [vp]
         L.na2d_softmax.restype = i
@@ -123,6 +129,57 @@ def na2d_forward_algo(q, k, v, rpb, out, kernel_size: int, dilation: int, algo: 
                                  B, heads, H, W, D, int(kernel_size), int(dilation),
                                  _DTYPE_CODES[q.dtype], ALGOS[algo], _stream(q))
     _check(st, "na2d_forward_algo")
+    return out
+
+
+def heads_view(x: torch.Tensor, heads: int) -> torch.Tensor:
+    """Channels-last hidden states [B, H, W, heads*D] (or a channel slice of a
+    fused QKV buffer) as the [B, heads, H, W, D] view the strided forward
+    takes; no copy."""
+    B, H, W, C = x.shape
+    return x.unflatten(3, (heads, C // heads)).permute(0, 3, 1, 2, 4)
+
+
+def _strided(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if t.stride(-1) != 1:
+        raise ValueError("%s must have contiguous channels (last stride 1)" % name)
+    return (ctypes.c_int64 * 4)(*[int(x) for x in t.stride()[:4]])
+
+
+def na2d_forward_strided(q, k, v, rpb, out, kernel_size: int, dilation: int):
+    """Fused forward into ``out`` on strided [B, heads, H, W, D] views: q, k
+    and v must share their strides; out has its own (checked by the library:
+    no aliasing, no overlap with the inputs)."""
+    B, heads, H, W, D = _qkv_shape(q)
+    si = _strided(q, "q", q.dtype, q.shape)
+    for t, n in ((k, "k"), (v, "v")):
+        if tuple(_strided(t, n, q.dtype, q.shape)) != tuple(si):
+            raise ValueError("q, k and v must share their strides")
+    so = _strided(out, "out", q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    st = lib().na2d_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out),
+                                    B, heads, H, W, D, int(kernel_size), int(dilation),
+                                    si, so, _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_forward_strided")
+    return out
+
+
+def forward_channels_last(q, k, v, rpb, heads: int, kernel_size: int, dilation: int):
+    """Allocating forward on channels-last hidden states: q, k, v are
+    [B, H, W, heads*D] tensors (or channel slices of one [B, H, W, 3*heads*D]
+    buffer); returns out as a new contiguous [B, H, W, heads*D] tensor."""
+    B, H, W, C = q.shape
+    out = torch.empty((B, H, W, C), dtype=q.dtype, device=q.device)
+    na2d_forward_strided(heads_view(q, heads), heads_view(k, heads), heads_view(v, heads), rpb,
+                         heads_view(out, heads), kernel_size, dilation)
     return out
 
 
