@@ -51,7 +51,7 @@ template <int KS> struct DenseGeometry {
   static constexpr int SIDE = 2 * KS - 1;
   static_assert(SG * NT == WAVES * TPW, "blocks hold whole classes");
   static_assert(DPW * WAVES == 2 * DPT, "DMA instructions spread evenly");
-  static_assert(2 * 2 * SG * CB + NCT * 4 <= 160 * 1024, "LDS");
+  static_assert(2 * 2 * SG * CB + 2 * NCT * 4 <= 160 * 1024, "LDS");
 };
 
 // Byte offset of pixel (0, 0) of class jh (numbered (b, ry, rx), rx fastest)
@@ -64,16 +64,22 @@ __device__ __forceinline__ int64_t class_base(int h, int jh, const Shape &s, int
 }
 
 // Block id -> (head, first class within the head, classes in the block).
+// Blocks of one head are consecutive (f divides by the blocks per head),
+// or, when the heads of a pixel share its lines (channels-last maps), the
+// heads alternate (f divides by the head count), so that the heads' blocks
+// of the same classes run back to back and share those lines in L2.
 struct DenseBlock {
   int h, j0, n;
 };
 
 template <int KS>
-__device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &fbph, int per_head) {
+__device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &f, int per_head,
+                                                  bool hfast) {
   using G = DenseGeometry<KS>;
   DenseBlock b;
-  b.h = (int)fast_div((uint32_t)id, fbph);
-  b.j0 = (id - b.h * (int)fbph.div) * G::SG;
+  const int t = (int)fast_div((uint32_t)id, f), r = id - t * (int)f.div;
+  b.h = hfast ? r : t;
+  b.j0 = (hfast ? t : r) * G::SG;
   b.n = min(G::SG, per_head - b.j0);
   return b;
 }
@@ -82,7 +88,7 @@ template <typename T, int KS>
 __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
-    FastDiv fbph, int per_head, int nblocks, int log2d) {
+    FastDiv fblk, bool hfast, int per_head, int nblocks, int log2d) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, TPW = G::TPW, SG = G::SG;
@@ -90,7 +96,9 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   constexpr int WAVES = G::WAVES, THREADS = G::THREADS;
   __shared__ __attribute__((aligned(16))) char kbuf0[SG * CB], vbuf0[SG * CB];
   __shared__ __attribute__((aligned(16))) char kbuf1[SG * CB], vbuf1[SG * CB];
-  __shared__ __attribute__((aligned(16))) float ctab[G::NCT];  // [tile][key block][lane][4]
+  // two accumulator tables, [slot][tile][key block][lane][4]; head h uses slot
+  // h & 1, so alternating heads (channels-last order) rebuild nothing
+  __shared__ __attribute__((aligned(16))) float ctab[2 * G::NCT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
@@ -145,11 +153,12 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
                                : static_cast<T>(0.0f);
     }
   };
-  auto store_ctab = [&]() {
+  auto store_ctab = [&](int slot) {
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
       const int e = tid + m * THREADS;
-      if (e < G::NCT) ctab[e] = ctab_src(e) < 0 ? -INFINITY : Elem<T>::to_f(craw[m]) * kSqrtD;
+      if (e < G::NCT)
+        ctab[slot * G::NCT + e] = ctab_src(e) < 0 ? -INFINITY : Elem<T>::to_f(craw[m]) * kSqrtD;
     }
   };
 
@@ -189,12 +198,13 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     return x;
   };
   // one tile: returns the lane's 8 output channels, rounded
-  auto tile = [&](const char *kb, const char *vb, int u, u32x4 qraw) -> u32x4 {
+  auto tile = [&](const char *kb, const char *vb, int u, u32x4 qraw, int slot) -> u32x4 {
     const int t = wave * TPW + u, c = t / NT, tt = t % NT;
     const vec qv = __builtin_bit_cast(vec, qraw);
     // key slot kbk*16 + ql, logical chunk g (the swizzle does not depend on kbk)
     const char *kp = kb + opaque(c * CB + ql * 64 + 16 * (g ^ ((ql >> 1) & 3)));
-    const f32x4 *ct = (const f32x4 *)((const char *)ctab + opaque(((tt * NKB) * 64 + lane) * 16));
+    const f32x4 *ct = (const f32x4 *)((const char *)ctab +
+                                      opaque(slot * G::NCT * 4 + ((tt * NKB) * 64 + lane) * 16));
     f32x4 sc[NKB];
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) {
@@ -268,14 +278,15 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   };
 
   // ---- prologue ----
-  DenseBlock cur = dense_block<KS>(b0, fbph, per_head);
+  DenseBlock cur = dense_block<KS>(b0, fblk, per_head, hfast);
   u32x4 qcur[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) qcur[u] = load_q(cur, u);
   load_ctab(cur.h);
   stage(cur, kbuf0, vbuf0);
-  store_ctab();
-  int ctab_h = cur.h;
+  store_ctab(cur.h & 1);
+  int slot_h[2] = {-1, -1};  // head whose table each slot holds
+  slot_h[cur.h & 1] = cur.h;
   __syncthreads();
 
   u32x4 res[TPW];
@@ -285,23 +296,27 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   // buffer being read.
   auto step = [&](int bi, const char *kc, const char *vc, char *kn, char *vn) {
     const bool more = bi + 1 < b1;
-    const DenseBlock nxt = dense_block<KS>(more ? bi + 1 : bi, fbph, per_head);
+    const DenseBlock nxt = dense_block<KS>(more ? bi + 1 : bi, fblk, per_head, hfast);
     u32x4 qnxt[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) qnxt[u] = load_q(nxt, u);
-    const bool newtab = more && nxt.h != ctab_h;
+    const int nslot = nxt.h & 1;
+    const bool newtab = more && slot_h[nslot] != nxt.h;
     if (newtab) load_ctab(nxt.h);
     if (more) stage(nxt, kn, vn);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       rok[u] = tile_ok(cur, u);
-      res[u] = (wave * TPW + u) / NT < cur.n ? tile(kc, vc, u, qcur[u]) : u32x4{0u, 0u, 0u, 0u};
+      res[u] = (wave * TPW + u) / NT < cur.n ? tile(kc, vc, u, qcur[u], cur.h & 1)
+                                             : u32x4{0u, 0u, 0u, 0u};
     }
     if (!more) return;
     if (newtab) {
-      __syncthreads();  // every wave is done with the old table
-      store_ctab();
-      ctab_h = nxt.h;
+      // the slot the current block reads: wait until every wave is done with
+      // it (the other slot was last read before the previous barrier)
+      if (nslot == (cur.h & 1)) __syncthreads();
+      store_ctab(nslot);
+      slot_h[nslot] = nxt.h;
     }
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // results leave after the barrier, whose wait then covers only the loads
@@ -345,9 +360,11 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   int log2d = 0;
   while ((1 << log2d) < s.dil) ++log2d;
   const int64_t grid = nblocks < dense_cus() ? nblocks : dense_cus();
+  // heads interleaved within pixels: alternate heads between blocks
+  const bool hfast = s.heads > 1 && (uint64_t)si.h < si.x;
   dense_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, si, so,
-      make_fastdiv((uint32_t)bph), (int)per_head, (int)nblocks, log2d);
+      make_fastdiv((uint32_t)(hfast ? s.heads : bph)), hfast, (int)per_head, (int)nblocks, log2d);
   return hipGetLastError();
 }
 
