@@ -184,3 +184,41 @@ def backward(q, k, v, rpb, dout, kernel_size: int, dilation: int, *,
     if rc != 0:
         raise ValueError("oracle rejected the problem (status %d)" % rc)
     return {"dq": dq, "dk": dk, "dv": dv, "drpb": drpb}
+
+
+def forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size: int, dilation: int, *,
+                   threads: int | None = None):
+    """Oracle of the padded forward pass (the DiNAT layer's maybe_pad: a map
+    smaller than kernel_size * dilation is padded, attended, and cropped
+    back; DiNAT walk-through blog, layer organisation).
+
+    Readings: the padding goes below and to the right, up to
+    H' = max(H, k*d) rows and W' = max(W, k*d) columns; a padded pixel holds
+    key pad_k[h] and value pad_v[h] ([heads, D], None = zeros: the projection
+    of a zero feature); windows are taken on the padded map; only the
+    original H x W queries are returned.
+
+    Written as the definition: build the padded tensors, run ``forward`` on
+    the original queries' positions, reshape.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 5 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, heads, H, W, D] shape")
+    B, heads, H, W, D = q.shape
+    ks, dil = int(kernel_size), int(dilation)
+    Hp, Wp = max(H, ks * dil), max(W, ks * dil)
+    pk = np.zeros((heads, D)) if pad_k is None else _f64(pad_k)
+    pv = np.zeros((heads, D)) if pad_v is None else _f64(pad_v)
+    if pk.shape != (heads, D) or pv.shape != (heads, D):
+        raise ValueError("pad_k and pad_v must be [heads, D]")
+    qp = np.zeros((B, heads, Hp, Wp, D))
+    kp = np.broadcast_to(pk[None, :, None, None, :], (B, heads, Hp, Wp, D)).copy()
+    vp = np.broadcast_to(pv[None, :, None, None, :], (B, heads, Hp, Wp, D)).copy()
+    qp[:, :, :H, :W] = q
+    kp[:, :, :H, :W] = k
+    vp[:, :, :H, :W] = v
+    bb, hh, ii, jj = np.meshgrid(np.arange(B), np.arange(heads), np.arange(H), np.arange(W),
+                                 indexing="ij")
+    idx = (((bb * heads + hh) * Hp + ii) * Wp + jj).reshape(-1)
+    out = forward(qp, kp, vp, rpb, ks, dil, idx=idx, threads=threads)["out"]
+    return out.reshape(B, heads, H, W, D)
