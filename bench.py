@@ -54,6 +54,7 @@ WORKLOADS = {
     "det_k13_d1_bf16": I.DETECTION[4], "det_k13_d1_f16": I.DETECTION[5],
     "det_k13_d8_bf16": I.DETECTION[6], "det_k13_d8_f16": I.DETECTION[7],
     "tiny_f32": I.TINY,
+    "dinat_s1_d8_pad48": I.DINAT_S1_D8_PAD48,
 }
 BACKWARD_SOURCES = ["vision_transformer_local_amd/csrc/na2d_backward.hip",
                     "vision_transformer_local_amd/csrc/na2d_internal.h"]
@@ -106,13 +107,20 @@ def measured_traffic(workload: str, path: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500, backward=False):
+def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500, backward=False,
+                 pads=None):
     """The float64 oracle on the host cores: whole-workload passes repeated
-    until about budget_s seconds of CPU work, median pass time."""
+    until about budget_s seconds of CPU work, median pass time.  pads: the
+    (pad_k, pad_v) of a padded forward."""
     import oracle
     threads = oracle.default_threads()
     arrs = [t.to(torch.float64).numpy() for t in cpu_inputs]
     fn = oracle.backward if backward else oracle.forward
+    if pads is not None:
+        pk, pv = (t.to(torch.float64).numpy() for t in pads)
+
+        def fn(q, k, v, rpb, ks, d, threads):
+            return oracle.forward_padded(q, k, v, rpb, pk, pv, ks, d, threads=threads)
     times = []
     start = time.perf_counter()
     while len(times) < min_runs or (time.perf_counter() - start < budget_s
@@ -154,6 +162,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="nat_tiny_s1", choices=sorted(WORKLOADS))
     ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
+    ap.add_argument("--padded", action="store_true",
+                    help="forward through na2d_forward_padded (maps smaller than k*d are "
+                         "padded with per-head pad vectors, attended and cropped)")
     ap.add_argument("--layout", default="dense", choices=["dense", "channels_last"],
                     help="forward I/O layout: dense [B, heads, H, W, D], or channels-last "
                          "[B, H, W, heads*D] through na2d_forward_strided")
@@ -203,8 +214,16 @@ def main(argv=None):
     B, heads, H, W, D = p.shape
     ks, dil = p.kernel_size, p.dilation
     cl = args.layout == "channels_last"
-    if cl and args.path != "fused":
-        print("--layout channels_last takes the fused path only", file=sys.stderr)
+    if (cl or args.padded) and args.path != "fused":
+        print("--layout channels_last and --padded take the fused path only", file=sys.stderr)
+        return 2
+    if cl and args.padded:
+        print("--padded takes the dense layout", file=sys.stderr)
+        return 2
+    span = p.kernel_size * p.dilation
+    if not args.padded and (p.H < span or p.W < span):
+        print("workload %s needs --padded (map below kernel*dilation)" % args.workload,
+              file=sys.stderr)
         return 2
     tbytes = q0.numel() * q0.element_size()
     attn_bytes = p.n_query_heads * p.kernel_size ** 2 * 4 if args.path == "unfused" else 0
@@ -230,6 +249,8 @@ def main(argv=None):
                             device=dev) if args.path == "unfused" else None)
         reps.append((q, k, v, out, attn))
 
+    gen = torch.Generator("cpu").manual_seed(500)
+    pad_k, pad_v = (torch.randn(heads, D, generator=gen).to(q0.dtype).to(dev) for _ in range(2))
     si = (ctypes.c_int64 * 4)(*reps[0][0].stride()[:4])
     so = (ctypes.c_int64 * 4)(*reps[0][3].stride()[:4])
 
@@ -242,6 +263,10 @@ def main(argv=None):
             r = r or L.na2d_softmax(attn.data_ptr(), attn.data_ptr(), B, heads, H, W, ks, st)
             r = r or L.na2d_av(attn.data_ptr(), v.data_ptr(), out.data_ptr(),
                                B, heads, H, W, D, ks, dil, dt_code, st)
+        elif args.padded:
+            r = L.na2d_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                      pad_k.data_ptr(), pad_v.data_ptr(), out.data_ptr(), B,
+                                      heads, H, W, D, ks, dil, dt_code, st)
         elif cl:
             r = L.na2d_forward_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
                                        out.data_ptr(), B, heads, H, W, D, ks, dil, si, so,
@@ -261,7 +286,11 @@ def main(argv=None):
     import oracle
     idx = np.random.default_rng(0).choice(p.n_query_heads, size=min(4096, p.n_query_heads),
                                           replace=False)
-    ref = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx)["out"]
+    if args.padded:
+        ref = oracle.forward_padded(q0, k0, v0, rpb0, pad_k.cpu(), pad_v.cpu(), ks,
+                                    dil).reshape(-1, D)[idx]
+    else:
+        ref = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx)["out"]
     got = reps[0][3].contiguous().reshape(-1, D)[torch.from_numpy(idx).to(dev)]
     got = got.double().cpu().numpy()
     max_err = float(np.abs(got - ref).max())
@@ -271,7 +300,8 @@ def main(argv=None):
     if args.path == "unfused":
         abytes += 4 * p.n_query_heads * p.kernel_size ** 2 * 4  # fp32 attn w, r, w, r
     achieved = abytes / (kernel_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload, args.path if not cl else "strided")
+    traffic = measured_traffic(args.workload,
+                               "strided" if cl else ("padded" if args.padded else args.path))
 
     rec = {
         "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
@@ -289,7 +319,7 @@ def main(argv=None):
         "config": {"workload": "%s: %s" % (args.workload, p.describe()),
                    "B": B, "heads": heads, "H": H, "W": W, "D": D,
                    "kernel_size": ks, "dilation": dil, "path": args.path,
-                   "layout": args.layout,
+                   "layout": args.layout, "padded": args.padded,
                    "timing": args.mode, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -304,7 +334,8 @@ def main(argv=None):
         rec["copy_reference"] = {"copy_gbs": copy_gbs, "achieved_over_copy": achieved / copy_gbs,
                                  "what": "torch device copy of 1 GiB, read+write bytes"}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(p, cpu)
+        rec["cpu_baseline"] = cpu_baseline(
+            p, cpu, pads=(pad_k.cpu(), pad_v.cpu()) if args.padded else None)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -121,6 +121,29 @@ na2d_status_t na2d_forward_strided(const void *q, const void *k, const void *v,
                                    na2d_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Forward pass on a map that may be smaller than the dilated window, as the
+ * DiNAT layer runs it (maybe_pad: a feature map smaller than
+ * kernel_size * dilation is padded, attended and cropped back; DiNAT
+ * walk-through blog, layer organisation).  The operator runs on an
+ * Hp x Wp map, Hp = max(H, k*d) and Wp = max(W, k*d), padded below and to
+ * the right: a padded pixel has key pad_k[h] and value pad_v[h], the
+ * projection of a zero feature (the key/value projection biases; NULL =
+ * zeros, i.e. no bias).  Windows are clamped inside the padded map.
+ *
+ *   q, k, v, out  dense [B, heads, H, W, D] at the real size; out receives
+ *                 the H x W queries (the crop)
+ *   pad_k, pad_v  [heads, D] in dtype, 16-byte aligned, or NULL
+ *
+ * H, W >= 1 (no k*d minimum); maps that need no padding run exactly
+ * na2d_forward (the pad vectors are unused).  Other rules as na2d_forward;
+ * out must not overlap q, k, v, rpb or the pad vectors.
+ */
+na2d_status_t na2d_forward_padded(const void *q, const void *k, const void *v, const void *rpb,
+                                  const void *pad_k, const void *pad_v, void *out, int B,
+                                  int heads, int H, int W, int D, int kernel_size,
+                                  int dilation, na2d_dtype_t dtype, hipStream_t stream);
+
+/*
  * Unfused step 1 (the blog's natten2dqkrpb): attn[b,h,i,j,n] =
  * q[b,h,i,j].k[neighbour n] / sqrt(D) + rpb[h][offset of n], in fp32.
  */

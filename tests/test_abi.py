@@ -301,3 +301,40 @@ def test_strided_forward_rejects_out_overlapping_an_input():
     far = [ctypes.c_void_p((1 << 41) * (i + 1)) for i in range(3)]
     inside = ctypes.c_void_p(far[2].value + 4096)
     assert L.na2d_forward_strided(*far, NULL, inside, *args, st, st, BF16, S) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# na2d_forward_padded: maps below k*d are valid; the rest as na2d_forward.
+PADDED_CASES = [
+    ((1, 1, 0, 5, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 5, 0, 32, 7, 1, BF16), INVALID),
+    ((0, 1, 5, 5, 32, 7, 1, BF16), INVALID),
+    ((1, 1, 5, 5, 32, 6, 1, BF16), INVALID),     # even kernel
+    ((1, 1, 5, 5, 32, 7, 0, BF16), INVALID),
+    ((1, 1, 5, 5, 32, 7, 1, 5), INVALID),
+    ((1, 1, 5, 5, 64, 7, 1, BF16), UNSUPPORTED),  # D != 32
+    ((1, 1, 5, 5, 32, 15, 1, BF16), UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("args,expect", PADDED_CASES)
+def test_padded_forward_validation(args, expect):
+    L = na2d.lib()
+    assert L.na2d_forward_padded(*P[:7], *args, S) == expect
+
+
+def test_padded_forward_pointer_rules():
+    L = na2d.lib()
+    args = (1, 2, 5, 5, 32, 7, 2, BF16)
+    for slot in (0, 1, 2, 6):
+        p = list(P[:7])
+        p[slot] = NULL
+        assert L.na2d_forward_padded(*p, *args, S) == INVALID
+    for slot in range(7):
+        p = list(P[:7])
+        p[slot] = ctypes.c_void_p(p[slot].value + 8)
+        assert L.na2d_forward_padded(*p, *args, S) == INVALID
+    # out overlapping a pad vector
+    p = list(P[:7])
+    p[6] = p[4]
+    assert L.na2d_forward_padded(*p, *args, S) == INVALID

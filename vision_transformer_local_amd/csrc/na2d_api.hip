@@ -80,22 +80,24 @@ bool injective(const na2d::Strides &t, const na2d::Shape &s) {
   return true;
 }
 
-// The forward pass for checked shapes, pointers and strides.
+// The forward pass for checked shapes, pointers, strides and padding.
 na2d_status_t forward_checked(const void *q, const void *k, const void *v, const void *rpb,
                               void *out, const na2d::Shape &s, const na2d::Strides &in,
-                              const na2d::Strides &os, na2d_dtype_t dtype, na2d_algo_t algo,
-                              hipStream_t stream) {
+                              const na2d::Strides &os, const na2d::Pad &pad,
+                              na2d_dtype_t dtype, na2d_algo_t algo, hipStream_t stream) {
   const bool automatic = algo == NA2D_ALGO_AUTO;
   if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
   if (algo == NA2D_ALGO_MFMA) {
     if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
     bool supported = true;
-    hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, dtype, stream, &supported);
+    hipError_t e =
+        na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, &supported);
     if (supported) return from_hip(e);
     if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
-    // planes too large for 32-bit in-plane offsets: the FMA kernel handles them
+    // planes too large for 32-bit in-plane offsets, and padded maps that are
+    // not k*d square: the FMA kernel handles them
   }
-  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, dtype, stream));
+  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, pad, dtype, stream));
 }
 
 }  // namespace
@@ -126,7 +128,7 @@ na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, con
       return NA2D_ERROR_INVALID_VALUE;
   }
   const na2d::Strides pl = na2d::planar_strides(s);
-  return forward_checked(q, k, v, rpb, out, s, pl, pl, dtype, algo, stream);
+  return forward_checked(q, k, v, rpb, out, s, pl, pl, na2d::no_pad(s), dtype, algo, stream);
 }
 
 na2d_status_t na2d_forward_strided(const void *q, const void *k, const void *v,
@@ -162,7 +164,43 @@ na2d_status_t na2d_forward_strided(const void *q, const void *k, const void *v,
     const int64_t side = 2 * kernel_size - 1;
     if (overlaps(out, ob, rpb, heads * side * side * eb)) return NA2D_ERROR_INVALID_VALUE;
   }
-  return forward_checked(q, k, v, rpb, out, s, in, os, dtype, NA2D_ALGO_AUTO, stream);
+  return forward_checked(q, k, v, rpb, out, s, in, os, na2d::no_pad(s), dtype, NA2D_ALGO_AUTO,
+                         stream);
+}
+
+na2d_status_t na2d_forward_padded(const void *q, const void *k, const void *v, const void *rpb,
+                                  const void *pad_k, const void *pad_v, void *out, int B,
+                                  int heads, int H, int W, int D, int kernel_size,
+                                  int dilation, na2d_dtype_t dtype, hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  if (H < 1 || W < 1 || kernel_size < 1 || dilation < 1) return NA2D_ERROR_INVALID_VALUE;
+  // shape rules on the padded map, then the real extent
+  const int64_t span = (int64_t)kernel_size * dilation;
+  const int64_t Hp = H > span ? H : span, Wp = W > span ? W : span;
+  if (Hp > INT_MAX || Wp > INT_MAX) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, (int)Hp, (int)Wp, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  s.H = H;
+  s.W = W;
+  s.n_query = s.n_query / ((int64_t)Hp * Wp) * ((int64_t)H * W);
+  if (!q || !k || !v || !out) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (rpb && !aligned16(rpb)) || (pad_k && !aligned16(pad_k)) || (pad_v && !aligned16(pad_v)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t tbytes = s.n_query * D * eb, pbytes = (int64_t)heads * D * eb;
+  if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
+      overlaps(out, tbytes, v, tbytes) || overlaps(out, tbytes, pad_k, pbytes) ||
+      overlaps(out, tbytes, pad_v, pbytes))
+    return NA2D_ERROR_INVALID_VALUE;
+  if (rpb) {
+    const int64_t side = 2 * kernel_size - 1;
+    if (overlaps(out, tbytes, rpb, heads * side * side * eb)) return NA2D_ERROR_INVALID_VALUE;
+  }
+  const na2d::Strides pl = na2d::planar_strides(s);
+  const na2d::Pad pad{pad_k, pad_v, (int)Hp, (int)Wp};
+  return forward_checked(q, k, v, rpb, out, s, pl, pl, pad, dtype, NA2D_ALGO_AUTO, stream);
 }
 
 na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const void *rpb,

@@ -63,6 +63,14 @@ __device__ __forceinline__ int64_t class_base(int h, int jh, const Shape &s, int
   return b * st.b + h * st.h + (int64_t)(ry * st.y + rx * st.x);
 }
 
+// Byte offset of the (batch, head) plane of class jh of head h.
+__device__ __forceinline__ int64_t plane_base(int h, int jh, int log2d, const ByteStrides &st) {
+  return (int64_t)(jh >> (2 * log2d)) * st.b + h * st.h;
+}
+
+// Key and value of padded pixels when the caller gives no pad vectors.
+__device__ __attribute__((aligned(64))) const char kZeroPixel[64] = {};
+
 // Block id -> (head, first class within the head, classes in the block).
 // Blocks of one head are consecutive (f divides by the blocks per head),
 // or, when the heads of a pixel share its lines (channels-last maps), the
@@ -84,11 +92,15 @@ __device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &f, int 
   return b;
 }
 
-template <typename T, int KS>
+// PAD: the map is padded to k*d x k*d (maybe_pad); pixels at row >= s.H or
+// column >= s.W are staged from the head's pad vectors and their queries are
+// neither read nor written.
+template <typename T, int KS, bool PAD>
 __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
-    FastDiv fblk, bool hfast, int per_head, int nblocks, int log2d) {
+    FastDiv fblk, bool hfast, int per_head, int nblocks, int log2d,
+    const T *__restrict__ pad_k, const T *__restrict__ pad_v) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, TPW = G::TPW, SG = G::SG;
@@ -114,6 +126,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   // of one class of one tensor; lane l lands at slot kg*16 + l/4, 16-byte
   // position l&3, which holds logical chunk (l&3) ^ swz(slot).
   unsigned doff[DPW];
+  int drow[DPW], dcol[DPW], dlch[DPW];  // padded maps: the key's pixel offsets in its class
 #pragma unroll
   for (int m = 0; m < DPW; ++m) {
     const int i = wave + WAVES * m, it = i % DPT;
@@ -121,17 +134,28 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const int slot = kg * 16 + (lane >> 2), key = min(slot, N - 1);
     const int lch = (lane & 3) ^ ((slot >> 1) & 3);
     doff[m] = (unsigned)(key / KS) * rowb + (unsigned)(key % KS) * colb + lch * 16u;
+    drow[m] = (key / KS) * d;
+    dcol[m] = (key % KS) * d;
+    dlch[m] = lch * 16;
   }
   // this wave's tiles: tile t = wave*TPW + u of the block is tile t % NT of
   // class t / NT; lane query slot tt*16 + ql (clamped to the last query)
   unsigned qoff[TPW], ooff[TPW];  // in q and in out
+  int qrow[TPW], qcol[TPW];        // padded maps: the query's pixel offsets in its class
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tt = (wave * TPW + u) % NT;
     const int nq = min(tt * 16 + ql, N - 1);
     qoff[u] = (unsigned)(nq / KS) * rowb + (unsigned)(nq % KS) * colb;
     ooff[u] = (unsigned)(nq / KS) * ((unsigned)d * so.y) + (unsigned)(nq % KS) * ((unsigned)d * so.x);
+    qrow[u] = (nq / KS) * d;
+    qcol[u] = (nq % KS) * d;
   }
+  // whether pixel (row, col) of class jh lies inside the unpadded map
+  auto real = [&](int jh, int row, int col) -> bool {
+    const int rx = jh & (d - 1), ry = (jh >> log2d) & (d - 1);
+    return ry + row < s.H && rx + col < s.W;
+  };
 
   // accumulator table for head h: entry (tt, kb, lane, i) = bias * sqrt(D)
   // of key slot kb*16 + 4g + i against query slot tt*16 + ql, -inf on
@@ -169,10 +193,17 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
       const int i = wave + WAVES * m;
       const bool isv = i >= DPT;
       const int it = i % DPT, c = it / (NK / 16), kg = it % (NK / 16);
-      const int64_t base = class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, si);
-      const char *src = (const char *)(isv ? v : k) + base;
+      const int jh = bk.j0 + min(c, bk.n - 1);
+      const int64_t base = class_base(bk.h, jh, s, log2d, si);
+      const char *src = (const char *)(isv ? v : k) + base + doff[m];
+      if constexpr (PAD) {
+        if (!real(jh, drow[m], dcol[m])) {
+          const T *pv = isv ? pad_v : pad_k;
+          src = (pv != nullptr ? (const char *)(pv + bk.h * kHeadDim) : kZeroPixel) + dlch[m];
+        }
+      }
       char *dst = (isv ? vb : kb) + c * CB + kg * 1024;
-      __builtin_amdgcn_global_load_lds((const void *)(src + doff[m]), (lds_void *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
     }
   };
   // byte offset of the class of this wave's tile u in block bk (strides st)
@@ -181,6 +212,12 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     return class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, st);
   };
   auto load_q = [&](const DenseBlock &bk, int u) -> u32x4 {
+    if constexpr (PAD) {
+      // a padded query is never stored: read pixel (0, 0) of its plane instead
+      const int jh = bk.j0 + min((wave * TPW + u) / NT, bk.n - 1);
+      if (!real(jh, qrow[u], qcol[u]))
+        return *(const u32x4 *)((const char *)q + plane_base(bk.h, jh, log2d, si) + g * 16u);
+    }
     return *(const u32x4 *)((const char *)q + tile_base(bk, u, si) + qoff[u] + g * 16u);
   };
 
@@ -267,7 +304,9 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   // whether this lane's query of tile u exists in block bk
   auto tile_ok = [&](const DenseBlock &bk, int u) -> bool {
     const int t = wave * TPW + u, c = t / NT, tt = t % NT;
-    return c < bk.n && tt * 16 + ql < N;
+    bool ok = c < bk.n && tt * 16 + ql < N;
+    if constexpr (PAD) ok = ok && real(bk.j0 + min(c, bk.n - 1), qrow[u], qcol[u]);
+    return ok;
   };
   auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok) {
     if (ok) {
@@ -351,7 +390,7 @@ int dense_cus() {
 template <typename T, int KS>
 hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, const ByteStrides &si, const ByteStrides &so,
-                        hipStream_t st) {
+                        const Pad &pad, hipStream_t st) {
   using G = DenseGeometry<KS>;
   const int64_t per_head = (int64_t)s.B * s.dil * s.dil;  // classes of one head
   const int64_t bph = (per_head + G::SG - 1) / G::SG;      // blocks per head
@@ -362,9 +401,12 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   const int64_t grid = nblocks < dense_cus() ? nblocks : dense_cus();
   // heads interleaved within pixels: alternate heads between blocks
   const bool hfast = s.heads > 1 && (uint64_t)si.h < si.x;
-  dense_mfma_kernel<T, KS><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
+  const bool padded = pad.Hp > s.H || pad.Wp > s.W;
+  auto kernel = padded ? dense_mfma_kernel<T, KS, true> : dense_mfma_kernel<T, KS, false>;
+  kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, si, so,
-      make_fastdiv((uint32_t)(hfast ? s.heads : bph)), hfast, (int)per_head, (int)nblocks, log2d);
+      make_fastdiv((uint32_t)(hfast ? s.heads : bph)), hfast, (int)per_head, (int)nblocks, log2d,
+      (const T *)pad.k, (const T *)pad.v);
   return hipGetLastError();
 }
 
@@ -372,26 +414,27 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
 
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const ByteStrides &si,
-                             const ByteStrides &so, na2d_dtype_t dt, hipStream_t st,
-                             bool *supported) {
+                             const ByteStrides &so, const Pad &pad, na2d_dtype_t dt,
+                             hipStream_t st, bool *supported) {
   *supported = true;
   const bool pow2_dil = (s.dil & (s.dil - 1)) == 0;
-  if ((int64_t)s.ks * s.dil != s.H || (int64_t)s.ks * s.dil != s.W || !pow2_dil ||
+  // the (padded) map must be exactly k*d square: every class k x k
+  if ((int64_t)s.ks * s.dil != pad.Hp || (int64_t)s.ks * s.dil != pad.Wp || !pow2_dil ||
       (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32) {
     *supported = false;
     return hipSuccess;
   }
   if (dt == NA2D_DTYPE_BF16) {
     switch (s.ks) {
-      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, si, so, st);
-      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, si, so, st);
-      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, si, so, st);
+      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, si, so, pad, st);
+      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, si, so, pad, st);
+      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, si, so, pad, st);
     }
   }
   switch (s.ks) {
-    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, si, so, st);
-    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, si, so, st);
-    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, si, so, st);
+    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, si, so, pad, st);
+    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, si, so, pad, st);
+    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, si, so, pad, st);
   }
 }
 

@@ -106,16 +106,27 @@ inline bool is_planar(const Strides &t, const Shape &s) {
   return t.b == p.b && t.h == p.h && t.y == p.y && t.x == p.x;
 }
 
+// Padding of a map smaller than kernel_size * dilation (the DiNAT layer's
+// maybe_pad): the operator runs on an Hp x Wp map (Hp = max(H, k*d), the same
+// for Wp) whose pixels at row >= H or column >= W hold the head's pad key
+// and value (D-vectors, [heads, D]; NULL = zeros).  Shape keeps the real H, W.
+struct Pad {
+  const void *k, *v;
+  int Hp, Wp;
+};
+
+inline Pad no_pad(const Shape &s) { return Pad{nullptr, nullptr, s.H, s.W}; }
+
 // Launchers (one per kernel family); each returns hipSuccess or the launch
 // error.  Argument checking happens before these are reached.  q, k and v
 // share the strides `in`; out has its own.
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
                             void *out, const Shape &s, const Strides &in, const Strides &out_st,
-                            na2d_dtype_t dt, hipStream_t st);
+                            const Pad &pad, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
-                             const Strides &out_st, na2d_dtype_t dt, hipStream_t st,
-                             bool *supported);
+                             const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
+                             hipStream_t st, bool *supported);
 // Whole-sub-grid kernel (H == W == k*d); sets *supported = false when the
 // problem is not of that kind.  Strides in bytes (mfma::ByteStrides).
 namespace mfma {
@@ -123,8 +134,8 @@ struct ByteStrides;
 }
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const mfma::ByteStrides &in,
-                             const mfma::ByteStrides &out_st, na2d_dtype_t dt, hipStream_t st,
-                             bool *supported);
+                             const mfma::ByteStrides &out_st, const Pad &pad,
+                             na2d_dtype_t dt, hipStream_t st, bool *supported);
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);

@@ -678,8 +678,8 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
-                             const Strides &out_st, na2d_dtype_t dt, hipStream_t st,
-                             bool *supported) {
+                             const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
+                             hipStream_t st, bool *supported) {
   *supported = true;
   if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) {
     *supported = false;
@@ -692,8 +692,13 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
     *supported = false;
     return hipSuccess;
   }
-  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, dt, st, supported);
+  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, pad, dt, st, supported);
   if (*supported) return e;
+  // the general kernel runs unpadded maps only
+  if (pad.Hp > s.H || pad.Wp > s.W) {
+    *supported = false;
+    return hipSuccess;
+  }
   *supported = true;
   if (dt == NA2D_DTYPE_BF16)
     return launch_dtype<__bf16>(q, k, v, rpb, out, s, lay, st, supported);

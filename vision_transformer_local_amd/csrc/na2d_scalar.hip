@@ -25,7 +25,9 @@ struct QueryPos {
   int h, i, j, ry, rx, ci, cj, sy, sx;
 };
 
-__device__ __forceinline__ QueryPos decode_query(int64_t t, const Shape &s) {
+// Windows are taken on the Hp x Wp map (Hp = H, Wp = W without padding).
+__device__ __forceinline__ QueryPos decode_query(int64_t t, const Shape &s, int Hp = 0,
+                                                 int Wp = 0) {
   QueryPos p;
   const int64_t hw = (int64_t)s.H * s.W;
   p.plane = t / hw;
@@ -37,8 +39,8 @@ __device__ __forceinline__ QueryPos decode_query(int64_t t, const Shape &s) {
   p.ci = p.i / s.dil;
   p.rx = p.j % s.dil;
   p.cj = p.j / s.dil;
-  p.sy = window_start(p.ci, class_len(s.H, p.ry, s.dil), s.ks);
-  p.sx = window_start(p.cj, class_len(s.W, p.rx, s.dil), s.ks);
+  p.sy = window_start(p.ci, class_len(Hp > 0 ? Hp : s.H, p.ry, s.dil), s.ks);
+  p.sx = window_start(p.cj, class_len(Wp > 0 ? Wp : s.W, p.rx, s.dil), s.ks);
   return p;
 }
 
@@ -61,10 +63,19 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
                                                         const T *__restrict__ v,
                                                         const T *__restrict__ rpb,
                                                         T *__restrict__ out, Shape s,
-                                                        Strides si, Strides so) {
+                                                        Strides si, Strides so, Pad pad) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= s.n_query) return;
-  const QueryPos p = decode_query(t, s);
+  const QueryPos p = decode_query(t, s, pad.Hp, pad.Wp);
+  // keys and values of padded pixels (zeros when no vectors are given)
+  float pk[D], pv[D];
+  const bool padded = pad.Hp > s.H || pad.Wp > s.W;
+  if (padded) {
+#pragma unroll
+    for (int e = 0; e < D; ++e) pk[e] = pv[e] = 0.f;
+    if (pad.k) load_row((const T *)pad.k + (int64_t)p.h * D, pk);
+    if (pad.v) load_row((const T *)pad.v + (int64_t)p.h * D, pv);
+  }
   const int64_t bb = p.plane / s.heads;
   const int64_t ibase = bb * si.b + p.h * si.h;
   const T *kp = k + ibase;
@@ -83,8 +94,14 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
     for (int c = 0; c < s.ks; ++c) {
       const int col = p.rx + (p.sx + c) * s.dil;
       const int64_t off = row * si.y + col * si.x;
+      const bool real = !padded || (row < s.H && col < s.W);
       float kr[D];
-      load_row(kp + off, kr);
+      if (real) {
+        load_row(kp + off, kr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D; ++e) kr[e] = pk[e];
+      }
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) dot = fmaf(qr[e], kr[e], dot);
@@ -99,7 +116,12 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
       const float pr = expf(sc - m);
       l += pr;
       float vr[D];
-      load_row(vp + off, vr);
+      if (real) {
+        load_row(vp + off, vr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D; ++e) vr[e] = pv[e];
+      }
 #pragma unroll
       for (int e = 0; e < D; ++e) acc[e] = fmaf(pr, vr[e], acc[e]);
     }
@@ -205,24 +227,24 @@ bool grid_for(int64_t work, int per_block, dim3 *grid) {
 
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
                             void *out, const Shape &s, const Strides &in, const Strides &out_st,
-                            na2d_dtype_t dt, hipStream_t st) {
+                            const Pad &pad, na2d_dtype_t dt, hipStream_t st) {
   dim3 grid;
   if (!grid_for(s.n_query, 256, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
     case NA2D_DTYPE_F32:
       fused_fma_kernel<float><<<grid, 256, 0, st>>>((const float *)q, (const float *)k,
                                                    (const float *)v, (const float *)rpb,
-                                                   (float *)out, s, in, out_st);
+                                                   (float *)out, s, in, out_st, pad);
       break;
     case NA2D_DTYPE_BF16:
       fused_fma_kernel<__bf16><<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
                                                     (const __bf16 *)v, (const __bf16 *)rpb,
-                                                    (__bf16 *)out, s, in, out_st);
+                                                    (__bf16 *)out, s, in, out_st, pad);
       break;
     case NA2D_DTYPE_F16:
       fused_fma_kernel<_Float16><<<grid, 256, 0, st>>>(
           (const _Float16 *)q, (const _Float16 *)k, (const _Float16 *)v, (const _Float16 *)rpb,
-          (_Float16 *)out, s, in, out_st);
+          (_Float16 *)out, s, in, out_st, pad);
       break;
   }
   return hipGetLastError();

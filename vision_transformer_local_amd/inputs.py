@@ -79,3 +79,6 @@ NAT_TINY_SWEEP = tuple(Problem(128, h, s, s, 32, 7, 1, "bf16")
                        for s, h in ((56, 2), (28, 4), (14, 8), (7, 16)))
 DETECTION = tuple(Problem(2, 6, 200, 336, 32, ks, d, dt)
                   for ks in (7, 13) for d in (1, 8) for dt in ("bf16", "f16"))
+# DiNAT stage 1 of a 192x192 image: a 48x48 map under the d = 8 layer, which
+# the layer pads to 56x56 (maybe_pad) before attending.
+DINAT_S1_D8_PAD48 = Problem(64, 2, 48, 48, 32, 7, 8, "bf16")

@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         i64p = ctypes.POINTER(ctypes.c_int64)
         L.na2d_forward_strided.restype = i
         L.na2d_forward_strided.argtypes = [vp] * 5 + [i] * 7 + [i64p, i64p, i, vp]
+        L.na2d_forward_padded.restype = i
+        L.na2d_forward_padded.argtypes = [vp] * 7 + [i] * 8 + [vp]
         L.na2d_qkrpb.restype = i
         L.na2d_qkrpb.argtypes = [vp] * 4 + [i] * 8 + [vp]
         L.na2d_softmax.restype = i
@@ -170,6 +172,30 @@ def na2d_forward_strided(q, k, v, rpb, out, kernel_size: int, dilation: int):
                                     si, so, _DTYPE_CODES[q.dtype], _stream(q))
     _check(st, "na2d_forward_strided")
     return out
+
+
+def na2d_forward_padded(q, k, v, rpb, pad_k, pad_v, out, kernel_size: int, dilation: int):
+    """Fused forward into ``out`` on a map that may be smaller than
+    kernel_size * dilation: padded below/right with the per-head pad vectors
+    ``pad_k``/``pad_v`` ([heads, D] or None = zeros), attended, cropped."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, q.shape)
+    for t, n in ((pad_k, "pad_k"), (pad_v, "pad_v")):
+        if t is not None:
+            _need(t, n, q.dtype, (heads, D))
+    _rpb_check(rpb, q, heads, kernel_size)
+    st = lib().na2d_forward_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(pad_k),
+                                   _ptr(pad_v), _ptr(out), B, heads, H, W, D, int(kernel_size),
+                                   int(dilation), _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_forward_padded")
+    return out
+
+
+def forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size: int, dilation: int):
+    """Allocating ``na2d_forward_padded``."""
+    return na2d_forward_padded(q, k, v, rpb, pad_k, pad_v, torch.empty_like(q), kernel_size,
+                               dilation)
 
 
 def forward_channels_last(q, k, v, rpb, heads: int, kernel_size: int, dilation: int):
