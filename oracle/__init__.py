@@ -222,3 +222,44 @@ def forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size: int, dilation: int, 
     idx = (((bb * heads + hh) * Hp + ii) * Wp + jj).reshape(-1)
     out = forward(qp, kp, vp, rpb, ks, dil, idx=idx, threads=threads)["out"]
     return out.reshape(B, heads, H, W, D)
+
+
+def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: int,
+                  dilation: int, *, threads: int | None = None):
+    """Oracle of the attention block around the operator: the NA module of
+    NAT / DiNAT (DiNAT walk-through blog, "What is DiNAT": query/key/value
+    projections with bias -- the configuration's qkv_bias -- then
+    natten2dqkrpb, softmax, natten2dav), closed by the output projection.
+
+    x: [B, H, W, C] channels-last features; w_qkv [3C, C] (rows: the query,
+    key and value projections, in that order), b_qkv [3C] or None; w_out
+    [C, C], b_out [C] or None; head h owns channels h*D .. h*D + D - 1 of
+    each projection (D = C / heads).  Maps smaller than kernel_size *
+    dilation are handled as the layer does (``forward_padded``: the padded
+    features project to the biases).  Returns y [B, H, W, C]:
+
+        qkv = x w_qkv^T + b_qkv;  ctx = NA(q, k, v) per head;
+        y = ctx w_out^T + b_out
+    """
+    x = _f64(x)
+    if x.ndim != 4:
+        raise ValueError("x must be [B, H, W, C]")
+    B, H, W, C = x.shape
+    if C % heads != 0:
+        raise ValueError("C must be a multiple of heads")
+    D = C // heads
+    w_qkv, w_out = _f64(w_qkv), _f64(w_out)
+    if w_qkv.shape != (3 * C, C) or w_out.shape != (C, C):
+        raise ValueError("w_qkv must be [3C, C] and w_out [C, C]")
+    b_qkv = np.zeros(3 * C) if b_qkv is None else _f64(b_qkv)
+    b_out = np.zeros(C) if b_out is None else _f64(b_out)
+    qkv = x @ w_qkv.T + b_qkv                                   # [B, H, W, 3C]
+
+    def heads_of(t):                                            # -> [B, heads, H, W, D]
+        return np.ascontiguousarray(t.reshape(B, H, W, heads, D).transpose(0, 3, 1, 2, 4))
+
+    q, k, v = (heads_of(qkv[..., i * C:(i + 1) * C]) for i in range(3))
+    pad_k, pad_v = b_qkv[C:2 * C].reshape(heads, D), b_qkv[2 * C:].reshape(heads, D)
+    ctx = forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size, dilation, threads=threads)
+    ctx = ctx.transpose(0, 2, 3, 1, 4).reshape(B, H, W, C)      # merge the heads
+    return ctx @ w_out.T + b_out
