@@ -144,6 +144,50 @@ na2d_status_t na2d_forward_padded(const void *q, const void *k, const void *v, c
                                   int dilation, na2d_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Linear projection of channels-last features: y[m, n] = sum_k x[m, k] *
+ * w[n, k] + b[n] (w in the [out, in] layout of a Linear layer), the
+ * projections the attention module wraps around the operator (DiNAT
+ * walk-through blog, "What is DiNAT": query/key/value projections with bias,
+ * the configuration's qkv_bias).  fp32 accumulation, y rounded once.
+ *
+ *   x [M, K], w [N, K], b [N] (NULL = no bias), y [M, N]: dense, 16-byte
+ *   aligned, y overlapping none of the others.
+ * N % 16 == 0 and K % 32 == 0 (else NA2D_ERROR_NOT_SUPPORTED).
+ */
+na2d_status_t na2d_linear(const void *x, const void *w, const void *b, void *y, int64_t M,
+                          int N, int K, na2d_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of scratch na2d_block_forward needs: B*H*W*4*C elements (the
+ * q|k|v projection and the attention output); 0 for invalid sizes. */
+size_t na2d_block_workspace_size(int B, int H, int W, int C, int heads, na2d_dtype_t dtype);
+
+/*
+ * The attention block around the operator, on channels-last features:
+ *   qkv = x w_qkv^T + b_qkv;  ctx = NA(q, k, v) per head;  y = ctx w_out^T + b_out
+ * (the NAT/DiNAT attention module: q/k/v projections with bias, then
+ * natten2dqkrpb, softmax and natten2dav -- DiNAT walk-through blog, "What is
+ * DiNAT" -- closed by the output projection).  Maps smaller than
+ * kernel_size * dilation are padded as the layer does (maybe_pad): the
+ * padded features project to the key/value biases.
+ *
+ *   x, y        [B, H, W, C] channels-last, C = heads * 32
+ *   w_qkv       [3C, C] (rows: query, key, value projections); b_qkv [3C] or NULL
+ *   w_out       [C, C]; b_out [C] or NULL
+ *   rpb         [heads, 2k-1, 2k-1] or NULL
+ *   workspace   >= na2d_block_workspace_size(...) bytes of device scratch;
+ *               its content on return is unspecified
+ * Three kernel launches on `stream` (projection, attention reading q, k, v
+ * straight out of the projection's rows, projection).  y and workspace must
+ * overlap none of the inputs nor each other.  D = C / heads != 32 returns
+ * NA2D_ERROR_NOT_SUPPORTED; other rules as na2d_forward_padded.
+ */
+na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b_qkv,
+                                 const void *rpb, const void *w_out, const void *b_out,
+                                 void *y, void *workspace, size_t workspace_bytes, int B, int H,
+                                 int W, int C, int heads, int kernel_size, int dilation,
+                                 na2d_dtype_t dtype, hipStream_t stream);
+
+/*
  * Unfused step 1 (the blog's natten2dqkrpb): attn[b,h,i,j,n] =
  * q[b,h,i,j].k[neighbour n] / sqrt(D) + rpb[h][offset of n], in fp32.
  */

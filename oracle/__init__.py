@@ -225,7 +225,7 @@ def forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size: int, dilation: int, 
 
 
 def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: int,
-                  dilation: int, *, threads: int | None = None):
+                  dilation: int, *, stored=None, threads: int | None = None):
     """Oracle of the attention block around the operator: the NA module of
     NAT / DiNAT (DiNAT walk-through blog, "What is DiNAT": query/key/value
     projections with bias -- the configuration's qkv_bias -- then
@@ -240,6 +240,10 @@ def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: i
 
         qkv = x w_qkv^T + b_qkv;  ctx = NA(q, k, v) per head;
         y = ctx w_out^T + b_out
+
+    stored: optional function applied to qkv and ctx, for a network that
+    stores those tensors in a narrower type (e.g. rounding to bf16); the
+    default keeps every step exact.
     """
     x = _f64(x)
     if x.ndim != 4:
@@ -253,7 +257,8 @@ def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: i
         raise ValueError("w_qkv must be [3C, C] and w_out [C, C]")
     b_qkv = np.zeros(3 * C) if b_qkv is None else _f64(b_qkv)
     b_out = np.zeros(C) if b_out is None else _f64(b_out)
-    qkv = x @ w_qkv.T + b_qkv                                   # [B, H, W, 3C]
+    keep = stored if stored is not None else (lambda a: a)
+    qkv = keep(x @ w_qkv.T + b_qkv)                             # [B, H, W, 3C]
 
     def heads_of(t):                                            # -> [B, heads, H, W, D]
         return np.ascontiguousarray(t.reshape(B, H, W, heads, D).transpose(0, 3, 1, 2, 4))
@@ -261,5 +266,5 @@ def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: i
     q, k, v = (heads_of(qkv[..., i * C:(i + 1) * C]) for i in range(3))
     pad_k, pad_v = b_qkv[C:2 * C].reshape(heads, D), b_qkv[2 * C:].reshape(heads, D)
     ctx = forward_padded(q, k, v, rpb, pad_k, pad_v, kernel_size, dilation, threads=threads)
-    ctx = ctx.transpose(0, 2, 3, 1, 4).reshape(B, H, W, C)      # merge the heads
+    ctx = keep(ctx.transpose(0, 2, 3, 1, 4).reshape(B, H, W, C))  # merge the heads
     return ctx @ w_out.T + b_out

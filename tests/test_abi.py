@@ -338,3 +338,89 @@ def test_padded_forward_pointer_rules():
     p = list(P[:7])
     p[6] = p[4]
     assert L.na2d_forward_padded(*p, *args, S) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# na2d_linear and na2d_block_forward
+LINEAR_CASES = [
+    ((0, 64, 64, BF16), INVALID),
+    ((128, 0, 64, BF16), INVALID),
+    ((128, 64, -1, BF16), INVALID),
+    ((128, 64, 64, 7), INVALID),
+    ((1 << 58, 64, 64, BF16), INVALID),      # M*K beyond 2^60
+    ((128, 40, 64, BF16), UNSUPPORTED),      # N % 16
+    ((128, 64, 48, BF16), UNSUPPORTED),      # K % 32
+]
+
+
+@pytest.mark.parametrize("args,expect", LINEAR_CASES)
+def test_linear_validation(args, expect):
+    L = na2d.lib()
+    far = [ctypes.c_void_p((1 << 44) * (i + 1)) for i in range(4)]
+    assert L.na2d_linear(*far, *args, S) == expect
+
+
+def test_linear_pointer_rules():
+    L = na2d.lib()
+    far = [ctypes.c_void_p((1 << 44) * (i + 1)) for i in range(4)]
+    args = (1000, 64, 64, BF16)
+    for slot in (0, 1, 3):
+        p = list(far)
+        p[slot] = NULL
+        assert L.na2d_linear(*p, *args, S) == INVALID
+    for slot in range(4):
+        p = list(far)
+        p[slot] = ctypes.c_void_p(p[slot].value + 8)
+        assert L.na2d_linear(*p, *args, S) == INVALID
+    p = list(far)
+    p[3] = ctypes.c_void_p(far[0].value + 64)  # y inside x
+    assert L.na2d_linear(*p, *args, S) == INVALID
+
+
+def test_block_workspace_size():
+    L = na2d.lib()
+    assert L.na2d_block_workspace_size(2, 7, 9, 64, 2, BF16) == 2 * 7 * 9 * 4 * 64 * 2
+    assert L.na2d_block_workspace_size(2, 7, 9, 64, 2, F32) == 2 * 7 * 9 * 4 * 64 * 4
+    assert L.na2d_block_workspace_size(0, 7, 9, 64, 2, BF16) == 0
+    assert L.na2d_block_workspace_size(2, 7, 9, 64, 2, 9) == 0
+
+
+BLOCK_CASES = [
+    ((2, 7, 9, 64, 3, 7, 1, BF16), INVALID),       # C % heads
+    ((2, 7, 9, 64, 2, 6, 1, BF16), INVALID),       # even kernel
+    ((0, 7, 9, 64, 2, 7, 1, BF16), INVALID),
+    ((2, 7, 9, 64, 2, 7, 0, BF16), INVALID),
+    ((2, 7, 9, 128, 2, 7, 1, BF16), UNSUPPORTED),  # D = 64
+    ((2, 7, 9, 64, 2, 15, 1, BF16), UNSUPPORTED),  # k > 13
+]
+
+
+def _block(L, ptrs, args, ws_bytes=1 << 40):
+    return L.na2d_block_forward(*ptrs, ws_bytes, *args, S)
+
+
+@pytest.mark.parametrize("args,expect", BLOCK_CASES)
+def test_block_validation(args, expect):
+    L = na2d.lib()
+    far = [ctypes.c_void_p((1 << 41) * (i + 1)) for i in range(8)]
+    assert _block(L, far, args) == expect
+
+
+def test_block_pointer_and_workspace_rules():
+    L = na2d.lib()
+    far = [ctypes.c_void_p((1 << 41) * (i + 1)) for i in range(8)]
+    args = (2, 7, 9, 64, 2, 7, 2, BF16)
+    need = L.na2d_block_workspace_size(2, 7, 9, 64, 2, BF16)
+    assert _block(L, far, args, need - 1) == INVALID
+    for slot in (0, 1, 4, 6, 7):
+        p = list(far)
+        p[slot] = NULL
+        assert _block(L, p, args) == INVALID
+    for slot in range(8):
+        p = list(far)
+        p[slot] = ctypes.c_void_p(p[slot].value + 8)
+        assert _block(L, p, args) == INVALID
+    for a, b in ((6, 0), (7, 1), (7, 6), (6, 4), (7, 3)):  # y/workspace over an input or each other
+        p = list(far)
+        p[a] = ctypes.c_void_p(p[b].value)
+        assert _block(L, p, args) == INVALID

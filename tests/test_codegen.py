@@ -21,7 +21,7 @@ import pytest
 
 from vision_transformer_local_amd import build as B
 
-SOURCES = ["na2d_mfma.hip", "na2d_dense.hip"]
+SOURCES = ["na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip"]
 KERNEL = re.compile(r"^(_ZN4na2d12_GLOBAL__N_1\d+\w*mfma_kernel\S*):", re.M)
 
 

@@ -211,6 +211,95 @@ na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const vo
                            NA2D_ALGO_AUTO, stream);
 }
 
+na2d_status_t na2d_linear(const void *x, const void *w, const void *b, void *y, int64_t M,
+                          int N, int K, na2d_dtype_t dtype, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  if (M < 1 || N < 1 || K < 1 || M > kMaxElems / N || M > kMaxElems / K)
+    return NA2D_ERROR_INVALID_VALUE;
+  if (!x || !w || !y) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (b && !aligned16(b)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t yb = M * N * eb;
+  if (overlaps(y, yb, x, M * K * eb) || overlaps(y, yb, w, (int64_t)N * K * eb) ||
+      overlaps(y, yb, b, N * eb))
+    return NA2D_ERROR_INVALID_VALUE;
+  if (!na2d::linear_supported(N, K)) return NA2D_ERROR_NOT_SUPPORTED;
+  return from_hip(na2d::launch_linear(x, w, b, y, M, N, K, dtype, stream));
+}
+
+size_t na2d_block_workspace_size(int B, int H, int W, int C, int heads, na2d_dtype_t dtype) {
+  if (!dtype_ok(dtype) || B < 1 || H < 1 || W < 1 || C < 1 || heads < 1) return 0;
+  const int64_t M = (int64_t)B * H * W;
+  if (M > kMaxElems / (4 * (int64_t)C)) return 0;
+  return (size_t)(M * 4 * C * elem_bytes(dtype));
+}
+
+na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b_qkv,
+                                 const void *rpb, const void *w_out, const void *b_out,
+                                 void *y, void *workspace, size_t workspace_bytes, int B, int H,
+                                 int W, int C, int heads, int kernel_size, int dilation,
+                                 na2d_dtype_t dtype, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  if (B < 1 || H < 1 || W < 1 || C < 1 || heads < 1 || kernel_size < 1 || dilation < 1)
+    return NA2D_ERROR_INVALID_VALUE;
+  if (C % heads != 0) return NA2D_ERROR_INVALID_VALUE;
+  const int D = C / heads;
+  // the attention step: shape rules on the padded map (maps below k*d are
+  // padded as the layer does), then the real extent
+  const int64_t span = (int64_t)kernel_size * dilation;
+  const int64_t Hp = H > span ? H : span, Wp = W > span ? W : span;
+  if (Hp > INT_MAX || Wp > INT_MAX) return NA2D_ERROR_INVALID_VALUE;
+  na2d::Shape s;
+  na2d_status_t st = check_shape(B, heads, (int)Hp, (int)Wp, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  s.H = H;
+  s.W = W;
+  s.n_query = s.n_query / ((int64_t)Hp * Wp) * ((int64_t)H * W);
+  const int64_t M = (int64_t)B * H * W;
+  if (M > kMaxElems / (4 * (int64_t)C)) return NA2D_ERROR_INVALID_VALUE;
+  if (!x || !w_qkv || !w_out || !y || !workspace) return NA2D_ERROR_INVALID_VALUE;
+  const void *ptrs[] = {x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
+  const int64_t eb = elem_bytes(dtype);
+  const size_t need = na2d_block_workspace_size(B, H, W, C, heads, dtype);
+  if (need == 0 || workspace_bytes < need) return NA2D_ERROR_INVALID_VALUE;
+  const int64_t side = 2 * kernel_size - 1;
+  struct Span {
+    const void *p;
+    int64_t n;
+  };
+  const Span read[] = {{x, M * C * eb},          {w_qkv, 3LL * C * C * eb},
+                       {b_qkv, 3LL * C * eb},    {rpb, heads * side * side * eb},
+                       {w_out, (int64_t)C * C * eb}, {b_out, C * eb}};
+  const Span written[] = {{y, M * C * eb}, {workspace, (int64_t)need}};
+  for (const Span &wr : written)
+    for (const Span &rd : read)
+      if (overlaps(wr.p, wr.n, rd.p, rd.n)) return NA2D_ERROR_INVALID_VALUE;
+  if (overlaps(y, M * C * eb, workspace, (int64_t)need)) return NA2D_ERROR_INVALID_VALUE;
+  if (!na2d::linear_supported(3 * C, C) || !na2d::linear_supported(C, C))
+    return NA2D_ERROR_NOT_SUPPORTED;
+  // 1. qkv = x w_qkv^T + b_qkv: [M, 3C], q | k | v channels per pixel
+  char *qkv = (char *)workspace;
+  char *ctx = qkv + M * 3 * C * eb;
+  hipError_t e = na2d::launch_linear(x, w_qkv, b_qkv, qkv, M, 3 * C, C, dtype, stream);
+  if (e != hipSuccess) return from_hip(e);
+  // 2. per-head attention on strided views of qkv, into ctx [M, C]; padded
+  //    pixels carry the key/value biases (the projection of a zero feature)
+  const int64_t C3 = 3LL * C;
+  const na2d::Strides in{(int64_t)H * W * C3, D, (int64_t)W * C3, C3};
+  const na2d::Strides os{(int64_t)H * W * C, D, (int64_t)W * C, C};
+  const char *bq = (const char *)b_qkv;
+  const na2d::Pad pad{bq ? bq + C * eb : nullptr, bq ? bq + 2 * C * eb : nullptr, (int)Hp,
+                      (int)Wp};
+  st = forward_checked(qkv, qkv + C * eb, qkv + 2 * C * eb, rpb, ctx, s, in, os, pad, dtype,
+                       NA2D_ALGO_AUTO, stream);
+  if (st != NA2D_SUCCESS) return st;
+  // 3. y = ctx w_out^T + b_out
+  return from_hip(na2d::launch_linear(ctx, w_out, b_out, y, M, C, C, dtype, stream));
+}
+
 na2d_status_t na2d_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                          int B, int heads, int H, int W, int D, int kernel_size,
                          int dilation, na2d_dtype_t dtype, hipStream_t stream) {

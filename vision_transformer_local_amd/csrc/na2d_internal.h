@@ -153,5 +153,9 @@ hipError_t launch_backward(const void *q, const void *k, const void *v, const vo
                            const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s,
                      na2d_dtype_t dt, hipStream_t st);
+// y[M, N] = x[M, K] . w[N, K]^T + b (b may be null); N % 16 == 0, K % 32 == 0.
+bool linear_supported(int N, int K);
+hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
+                         int K, na2d_dtype_t dt, hipStream_t st);
 
 }  // namespace na2d

@@ -82,3 +82,42 @@ DETECTION = tuple(Problem(2, 6, 200, 336, 32, ks, d, dt)
 # DiNAT stage 1 of a 192x192 image: a 48x48 map under the d = 8 layer, which
 # the layer pads to 56x56 (maybe_pad) before attending.
 DINAT_S1_D8_PAD48 = Problem(64, 2, 48, 48, 32, 7, 8, "bf16")
+
+
+# Attention-block inputs (channels-last features and projection weights).
+@dataclasses.dataclass(frozen=True)
+class BlockProblem:
+    B: int
+    H: int
+    W: int
+    C: int
+    heads: int
+    kernel_size: int
+    dilation: int
+    dtype: str = "bf16"
+
+    def describe(self) -> str:
+        return "B%d %dx%d C%d h%d k%d d%d %s" % (self.B, self.H, self.W, self.C, self.heads,
+                                                  self.kernel_size, self.dilation, self.dtype)
+
+
+def make_block_inputs(p: BlockProblem, seed: int = 0):
+    """x ~ N(0, 1) [B, H, W, C]; w_qkv ~ N(0, 1/C) [3C, C]; b_qkv ~ 0.5 N(0, 1)
+    [3C]; w_out ~ N(0, 1/C) [C, C]; b_out ~ 0.5 N(0, 1) [C]; rpb ~ 0.02 N(0, 1)
+    [heads, 2k-1, 2k-1]; drawn in fp32 in that order from one seeded
+    generator, then rounded once to the run dtype."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    C, side = p.C, 2 * p.kernel_size - 1
+    x = torch.randn(p.B, p.H, p.W, C, generator=g)
+    w_qkv = torch.randn(3 * C, C, generator=g) / C ** 0.5
+    b_qkv = 0.5 * torch.randn(3 * C, generator=g)
+    w_out = torch.randn(C, C, generator=g) / C ** 0.5
+    b_out = 0.5 * torch.randn(C, generator=g)
+    rpb = 0.02 * torch.randn(p.heads, side, side, generator=g)
+    dt = DTYPES[p.dtype]
+    return tuple(t.to(dt) for t in (x, w_qkv, b_qkv, rpb, w_out, b_out))
+
+
+# The NAT-Tiny sweep shapes as attention blocks (C = heads * 32).
+BLOCK_SWEEP = tuple(BlockProblem(128, s, s, 32 * h, h, 7, 1, "bf16")
+                    for s, h in ((56, 2), (28, 4), (14, 8), (7, 16)))

@@ -55,6 +55,12 @@ def lib() -> ctypes.CDLL:
         L.na2d_forward_strided.argtypes = [vp] * 5 + [i] * 7 + [i64p, i64p, i, vp]
         L.na2d_forward_padded.restype = i
         L.na2d_forward_padded.argtypes = [vp] * 7 + [i] * 8 + [vp]
+        L.na2d_linear.restype = i
+        L.na2d_linear.argtypes = [vp] * 4 + [ctypes.c_int64, i, i, i, vp]
+        L.na2d_block_workspace_size.restype = ctypes.c_size_t
+        L.na2d_block_workspace_size.argtypes = [i] * 6
+        L.na2d_block_forward.restype = i
+        L.na2d_block_forward.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 8 + [vp]
         L.na2d_qkrpb.restype = i
         L.na2d_qkrpb.argtypes = [vp] * 4 + [i] * 8 + [vp]
         L.na2d_softmax.restype = i
@@ -318,3 +324,75 @@ def backward(q, k, v, rpb, dout, kernel_size: int, dilation: int, bias_grad: boo
             if bias_grad else None)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     return na2d_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, kernel_size, dilation)
+
+
+def na2d_linear(x, w, b, y):
+    """y = x w^T + b on the last dimension (x [..., K], w [N, K], b [N] or
+    None, y [..., N]; all contiguous, same dtype)."""
+    if x.dtype not in _DTYPE_CODES:
+        raise ValueError("dtype %s not supported" % x.dtype)
+    N, K = (int(d) for d in w.shape)
+    if x.shape[-1] != K:
+        raise ValueError("x must end in K = %d" % K)
+    M = x.numel() // K
+    _need(x, "x", x.dtype)
+    _need(w, "w", x.dtype, (N, K))
+    _need(y, "y", x.dtype, tuple(x.shape[:-1]) + (N,))
+    if b is not None:
+        _need(b, "b", x.dtype, (N,))
+    st = lib().na2d_linear(_ptr(x), _ptr(w), _ptr(b), _ptr(y), M, N, K, _DTYPE_CODES[x.dtype],
+                           _stream(x))
+    _check(st, "na2d_linear")
+    return y
+
+
+def linear(x, w, b=None):
+    """Allocating ``na2d_linear``."""
+    return na2d_linear(x, w, b, torch.empty(tuple(x.shape[:-1]) + (w.shape[0],), dtype=x.dtype,
+                                            device=x.device))
+
+
+def na2d_block_workspace_size(B, H, W, C, heads, dtype) -> int:
+    return int(lib().na2d_block_workspace_size(B, H, W, C, heads, _DTYPE_CODES[dtype]))
+
+
+def na2d_block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace, heads: int,
+                       kernel_size: int, dilation: int):
+    """The attention block on channels-last features x [B, H, W, C] into y:
+    q/k/v projection, per-head NA (maps below k*d padded as the layer does),
+    output projection.  workspace: a uint8 device tensor of at least
+    ``na2d_block_workspace_size`` bytes."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, W, C]")
+    B, H, W, C = (int(d) for d in x.shape)
+    dt = x.dtype
+    _need(x, "x", dt)
+    _need(y, "y", dt, x.shape)
+    _need(w_qkv, "w_qkv", dt, (3 * C, C))
+    _need(w_out, "w_out", dt, (C, C))
+    if b_qkv is not None:
+        _need(b_qkv, "b_qkv", dt, (3 * C,))
+    if b_out is not None:
+        _need(b_out, "b_out", dt, (C,))
+    side = 2 * kernel_size - 1
+    if rpb is not None:
+        _need(rpb, "rpb", dt, (heads, side, side))
+    _need(workspace, "workspace", torch.uint8)
+    st = lib().na2d_block_forward(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(rpb), _ptr(w_out),
+                                  _ptr(b_out), _ptr(y), _ptr(workspace), workspace.numel(), B, H,
+                                  W, C, heads, int(kernel_size), int(dilation),
+                                  _DTYPE_CODES[dt], _stream(x))
+    _check(st, "na2d_block_forward")
+    return y
+
+
+def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: int,
+                  dilation: int):
+    """Allocating ``na2d_block_forward`` (y and the workspace)."""
+    B, H, W, C = (int(d) for d in x.shape)
+    n = na2d_block_workspace_size(B, H, W, C, heads, x.dtype)
+    if n == 0:
+        raise Na2dError(INVALID_VALUE, "na2d_block_workspace_size: invalid problem")
+    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    return na2d_block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, torch.empty_like(x), ws, heads,
+                              kernel_size, dilation)
