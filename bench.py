@@ -56,9 +56,14 @@ WORKLOADS = {
     "tiny_f32": I.TINY,
     "dinat_s1_d8_pad48": I.DINAT_S1_D8_PAD48,
 }
+BLOCK_WORKLOADS = {
+    "block_56": I.BLOCK_SWEEP[0], "block_28": I.BLOCK_SWEEP[1],
+    "block_14": I.BLOCK_SWEEP[2], "block_7": I.BLOCK_SWEEP[3],
+}
 BACKWARD_SOURCES = ["vision_transformer_local_amd/csrc/na2d_backward.hip",
                     "vision_transformer_local_amd/csrc/na2d_internal.h"]
 KERNEL_SOURCES = ["vision_transformer_local_amd/csrc/na2d_mfma.hip",
+                  "vision_transformer_local_amd/csrc/na2d_linear.hip",
                   "vision_transformer_local_amd/csrc/na2d_dense.hip",
                   "vision_transformer_local_amd/csrc/na2d_mfma_common.h",
                   "vision_transformer_local_amd/csrc/na2d_scalar.hip",
@@ -159,9 +164,14 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="nat_tiny_s1", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="nat_tiny_s1",
+                    choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
     ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
+    ap.add_argument("--pass", dest="which", default="forward",
+                    choices=["forward", "backward", "block"],
+                    help="forward: the operator; backward: its gradients; block: the "
+                         "attention block (projection -> NA -> projection) on the "
+                         "block_* workloads")
     ap.add_argument("--padded", action="store_true",
                     help="forward through na2d_forward_padded (maps smaller than k*d are "
                          "padded with per-head pad vectors, attended and cropped)")
@@ -202,8 +212,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": max(1, args.steps)}))
         return 0
-    p = WORKLOADS[args.workload]
     L = na2d.lib()
+    if args.which == "block":
+        return bench_block(args, dev, L)
+    p = WORKLOADS[args.workload]
     if args.which == "backward":
         return bench_backward(args, p, dev, L)
 
@@ -375,6 +387,86 @@ def time_steps(args, launch, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+
+
+def block_algorithmic_bytes(p) -> int:
+    """Bytes the block itself must move: x read and y written once, the
+    weights, biases and bias table read once."""
+    s = elem_size(p.dtype)
+    side = 2 * p.kernel_size - 1
+    M = p.B * p.H * p.W
+    return (2 * M * p.C + 4 * p.C * p.C + 4 * p.C + p.heads * side * side) * s
+
+
+def bench_block(args, dev, L):
+    """One step = the attention block (three launches) over the workload."""
+    import numpy as np
+    if args.workload not in BLOCK_WORKLOADS:
+        print("--pass block takes a block_* workload", file=sys.stderr)
+        return 2
+    p = BLOCK_WORKLOADS[args.workload]
+    cpu = I.make_block_inputs(p, seed=0)
+    x0, w_qkv, b_qkv, rpb, w_out, b_out = cpu
+    B, H, W, C = x0.shape
+    ks, dil = p.kernel_size, p.dilation
+    params = [t.to(dev) for t in (w_qkv, b_qkv, rpb, w_out, b_out)]
+    wsb = na2d.na2d_block_workspace_size(B, H, W, C, p.heads, x0.dtype)
+    xbytes = x0.numel() * x0.element_size()
+    R = max(2, math.ceil(args.rotate_bytes / (2 * xbytes + wsb)))
+    reps = [(x0.to(dev), torch.empty_like(x0, device=dev),
+             torch.empty(wsb, dtype=torch.uint8, device=dev)) for _ in range(R)]
+    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
+    wq, bq, rp, wo, bo = params
+
+    def launch(i, stream):
+        x, y, ws = reps[i % R]
+        r = L.na2d_block_forward(x.data_ptr(), wq.data_ptr(), bq.data_ptr(), rp.data_ptr(),
+                                 wo.data_ptr(), bo.data_ptr(), y.data_ptr(), ws.data_ptr(), wsb,
+                                 B, H, W, C, p.heads, ks, dil, dt_code, ctypes.c_void_p(stream))
+        if r != 0:
+            raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
+
+    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+
+    # sanity: a sample of pixels of the first replica against the oracle
+    import oracle
+    idx = np.random.default_rng(0).choice(B * H * W, size=min(2048, B * H * W), replace=False)
+    dt = x0.dtype
+    ref = oracle.block_forward(
+        x0, w_qkv, b_qkv, rpb, w_out, b_out, p.heads, ks, dil,
+        stored=lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt).double().numpy())
+    got = reps[0][1].reshape(-1, C)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+    max_err = float(np.abs(got - ref.reshape(-1, C)[idx]).max())
+
+    abytes = block_algorithmic_bytes(p)
+    achieved = abytes / (kernel_ms / 1e3) / 1e9
+    M = B * H * W
+    rec = {
+        "metric": "NA block pixels/s (+ achieved HBM GB/s as % of MI355X peak)",
+        "value": M / (ms_per_step / 1e3),
+        "unit": "pixels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) features, N(0,1/C) weights, 0.5*N(0,1) biases)",
+        "config": {"workload": "%s block: %s" % (args.workload, p.describe()),
+                   "B": B, "H": H, "W": W, "C": C, "heads": p.heads, "kernel_size": ks,
+                   "dilation": dil, "path": "block", "timing": args.mode, "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload, "block")},
+        "kernel_ms": kernel_ms,
+        "algorithmic_bytes_per_step": abytes,
+        "sample_max_abs_err": max_err,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def bench_backward(args, p, dev, L):

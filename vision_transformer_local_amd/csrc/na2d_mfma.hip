@@ -221,7 +221,9 @@ __device__ __forceinline__ QueryOffs query_offsets(const RowPart &r, const ColPa
   const int cj = c.cc0 + min(lc, c.cc1 - 1 - c.cc0);
   const unsigned row = r.ry + __umul24((unsigned)ci, (unsigned)s.dil);
   const unsigned col = c.rx + __umul24((unsigned)cj, (unsigned)s.dil);
-  return QueryOffs{row * si.y + col * si.x, row * so.y + col * so.x};
+  // row < 2^24 pixels and strides < 2^24 bytes (checked on the host)
+  return QueryOffs{(unsigned)__umul24(row, si.y) + (unsigned)__umul24(col, si.x),
+                   (unsigned)__umul24(row, so.y) + (unsigned)__umul24(col, so.x)};
 }
 
 // Copy a block's K and V halo into one LDS buffer with the direct
@@ -589,7 +591,9 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // the block's results leave after the barrier, so that its wait covers
     // the next block's loads but not these stores
-    store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
+    // (STREAM runs dense maps only: out has q's strides)
+    if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
+    else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
     rcur = rnxt;
     ccur = cnxt;
     pcur = pnxt;
@@ -602,7 +606,9 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     if (!more0) break;
     step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < b1);
   }
-  store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);  // the last block
+  // the last block
+  if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
+  else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
 }
 
 // Compute units of the current device (queried once per device).

@@ -37,11 +37,14 @@ struct ByteStrides {
 };
 
 // Byte strides, or false when a (batch, head) plane's span does not fit the
-// kernels' 32-bit in-plane offsets (or a stride is negative).
+// kernels' 32-bit in-plane offsets, a row or column stride does not fit the
+// 24-bit multiplies that form them (16 MB; every realistic map), or a stride
+// is negative.
 inline bool byte_strides(const Strides &t, const Shape &s, int64_t elem, ByteStrides *out) {
   if (t.b < 0 || t.h < 0 || t.y < 0 || t.x < 0) return false;
   const int64_t span = ((int64_t)(s.H - 1) * t.y + (int64_t)(s.W - 1) * t.x + kHeadDim) * elem;
   if (span > (int64_t(1) << 31)) return false;
+  if (t.y * elem >= (int64_t(1) << 24) || t.x * elem >= (int64_t(1) << 24)) return false;
   *out = ByteStrides{t.b * elem, t.h * elem, (uint32_t)(t.y * elem), (uint32_t)(t.x * elem)};
   return true;
 }
