@@ -278,22 +278,26 @@ na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b
     for (const Span &rd : read)
       if (overlaps(wr.p, wr.n, rd.p, rd.n)) return NA2D_ERROR_INVALID_VALUE;
   if (overlaps(y, M * C * eb, workspace, (int64_t)need)) return NA2D_ERROR_INVALID_VALUE;
-  if (!na2d::linear_supported(3 * C, C) || !na2d::linear_supported(C, C))
+  if (!na2d::linear_planar_supported(M, C, heads) || !na2d::linear_supported(C, C))
     return NA2D_ERROR_NOT_SUPPORTED;
-  // 1. qkv = x w_qkv^T + b_qkv: [M, 3C], q | k | v channels per pixel
+  // 1. q, k, v = x w_qkv^T + b_qkv, written as three dense [B, heads, H, W, D]
+  //    tensors (each head's rows contiguous, so the attention reads no line
+  //    shared with another head's or another projection's channels)
   char *qkv = (char *)workspace;
-  char *ctx = qkv + M * 3 * C * eb;
-  hipError_t e = na2d::launch_linear(x, w_qkv, b_qkv, qkv, M, 3 * C, C, dtype, stream);
+  const int64_t third = M * C * eb;
+  char *ctx = qkv + 3 * third;
+  hipError_t e =
+      na2d::launch_linear_qkv_planar(x, w_qkv, b_qkv, qkv, B, H * W, C, heads, dtype, stream);
   if (e != hipSuccess) return from_hip(e);
-  // 2. per-head attention on strided views of qkv, into ctx [M, C]; padded
-  //    pixels carry the key/value biases (the projection of a zero feature)
-  const int64_t C3 = 3LL * C;
-  const na2d::Strides in{(int64_t)H * W * C3, D, (int64_t)W * C3, C3};
+  // 2. per-head attention into ctx [M, C] (channels-last, the output
+  //    projection's input); padded pixels carry the key/value biases (the
+  //    projection of a zero feature)
+  const na2d::Strides in = na2d::planar_strides(s);
   const na2d::Strides os{(int64_t)H * W * C, D, (int64_t)W * C, C};
   const char *bq = (const char *)b_qkv;
   const na2d::Pad pad{bq ? bq + C * eb : nullptr, bq ? bq + 2 * C * eb : nullptr, (int)Hp,
                       (int)Wp};
-  st = forward_checked(qkv, qkv + C * eb, qkv + 2 * C * eb, rpb, ctx, s, in, os, pad, dtype,
+  st = forward_checked(qkv, qkv + third, qkv + 2 * third, rpb, ctx, s, in, os, pad, dtype,
                        NA2D_ALGO_AUTO, stream);
   if (st != NA2D_SUCCESS) return st;
   // 3. y = ctx w_out^T + b_out

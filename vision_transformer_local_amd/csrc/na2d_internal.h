@@ -157,5 +157,10 @@ hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s
 bool linear_supported(int N, int K);
 hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
                          int K, na2d_dtype_t dt, hipStream_t st);
+// The q|k|v projection (w[3C, C]) of B*HW pixels written head-planar: three
+// dense [B, heads, H, W, C/heads] tensors at y, y + B*HW*C, y + 2*B*HW*C.
+bool linear_planar_supported(int64_t pixels, int C, int heads);
+hipError_t launch_linear_qkv_planar(const void *x, const void *w, const void *b, void *y, int B,
+                                    int HW, int C, int heads, na2d_dtype_t dt, hipStream_t st);
 
 }  // namespace na2d

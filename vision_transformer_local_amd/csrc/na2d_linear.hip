@@ -6,13 +6,22 @@
 // qkv_bias) and closes with an output projection.
 //
 // Matrix-core kernel (bf16 / fp16, fp32 accumulation): a workgroup computes
-// a 128-pixel x TN-feature tile, four waves of 64 pixels x TN/2 features.
+// a 128-pixel x TN-feature tile (TN = N up to 192 features, so that x is read
+// once), four waves of 64 pixels x TN/2 features.
 // The product is formed transposed, y^T = w . x^T, so that each lane ends up
 // with 4 consecutive features of one pixel (one 8-byte store) and the bias
-// is the accumulator input.  K advances in chunks of 32: the chunk's w and x
-// rows are copied to LDS by the direct global->LDS path (16 bytes per lane,
-// chunks XOR-swizzled by row against bank conflicts) into one buffer while
-// the other is read.  fp32 data takes a scalar kernel.
+// is the accumulator input.  K advances in chunks of 32: each lane loads its
+// 16-byte pieces of the chunk's w and x rows into registers two chunks ahead
+// of the one being multiplied and writes them to one of two LDS buffers
+// (16-byte pieces XOR-swizzled by row against bank conflicts) while the other
+// is read, so that a long K loop (few tiles, wide K) is not one memory
+// latency per chunk.  fp32 data takes a scalar kernel.
+//
+// Output layouts: y[M, N] row-major, or -- for the block's q|k|v projection,
+// N = 3C, C = heads*D -- head-planar: feature n = t*C + h*D + e of pixel
+// m = b*HW + p goes to ((t*B + b)*heads + h)*HW*D + p*D + e, i.e. three dense
+// [B, heads, H, W, D] tensors, which the attention kernels then read without
+// cache lines shared between heads.
 #include "na2d_mfma_common.h"
 
 #include <limits.h>
@@ -23,7 +32,7 @@ namespace {
 using namespace mfma;
 
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kTM = 128;     // pixels per workgroup tile
 constexpr int kKC = 32;      // K per chunk (one MFMA)
@@ -37,39 +46,78 @@ template <int TN> struct LinGeom {
   static constexpr int WB = TN * kKC * 2;    // bytes of a staged w chunk
 };
 
-// Copies rows [r0, r0 + R) (clamped to n - 1) x K-chunk c of a row-major
-// [n, K] 16-bit matrix into buf: row r at r * 64 bytes, logical 16-byte chunk
-// j at position j ^ ((r >> 1) & 3).  R * 4 slots, 64 per copy instruction.
+// A chunk's x and w pieces held by one lane between its load and its LDS write.
+template <int TN> struct ChunkRegs {
+  u32x4 x[kTM / 64], w[TN / 64];
+};
+
+// Rows [r0, r0 + R) (clamped to n - 1) x K-chunk c of a row-major [n, K]
+// 16-bit matrix, as staged in LDS: row r at r * 64 bytes, logical 16-byte
+// piece j at position j ^ ((r >> 1) & 3).  The R * 4 pieces are numbered by
+// their LDS position (slot = 4 r + position); the 256 lanes take slots
+// 256 j + tid, R / 64 each.
 template <int R>
-__device__ __forceinline__ void stage_rows(const char *src, int64_t n, int K, int64_t r0, int c,
-                                           char *buf, int wave, int lane) {
-  constexpr int NI = R * 4 / 64;
+__device__ __forceinline__ void load_rows(const char *src, int64_t n, int K, int64_t r0, int c,
+                                          int tid, u32x4 *v) {
+  static_assert(R % 64 == 0, "pieces must split evenly over the workgroup");
 #pragma unroll
-  for (int j = 0; j < (NI + 3) / 4; ++j) {
-    const int ins = wave + 4 * j;
-    if (ins < NI) {
-      const int slot = ins * 64 + lane, row = slot >> 2, pos = slot & 3;
-      const int lch = pos ^ ((row >> 1) & 3);
-      const int64_t rr = min(r0 + row, n - 1);
-      const char *p = src + (rr * K + (int64_t)c * kKC + lch * 8) * 2;
-      __builtin_amdgcn_global_load_lds((const void *)p, (lds_void *)(buf + ins * 1024), 16, 0, 0);
-    }
+  for (int j = 0; j < R / 64; ++j) {
+    const int slot = j * kThreads + tid, row = slot >> 2, pos = slot & 3;
+    const int lch = pos ^ ((row >> 1) & 3);
+    const int64_t rr = min(r0 + row, n - 1);
+    v[j] = *(const u32x4 *)(src + (rr * K + (int64_t)c * kKC + lch * 8) * 2);
   }
 }
 
-template <typename T, int TN>
+template <int R>
+__device__ __forceinline__ void write_rows(char *buf, int tid, const u32x4 *v) {
+#pragma unroll
+  for (int j = 0; j < R / 64; ++j) *(u32x4 *)(buf + (j * kThreads + tid) * 16) = v[j];
+}
+
+// Workgroups go to the eight XCDs round-robin by id, each XCD with its own
+// L2.  Tile indices are handed out so that every XCD takes one contiguous
+// range of them: the feature tiles of a pixel tile, which read the same x
+// rows, then mostly share an L2.  A bijection on [0, n).
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t id, uint32_t n) {
+  const uint32_t q = n / 8, r = n % 8, xcd = id % 8;
+  return xcd * q + min(xcd, r) + id / 8;
+}
+
+// Head-planar output: pixels per image (HW), C, head dim (D), images, heads.
+struct PlanarOut {
+  FastDiv hw, c, d;
+  int B, heads;
+};
+
+// Element offset of feature f (a multiple of 4, so f..f+3 stay in one head)
+// within the head-planar output, without the pixel's part.
+__device__ __forceinline__ int64_t planar_feature(uint32_t f, const PlanarOut &po) {
+  const uint32_t t = fast_div(f, po.c), r = f - t * po.c.div;
+  const uint32_t h = fast_div(r, po.d), e = r - h * po.d.div;
+  return ((int64_t)t * po.B * po.heads + h) * ((int64_t)po.hw.div * po.d.div) + e;
+}
+
+// Element offset of pixel m = b*HW + p within the head-planar output.
+__device__ __forceinline__ int64_t planar_pixel(uint32_t m, const PlanarOut &po) {
+  const uint32_t bb = fast_div(m, po.hw), p = m - bb * po.hw.div;
+  return ((int64_t)bb * po.heads * po.hw.div + p) * po.d.div;
+}
+
+template <typename T, int TN, bool PLANAR>
 __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restrict__ x,
                                                                const T *__restrict__ w,
                                                                const T *__restrict__ b,
                                                                T *__restrict__ y, int64_t M,
-                                                               int N, int K, int ntn) {
+                                                               int N, int K, int ntn,
+                                                               PlanarOut po) {
   using G = LinGeom<TN>;
   using vec = typename Mma<T>::vec;
   __shared__ __attribute__((aligned(16))) char xs0[G::XB], ws0[G::WB];
   __shared__ __attribute__((aligned(16))) char xs1[G::XB], ws1[G::WB];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
   const int64_t m0 = (tile / ntn) * kTM;
   const int n0 = (int)(tile % ntn) * TN;
   const int wm = wave >> 1, wn = wave & 1;  // this wave: pixels m0 + 64wm.., features n0 + WN wn..
@@ -106,31 +154,62 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
       for (int fb = 0; fb < G::FB; ++fb) acc[tb][fb] = Mma<T>::run(a[fb], bx[tb], acc[tb][fb]);
   };
   const char *xc = (const char *)x, *wc = (const char *)w;
-  stage_rows<kTM>(xc, M, K, m0, 0, xs0, wave, lane);
-  stage_rows<TN>(wc, N, K, n0, 0, ws0, wave, lane);
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) {
-      stage_rows<kTM>(xc, M, K, m0, c + 1, xs1, wave, lane);
-      stage_rows<TN>(wc, N, K, n0, c + 1, ws1, wave, lane);
-    }
-    compute(xs0, ws0);
+  ChunkRegs<TN> r0, r1;  // chunks c + 1 and c + 2 (alternately) in flight
+  auto load = [&](int c, ChunkRegs<TN> &r) {
+    load_rows<kTM>(xc, M, K, m0, c, tid, r.x);
+    load_rows<TN>(wc, N, K, n0, c, tid, r.w);
+  };
+  auto write = [&](const ChunkRegs<TN> &r, char *xs, char *ws) {
+    write_rows<kTM>(xs, tid, r.x);
+    write_rows<TN>(ws, tid, r.w);
+  };
+  // chunk c sits in LDS buffer c % 2 and, before that, in registers r(c % 2);
+  // the barrier closing step c ends every wave's reads of buffer c % 2 and
+  // publishes chunk c + 1's writes.  The steady-state loop has no branch
+  // inside (chunks c + 1 and c + 3 exist), which keeps the compiler's waits
+  // for the loads exact; the last steps follow it.
+  auto step = [&](int c, const char *xs, const char *ws, char *xn, char *wn2,
+                  ChunkRegs<TN> &rn) {
+    compute(xs, ws);
+    if (c + 1 < nchunks) write(rn, xn, wn2);
+    if (c + 3 < nchunks) load(c + 3, rn);
     __syncthreads();
-    if (c + 1 >= nchunks) break;
-    if (c + 2 < nchunks) {
-      stage_rows<kTM>(xc, M, K, m0, c + 2, xs0, wave, lane);
-      stage_rows<TN>(wc, N, K, n0, c + 2, ws0, wave, lane);
-    }
+  };
+  load(0, r0);
+  if (nchunks > 1) load(1, r1);
+  write(r0, xs0, ws0);
+  if (nchunks > 2) load(2, r0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 4 < nchunks; c += 2) {
+    compute(xs0, ws0);
+    write(r1, xs1, ws1);
+    load(c + 3, r1);
+    __syncthreads();
     compute(xs1, ws1);
+    write(r0, xs0, ws0);
+    load(c + 4, r0);
     __syncthreads();
   }
+  // at most four chunks remain, the first in buffer 0
+  if (c < nchunks) step(c, xs0, ws0, xs1, ws1, r1);
+  if (c + 1 < nchunks) step(c + 1, xs1, ws1, xs0, ws0, r0);
+  if (c + 2 < nchunks) step(c + 2, xs0, ws0, xs1, ws1, r1);
+  if (c + 3 < nchunks) step(c + 3, xs1, ws1, xs0, ws0, r0);
 
   // lane (g, ql) holds features f..f+3 of pixel m for each (tb, fb)
   typedef __attribute__((ext_vector_type(4))) T vec4;
+  int64_t fofs[G::FB];  // planar: the features' part of the output offset
+  if constexpr (PLANAR) {
+#pragma unroll
+    for (int fb = 0; fb < G::FB; ++fb)
+      fofs[fb] = planar_feature((uint32_t)min(n0 + wn * G::WN + fb * 16 + 4 * g, N - 4), po);
+  }
 #pragma unroll
   for (int tb = 0; tb < G::TB; ++tb) {
     const int64_t m = m0 + wm * 64 + tb * 16 + ql;
     if (m >= M) continue;
+    const int64_t mofs = PLANAR ? planar_pixel((uint32_t)m, po) : 0;
 #pragma unroll
     for (int fb = 0; fb < G::FB; ++fb) {
       const int f = n0 + wn * G::WN + fb * 16 + 4 * g;
@@ -138,17 +217,19 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
       vec4 r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = static_cast<T>(acc[tb][fb][i]);
-      *(u32x2 *)(y + m * N + f) = __builtin_bit_cast(u32x2, r);
+      T *dst = PLANAR ? y + fofs[fb] + mofs : y + m * N + f;
+      *(u32x2 *)dst = __builtin_bit_cast(u32x2, r);
     }
   }
 }
 
 // fp32: one lane per (pixel, 4 features), K-loop in fp32 FMA.
+template <bool PLANAR>
 __global__ __launch_bounds__(kThreads) void linear_fma_kernel(const float *__restrict__ x,
                                                               const float *__restrict__ w,
                                                               const float *__restrict__ b,
                                                               float *__restrict__ y, int64_t M,
-                                                              int N, int K) {
+                                                              int N, int K, PlanarOut po) {
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int nq = N / 4;
   if (t >= M * nq) return;
@@ -163,26 +244,57 @@ __global__ __launch_bounds__(kThreads) void linear_fma_kernel(const float *__res
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(xv, w[(int64_t)(f + i) * K + kk], acc[i]);
   }
+  float *dst = PLANAR ? y + planar_pixel((uint32_t)m, po) + planar_feature((uint32_t)f, po)
+                      : y + m * N + f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) y[m * N + f + i] = acc[i];
+  for (int i = 0; i < 4; ++i) dst[i] = acc[i];
+}
+
+hipError_t launch_fma(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
+                      int K, const PlanarOut *po, hipStream_t st) {
+  const int64_t work = M * (N / 4), blocks = (work + kThreads - 1) / kThreads;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
+  if (po != nullptr)
+    linear_fma_kernel<true><<<grid, kThreads, 0, st>>>((const float *)x, (const float *)w,
+                                                       (const float *)b, (float *)y, M, N, K,
+                                                       *po);
+  else
+    linear_fma_kernel<false><<<grid, kThreads, 0, st>>>((const float *)x, (const float *)w,
+                                                        (const float *)b, (float *)y, M, N, K,
+                                                        PlanarOut{});
+  return hipGetLastError();
 }
 
 template <typename T, int TN>
 hipError_t launch_mfma(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
-                       int K, hipStream_t st) {
+                       int K, const PlanarOut *po, hipStream_t st) {
   const int64_t ntm = (M + kTM - 1) / kTM, ntn = (N + TN - 1) / TN;
   if (ntm * ntn > INT_MAX) return hipErrorInvalidConfiguration;
-  linear_mfma_kernel<T, TN><<<dim3((unsigned)(ntm * ntn)), kThreads, 0, st>>>(
-      (const T *)x, (const T *)w, (const T *)b, (T *)y, M, N, K, (int)ntn);
+  const dim3 grid((unsigned)(ntm * ntn));
+  if (po != nullptr)
+    linear_mfma_kernel<T, TN, true><<<grid, kThreads, 0, st>>>(
+        (const T *)x, (const T *)w, (const T *)b, (T *)y, M, N, K, (int)ntn, *po);
+  else
+    linear_mfma_kernel<T, TN, false><<<grid, kThreads, 0, st>>>(
+        (const T *)x, (const T *)w, (const T *)b, (T *)y, M, N, K, (int)ntn, PlanarOut{});
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_tn(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
-                     int K, hipStream_t st) {
-  // 128-feature tiles when they divide N, else 64 (at most one ragged tile)
-  if (N % 128 == 0) return launch_mfma<T, 128>(x, w, b, y, M, N, K, st);
-  return launch_mfma<T, 64>(x, w, b, y, M, N, K, st);
+                     int K, const PlanarOut *po, hipStream_t st) {
+  // N <= 192: one tile across all features (N rounded up to a multiple of
+  // 64), so that x is read once; wider N: 128-feature tiles when they divide
+  // N, else 64 (one ragged tile at most).  Wider tiles need more registers
+  // than two waves per SIMD allow, which costs more than the x re-reads
+  // (mostly L2 hits: the feature tiles of a pixel tile share an XCD).
+  const int tn = N <= 192 ? (N + 63) / 64 * 64 : N % 128 == 0 ? 128 : 64;
+  switch (tn) {
+    case 192: return launch_mfma<T, 192>(x, w, b, y, M, N, K, po, st);
+    case 128: return launch_mfma<T, 128>(x, w, b, y, M, N, K, po, st);
+    default: return launch_mfma<T, 64>(x, w, b, y, M, N, K, po, st);
+  }
 }
 
 }  // namespace
@@ -192,15 +304,28 @@ bool linear_supported(int N, int K) { return N % 16 == 0 && K % kKC == 0; }
 hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
                          int K, na2d_dtype_t dt, hipStream_t st) {
   switch (dt) {
-    case NA2D_DTYPE_BF16: return launch_tn<__bf16>(x, w, b, y, M, N, K, st);
-    case NA2D_DTYPE_F16: return launch_tn<_Float16>(x, w, b, y, M, N, K, st);
-    case NA2D_DTYPE_F32: {
-      const int64_t work = M * (N / 4), blocks = (work + kThreads - 1) / kThreads;
-      if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
-      linear_fma_kernel<<<dim3((unsigned)blocks), kThreads, 0, st>>>(
-          (const float *)x, (const float *)w, (const float *)b, (float *)y, M, N, K);
-      return hipGetLastError();
-    }
+    case NA2D_DTYPE_BF16: return launch_tn<__bf16>(x, w, b, y, M, N, K, nullptr, st);
+    case NA2D_DTYPE_F16: return launch_tn<_Float16>(x, w, b, y, M, N, K, nullptr, st);
+    case NA2D_DTYPE_F32: return launch_fma(x, w, b, y, M, N, K, nullptr, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool linear_planar_supported(int64_t pixels, int C, int heads) {
+  // pixel and feature indices in 32 bits; 4-feature groups within one head
+  return pixels < (int64_t(1) << 31) && C % heads == 0 && (C / heads) % 4 == 0 &&
+         linear_supported(3 * C, C);
+}
+
+hipError_t launch_linear_qkv_planar(const void *x, const void *w, const void *b, void *y, int B,
+                                    int HW, int C, int heads, na2d_dtype_t dt, hipStream_t st) {
+  const PlanarOut po{make_fastdiv((uint32_t)HW), make_fastdiv((uint32_t)C),
+                     make_fastdiv((uint32_t)(C / heads)), B, heads};
+  const int64_t M = (int64_t)B * HW;
+  switch (dt) {
+    case NA2D_DTYPE_BF16: return launch_tn<__bf16>(x, w, b, y, M, 3 * C, C, &po, st);
+    case NA2D_DTYPE_F16: return launch_tn<_Float16>(x, w, b, y, M, 3 * C, C, &po, st);
+    case NA2D_DTYPE_F32: return launch_fma(x, w, b, y, M, 3 * C, C, &po, st);
   }
   return hipErrorInvalidValue;
 }
