@@ -60,14 +60,16 @@ BLOCK_WORKLOADS = {
     "block_56": I.BLOCK_SWEEP[0], "block_28": I.BLOCK_SWEEP[1],
     "block_14": I.BLOCK_SWEEP[2], "block_7": I.BLOCK_SWEEP[3],
 }
-BACKWARD_SOURCES = ["vision_transformer_local_amd/csrc/na2d_backward.hip",
-                    "vision_transformer_local_amd/csrc/na2d_internal.h"]
-KERNEL_SOURCES = ["vision_transformer_local_amd/csrc/na2d_mfma.hip",
-                  "vision_transformer_local_amd/csrc/na2d_linear.hip",
-                  "vision_transformer_local_amd/csrc/na2d_dense.hip",
-                  "vision_transformer_local_amd/csrc/na2d_mfma_common.h",
-                  "vision_transformer_local_amd/csrc/na2d_scalar.hip",
-                  "vision_transformer_local_amd/csrc/na2d_internal.h"]
+# Kernel sources per measured family: a committed counter summary is used
+# only while the sources of its family are unchanged.
+_CSRC = "vision_transformer_local_amd/csrc/"
+_SHARED = [_CSRC + "na2d_mfma_common.h", _CSRC + "na2d_internal.h"]
+_FORWARD = [_CSRC + f for f in ("na2d_mfma.hip", "na2d_dense.hip", "na2d_scalar.hip")] + _SHARED
+SOURCE_FAMILIES = {
+    "forward": _FORWARD,
+    "block": [_CSRC + "na2d_linear.hip", _CSRC + "na2d_block.hip"] + _FORWARD,
+    "backward": [_CSRC + "na2d_backward.hip", _CSRC + "na2d_backward_mfma.hip"] + _SHARED,
+}
 
 
 def elem_size(dtype: str) -> int:
@@ -92,7 +94,7 @@ def backward_algorithmic_bytes(p) -> int:
 
 def kernel_source_hash(which: str = "forward") -> str:
     h = hashlib.sha256()
-    for rel in BACKWARD_SOURCES if which == "backward" else KERNEL_SOURCES:
+    for rel in SOURCE_FAMILIES[which]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -106,8 +108,8 @@ def measured_traffic(workload: str, path: str):
         return None
     with open(fn) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash(
-            "backward" if path == "backward" else "forward"):
+    family = path if path in ("backward", "block") else "forward"
+    if rec.get("kernel_source_hash") != kernel_source_hash(family):
         return None  # kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
 
@@ -398,6 +400,15 @@ def block_algorithmic_bytes(p) -> int:
     return (2 * M * p.C + 4 * p.C * p.C + 4 * p.C + p.heads * side * side) * s
 
 
+def na2d_block_fused(p):
+    """Whether the library's automatic plan runs this block as one kernel
+    (mirrors the fused kernel's coverage: bf16/fp16, C = 64 in 2 heads,
+    k in {3, 5, 7}, no dilation, no padding)."""
+    return (p.dtype in ("bf16", "f16") and p.C == 64 and p.heads == 2 and
+            p.kernel_size in (3, 5, 7) and p.dilation == 1 and
+            min(p.H, p.W) >= p.kernel_size)
+
+
 def bench_block(args, dev, L):
     """One step = the attention block (three launches) over the workload."""
     import numpy as np
@@ -418,11 +429,16 @@ def bench_block(args, dev, L):
     dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
     wq, bq, rp, wo, bo = params
 
+    # --path fused: the library's choice (one fused kernel where it applies);
+    # --path unfused: the three launches
+    plan = na2d.BLOCK_UNFUSED if args.path == "unfused" else na2d.BLOCK_AUTO
+
     def launch(i, stream):
         x, y, ws = reps[i % R]
-        r = L.na2d_block_forward(x.data_ptr(), wq.data_ptr(), bq.data_ptr(), rp.data_ptr(),
-                                 wo.data_ptr(), bo.data_ptr(), y.data_ptr(), ws.data_ptr(), wsb,
-                                 B, H, W, C, p.heads, ks, dil, dt_code, ctypes.c_void_p(stream))
+        r = L.na2d_block_forward_path(x.data_ptr(), wq.data_ptr(), bq.data_ptr(), rp.data_ptr(),
+                                      wo.data_ptr(), bo.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                                      wsb, B, H, W, C, p.heads, ks, dil, dt_code, plan,
+                                      ctypes.c_void_p(stream))
         if r != 0:
             raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
 
@@ -456,14 +472,16 @@ def bench_block(args, dev, L):
         "data": "synthetic (seeded N(0,1) features, N(0,1/C) weights, 0.5*N(0,1) biases)",
         "config": {"workload": "%s block: %s" % (args.workload, p.describe()),
                    "B": B, "H": H, "W": W, "C": C, "heads": p.heads, "kernel_size": ks,
-                   "dilation": dil, "path": "block", "timing": args.mode, "replicas": R},
+                   "dilation": dil, "path": "block_unfused" if plan == na2d.BLOCK_UNFUSED else
+                   ("block_fused" if na2d_block_fused(p) else "block_unfused"),
+                   "timing": args.mode, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload, "block")},
         "kernel_ms": kernel_ms,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("block"),
     }
     print(json.dumps(rec), flush=True)
     return 0

@@ -176,9 +176,10 @@ size_t na2d_block_workspace_size(int B, int H, int W, int C, int heads, na2d_dty
  *   rpb         [heads, 2k-1, 2k-1] or NULL
  *   workspace   >= na2d_block_workspace_size(...) bytes of device scratch;
  *               its content on return is unspecified
- * Three kernel launches on `stream` (projection, attention reading q, k, v
- * straight out of the projection's rows, projection).  y and workspace must
- * overlap none of the inputs nor each other.  D = C / heads != 32 returns
+ * On `stream`: one fused kernel where it applies (see na2d_block_path_t),
+ * else three launches (the q|k|v projection written as three dense
+ * [B, heads, H, W, D] tensors, the attention, the output projection).  y and
+ * workspace must overlap none of the inputs nor each other.  D = C / heads != 32 returns
  * NA2D_ERROR_NOT_SUPPORTED; other rules as na2d_forward_padded.
  */
 na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b_qkv,
@@ -186,6 +187,30 @@ na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b
                                  void *y, void *workspace, size_t workspace_bytes, int B, int H,
                                  int W, int C, int heads, int kernel_size, int dilation,
                                  na2d_dtype_t dtype, hipStream_t stream);
+
+/* Kernel plan of the attention block. */
+typedef enum {
+    NA2D_BLOCK_AUTO = 0,     /* the fused kernel where it applies, else three launches */
+    NA2D_BLOCK_UNFUSED = 1,  /* projection, attention, projection: three launches */
+    NA2D_BLOCK_FUSED = 2     /* one kernel: bf16/fp16, C = 64 in 2 heads, k in {3, 5, 7},
+                                dilation 1, H, W >= k (no padding), H*W <= 2^24;
+                                elsewhere NA2D_ERROR_NOT_SUPPORTED */
+} na2d_block_path_t;
+
+/*
+ * na2d_block_forward with an explicit kernel plan.  The fused kernel keeps
+ * q, k, v and the attention output on chip (each rounded to `dtype` as the
+ * three-launch path stores them) and reads no workspace: with
+ * NA2D_BLOCK_FUSED, workspace may be NULL and workspace_bytes 0.  AUTO and
+ * UNFUSED validate the workspace as na2d_block_forward does, whichever path
+ * then runs.  Invalid `path` returns NA2D_ERROR_INVALID_VALUE.
+ */
+na2d_status_t na2d_block_forward_path(const void *x, const void *w_qkv, const void *b_qkv,
+                                      const void *rpb, const void *w_out, const void *b_out,
+                                      void *y, void *workspace, size_t workspace_bytes, int B,
+                                      int H, int W, int C, int heads, int kernel_size,
+                                      int dilation, na2d_dtype_t dtype, na2d_block_path_t path,
+                                      hipStream_t stream);
 
 /*
  * Unfused step 1 (the blog's natten2dqkrpb): attn[b,h,i,j,n] =

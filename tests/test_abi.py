@@ -424,3 +424,34 @@ def test_block_pointer_and_workspace_rules():
         p = list(far)
         p[a] = ctypes.c_void_p(p[b].value)
         assert _block(L, p, args) == INVALID
+
+
+def _block_path(L, ptrs, args, path, ws_bytes=1 << 40):
+    return L.na2d_block_forward_path(*ptrs, ws_bytes, *args, path, S)
+
+
+def test_block_path_rules():
+    L = na2d.lib()
+    far = [ctypes.c_void_p((1 << 41) * (i + 1)) for i in range(8)]
+    fusable = (2, 7, 9, 64, 2, 7, 1, BF16)
+    assert _block_path(L, far, fusable, 3) == INVALID
+    assert _block_path(L, far, fusable, -1) == INVALID
+    # forced fused on what the fused kernel does not cover
+    for args in ((2, 7, 9, 64, 2, 7, 2, BF16),     # dilation
+                 (2, 5, 9, 64, 2, 7, 1, BF16),     # padded map
+                 (2, 7, 9, 128, 4, 7, 1, BF16),    # C = 128
+                 (2, 9, 9, 64, 2, 9, 1, BF16),     # k = 9
+                 (2, 7, 9, 64, 2, 7, 1, F32)):
+        assert _block_path(L, far, args, na2d.BLOCK_FUSED) == UNSUPPORTED
+    # the workspace is required unless the fused kernel is forced
+    p = list(far)
+    p[7] = NULL
+    for path in (na2d.BLOCK_AUTO, na2d.BLOCK_UNFUSED):
+        assert _block_path(L, p, fusable, path, 0) == INVALID
+    # forced fused still checks the other pointers and overlaps
+    p[6] = NULL
+    assert _block_path(L, p, fusable, na2d.BLOCK_FUSED, 0) == INVALID
+    p = list(far)
+    p[7] = NULL
+    p[6] = ctypes.c_void_p(far[0].value)  # y over x
+    assert _block_path(L, p, fusable, na2d.BLOCK_FUSED, 0) == INVALID

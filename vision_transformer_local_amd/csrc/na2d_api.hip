@@ -240,7 +240,20 @@ na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b
                                  void *y, void *workspace, size_t workspace_bytes, int B, int H,
                                  int W, int C, int heads, int kernel_size, int dilation,
                                  na2d_dtype_t dtype, hipStream_t stream) {
+  return na2d_block_forward_path(x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace,
+                                 workspace_bytes, B, H, W, C, heads, kernel_size, dilation, dtype,
+                                 NA2D_BLOCK_AUTO, stream);
+}
+
+na2d_status_t na2d_block_forward_path(const void *x, const void *w_qkv, const void *b_qkv,
+                                      const void *rpb, const void *w_out, const void *b_out,
+                                      void *y, void *workspace, size_t workspace_bytes, int B,
+                                      int H, int W, int C, int heads, int kernel_size,
+                                      int dilation, na2d_dtype_t dtype, na2d_block_path_t path,
+                                      hipStream_t stream) {
   if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  if (path != NA2D_BLOCK_AUTO && path != NA2D_BLOCK_UNFUSED && path != NA2D_BLOCK_FUSED)
+    return NA2D_ERROR_INVALID_VALUE;
   if (B < 1 || H < 1 || W < 1 || C < 1 || heads < 1 || kernel_size < 1 || dilation < 1)
     return NA2D_ERROR_INVALID_VALUE;
   if (C % heads != 0) return NA2D_ERROR_INVALID_VALUE;
@@ -258,13 +271,19 @@ na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b
   s.n_query = s.n_query / ((int64_t)Hp * Wp) * ((int64_t)H * W);
   const int64_t M = (int64_t)B * H * W;
   if (M > kMaxElems / (4 * (int64_t)C)) return NA2D_ERROR_INVALID_VALUE;
-  if (!x || !w_qkv || !w_out || !y || !workspace) return NA2D_ERROR_INVALID_VALUE;
+  // the fused kernel needs no workspace: a forced fused call may pass none
+  const bool fused = path != NA2D_BLOCK_UNFUSED &&
+                     na2d::block_fused_supported(H, W, C, heads, kernel_size, dilation, dtype);
+  if (path == NA2D_BLOCK_FUSED && !fused) return NA2D_ERROR_NOT_SUPPORTED;
+  const bool need_ws = path != NA2D_BLOCK_FUSED;
+  if (!x || !w_qkv || !w_out || !y || (need_ws && !workspace)) return NA2D_ERROR_INVALID_VALUE;
   const void *ptrs[] = {x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
   const int64_t eb = elem_bytes(dtype);
   const size_t need = na2d_block_workspace_size(B, H, W, C, heads, dtype);
-  if (need == 0 || workspace_bytes < need) return NA2D_ERROR_INVALID_VALUE;
+  if (need == 0) return NA2D_ERROR_INVALID_VALUE;
+  if (need_ws && workspace_bytes < need) return NA2D_ERROR_INVALID_VALUE;
   const int64_t side = 2 * kernel_size - 1;
   struct Span {
     const void *p;
@@ -273,11 +292,17 @@ na2d_status_t na2d_block_forward(const void *x, const void *w_qkv, const void *b
   const Span read[] = {{x, M * C * eb},          {w_qkv, 3LL * C * C * eb},
                        {b_qkv, 3LL * C * eb},    {rpb, heads * side * side * eb},
                        {w_out, (int64_t)C * C * eb}, {b_out, C * eb}};
-  const Span written[] = {{y, M * C * eb}, {workspace, (int64_t)need}};
+  // (the workspace is validated whenever the three-launch path may run, also
+  // when the automatic choice then takes the fused kernel)
+  const int64_t wsn = need_ws ? (int64_t)need : 0;
+  const Span written[] = {{y, M * C * eb}, {workspace, wsn}};
   for (const Span &wr : written)
     for (const Span &rd : read)
       if (overlaps(wr.p, wr.n, rd.p, rd.n)) return NA2D_ERROR_INVALID_VALUE;
-  if (overlaps(y, M * C * eb, workspace, (int64_t)need)) return NA2D_ERROR_INVALID_VALUE;
+  if (overlaps(y, M * C * eb, workspace, wsn)) return NA2D_ERROR_INVALID_VALUE;
+  if (fused)
+    return from_hip(na2d::launch_block_fused(x, w_qkv, b_qkv, rpb, w_out, b_out, y, B, H, W,
+                                             kernel_size, dtype, stream));
   if (!na2d::linear_planar_supported(M, C, heads) || !na2d::linear_supported(C, C))
     return NA2D_ERROR_NOT_SUPPORTED;
   // 1. q, k, v = x w_qkv^T + b_qkv, written as three dense [B, heads, H, W, D]

@@ -157,6 +157,12 @@ hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s
 bool linear_supported(int N, int K);
 hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
                          int K, na2d_dtype_t dt, hipStream_t st);
+// The attention block in one kernel (projections, attention, projection):
+// C = 64 in 2 heads, k in {3, 5, 7}, no dilation, no padding, bf16 / fp16.
+bool block_fused_supported(int H, int W, int C, int heads, int ks, int dil, na2d_dtype_t dt);
+hipError_t launch_block_fused(const void *x, const void *w_qkv, const void *b_qkv,
+                              const void *rpb, const void *w_out, const void *b_out, void *y,
+                              int B, int H, int W, int ks, na2d_dtype_t dt, hipStream_t st);
 // The q|k|v projection (w[3C, C]) of B*HW pixels written head-planar: three
 // dense [B, heads, H, W, C/heads] tensors at y, y + B*HW*C, y + 2*B*HW*C.
 bool linear_planar_supported(int64_t pixels, int C, int heads);

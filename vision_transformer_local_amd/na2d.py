@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.na2d_block_workspace_size.argtypes = [i] * 6
         L.na2d_block_forward.restype = i
         L.na2d_block_forward.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 8 + [vp]
+        L.na2d_block_forward_path.restype = i
+        L.na2d_block_forward_path.argtypes = [vp] * 8 + [ctypes.c_size_t] + [i] * 9 + [vp]
         L.na2d_qkrpb.restype = i
         L.na2d_qkrpb.argtypes = [vp] * 4 + [i] * 8 + [vp]
         L.na2d_softmax.restype = i
@@ -356,12 +358,21 @@ def na2d_block_workspace_size(B, H, W, C, heads, dtype) -> int:
     return int(lib().na2d_block_workspace_size(B, H, W, C, heads, _DTYPE_CODES[dtype]))
 
 
+# na2d_block_path_t
+BLOCK_AUTO, BLOCK_UNFUSED, BLOCK_FUSED = 0, 1, 2
+_BLOCK_PATHS = {"auto": BLOCK_AUTO, "unfused": BLOCK_UNFUSED, "fused": BLOCK_FUSED}
+
+
 def na2d_block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace, heads: int,
-                       kernel_size: int, dilation: int):
+                       kernel_size: int, dilation: int, path: str = "auto"):
     """The attention block on channels-last features x [B, H, W, C] into y:
     q/k/v projection, per-head NA (maps below k*d padded as the layer does),
     output projection.  workspace: a uint8 device tensor of at least
-    ``na2d_block_workspace_size`` bytes."""
+    ``na2d_block_workspace_size`` bytes (may be None with path="fused").
+    path: "auto" (na2d_block_forward), "unfused" or "fused"
+    (na2d_block_forward_path)."""
+    if path not in _BLOCK_PATHS:
+        raise ValueError("path must be one of %s" % sorted(_BLOCK_PATHS))
     if x.dim() != 4:
         raise ValueError("x must be [B, H, W, C]")
     B, H, W, C = (int(d) for d in x.shape)
@@ -377,22 +388,31 @@ def na2d_block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, y, workspace, heads: 
     side = 2 * kernel_size - 1
     if rpb is not None:
         _need(rpb, "rpb", dt, (heads, side, side))
-    _need(workspace, "workspace", torch.uint8)
-    st = lib().na2d_block_forward(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(rpb), _ptr(w_out),
-                                  _ptr(b_out), _ptr(y), _ptr(workspace), workspace.numel(), B, H,
-                                  W, C, heads, int(kernel_size), int(dilation),
-                                  _DTYPE_CODES[dt], _stream(x))
-    _check(st, "na2d_block_forward")
+    if workspace is not None or path != "fused":
+        _need(workspace, "workspace", torch.uint8)
+    wsn = workspace.numel() if workspace is not None else 0
+    args = (_ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(rpb), _ptr(w_out), _ptr(b_out), _ptr(y),
+            _ptr(workspace), wsn, B, H, W, C, heads, int(kernel_size), int(dilation),
+            _DTYPE_CODES[dt])
+    if path == "auto":
+        st = lib().na2d_block_forward(*args, _stream(x))
+        _check(st, "na2d_block_forward")
+    else:
+        st = lib().na2d_block_forward_path(*args, _BLOCK_PATHS[path], _stream(x))
+        _check(st, "na2d_block_forward_path")
     return y
 
 
 def block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, heads: int, kernel_size: int,
-                  dilation: int):
-    """Allocating ``na2d_block_forward`` (y and the workspace)."""
+                  dilation: int, path: str = "auto"):
+    """Allocating ``na2d_block_forward`` (y and, unless path="fused", the
+    workspace)."""
     B, H, W, C = (int(d) for d in x.shape)
-    n = na2d_block_workspace_size(B, H, W, C, heads, x.dtype)
-    if n == 0:
-        raise Na2dError(INVALID_VALUE, "na2d_block_workspace_size: invalid problem")
-    ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    ws = None
+    if path != "fused":
+        n = na2d_block_workspace_size(B, H, W, C, heads, x.dtype)
+        if n == 0:
+            raise Na2dError(INVALID_VALUE, "na2d_block_workspace_size: invalid problem")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
     return na2d_block_forward(x, w_qkv, b_qkv, rpb, w_out, b_out, torch.empty_like(x), ws, heads,
-                              kernel_size, dilation)
+                              kernel_size, dilation, path)
