@@ -95,6 +95,19 @@ __device__ __forceinline__ int table_entry(int e) {
 // over all banks.
 __device__ __forceinline__ int wpiece(int r, int c) { return r * 128 + 16 * (c ^ (r & 7)); }
 
+// A lane reads piece 4kk + g of row r0 + ql of an operand (r0 a multiple of
+// 8, so that r & 7 = ql & 7): wpiece(r0 + ql, 4kk + g) = r0 * 128 + wl[kk]
+// with the two per-lane offsets below (wl[1] = wl[0] ^ 64).  Operand reads
+// then cost one register each plus an immediate offset.
+struct WeightLane {
+  int wl0, wl1;
+};
+
+__device__ __forceinline__ WeightLane weight_lane(int ql, int g) {
+  const int wl0 = ql * 128 + 16 * (g ^ (ql & 3)) + 64 * ((ql >> 2) & 1);
+  return WeightLane{wl0, wl0 ^ 64};
+}
+
 // Compute units of the current device (queried once per device).
 int block_device_cus() {
   static int cache[64];
@@ -344,6 +357,7 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
     }
 
   const char *wq = wts, *wk = wts + G::WMAT, *wv = wts + 2 * G::WMAT, *wo = wts + 3 * G::WMAT;
+  const WeightLane wl = weight_lane(ql, g);
   for (int bi = b0; bi < b1; ++bi) {
     const BlockPos p = pos;
     __syncthreads();  // weights and biases written (first block); previous block done
@@ -354,10 +368,12 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
       f32x4 acc[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        // operands of one channel block at a time (bounds the registers)
+        asm volatile("" ::: "memory");
         acc[c] = *(const f32x4 *)(bias + 16 * c + 4 * g);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          acc[c] = Mma<T>::run(*(const vec *)(wq + wpiece(16 * c + ql, 4 * kk + g)),
+          acc[c] = Mma<T>::run(*(const vec *)(wq + 16 * c * 128 + (kk ? wl.wl1 : wl.wl0)),
                                __builtin_bit_cast(vec, xo.query[kk]), acc[c]);
       }
 #pragma unroll
@@ -376,31 +392,33 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
       }
       // K^T, V^T of head h for this wave's halo rows
       {
-        vec ak[2][2], av[2][2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            ak[c][kk] = *(const vec *)(wk + wpiece(32 * h + 16 * c + ql, 4 * kk + g));
-            av[c][kk] = *(const vec *)(wv + wpiece(32 * h + 16 * c + ql, 4 * kk + g));
-          }
         const int swz = (ql >> 1) & 3;
 #pragma unroll
-        for (int j = 0; j < G::RPW; ++j) {
-          const int r = wave + j * G::WAVES;
-          if (r < G::HR) {
-            char *kp = kbuf + (r * G::HC + ql) * 64;
-            char *vp = vbuf + (r * G::HC + ql) * 64;
+        for (int c = 0; c < 2; ++c) {
+          // the weights of one 16-channel block of K and of V at a time
+          asm volatile("" ::: "memory");
+          vec ak[2], av[2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              f32x4 ka = *(const f32x4 *)(bias + kC + 32 * h + 16 * c + 4 * g);
-              f32x4 va = *(const f32x4 *)(bias + 2 * kC + 32 * h + 16 * c + 4 * g);
+          for (int kk = 0; kk < 2; ++kk) {
+            const int off = (32 * h + 16 * c) * 128 + (kk ? wl.wl1 : wl.wl0);
+            ak[kk] = *(const vec *)(wk + off);
+            av[kk] = *(const vec *)(wv + off);
+          }
+          const f32x4 kb0 = *(const f32x4 *)(bias + kC + 32 * h + 16 * c + 4 * g);
+          const f32x4 vb0 = *(const f32x4 *)(bias + 2 * kC + 32 * h + 16 * c + 4 * g);
+#pragma unroll
+          for (int j = 0; j < G::RPW; ++j) {
+            const int r = wave + j * G::WAVES;
+            if (r < G::HR) {
+              f32x4 ka = kb0, va = vb0;
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
                 const vec xb = __builtin_bit_cast(vec, xo.halo[j][kk]);
-                ka = Mma<T>::run(ak[c][kk], xb, ka);
-                va = Mma<T>::run(av[c][kk], xb, va);
+                ka = Mma<T>::run(ak[kk], xb, ka);
+                va = Mma<T>::run(av[kk], xb, va);
               }
+              char *kp = kbuf + (r * G::HC + ql) * 64;
+              char *vp = vbuf + (r * G::HC + ql) * 64;
               // K: piece g holds channels 4g.. (c = 0) and 16+4g.. (c = 1)
               *(u32x2 *)(kp + 16 * (g ^ swz) + 8 * c) = pack4<T>(ka);
               // V: channels 16c + 4g.. sit in piece 2c + g/2, half g&1
@@ -431,10 +449,11 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
       T *dst = y + p.img + ((int64_t)qr * W + qc) * kC + 4 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
+        asm volatile("" ::: "memory");
         f32x4 acc = *(const f32x4 *)(bias + 3 * kC + 16 * c + 4 * g);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc = Mma<T>::run(*(const vec *)(wo + wpiece(16 * c + ql, 4 * h + g)),
+          acc = Mma<T>::run(*(const vec *)(wo + 16 * c * 128 + (h ? wl.wl1 : wl.wl0)),
                             __builtin_bit_cast(vec, ctx[h]), acc);
         if (store) *(u32x2 *)(dst + 16 * c) = pack4<T>(acc);
       }
