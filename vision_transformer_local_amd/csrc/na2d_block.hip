@@ -7,7 +7,8 @@
 // channels in 2 heads of 32, k in {3, 5, 7}, no dilation, maps of at least
 // k x k (no padding); other blocks take the three-launch path.
 //
-// Per block of RY x 8 queries of one image, with both heads:
+// Per block of 16 x 8 queries of one image (four waves, each with two 2 x 8
+// query tiles), with both heads:
 //   * x is read straight into MFMA operands (lane (g, i) holds 8 channels of
 //     pixel i), never staged: the halo rows of the block for the key/value
 //     projection, the block's own pixels for the query projection.
@@ -22,7 +23,7 @@
 //     the block's halo repeat the last map row -- finite values that only ever
 //     meet masked scores) are projected into LDS, K in order pi, V in channel
 //     order, 16-byte pieces XOR-swizzled by column; then each wave runs the
-//     attention of its 2 x 8 query tile against them as the general matrix-core
+//     attention of its two query tiles against them as the general matrix-core
 //     kernel does (scores transposed, bias and mask as the accumulator input,
 //     V^T read with ds_read_b64_tr_b16, softmax denominator from a product with
 //     ones over the 16-bit weights).
@@ -30,8 +31,10 @@
 //     per head and feed the output projection directly: Wo sits in LDS with
 //     its input channels permuted to pi.  y rows are written once.
 // The weights (q, k, v, out: 32 KB) live in LDS for the life of a persistent
-// workgroup; one head's K and V halo (44 KB at RY = 16) plus the bias table
-// leave room for two workgroups per compute unit.
+// workgroup; one head's K and V halo (44 KB) plus the bias table leave room
+// for two workgroups per compute unit, 2 waves per SIMD with 256 registers
+// each.  Each weight operand read from LDS serves two query tiles (the query
+// and output projections) or about six halo rows (key/value projection).
 #include "na2d_mfma_common.h"
 
 #include <limits.h>
@@ -49,9 +52,10 @@ constexpr int kC = 64;  // channels: 2 heads of 32
 
 template <int KS, int RY> struct BlockGeom {
   static constexpr int R = KS / 2;
-  static constexpr int TY = 2, TX = 8;          // query tile (16 queries, one wave)
+  static constexpr int TY = 2, TX = 8;          // query tile (16 queries)
+  static constexpr int TPW = 2;                 // tiles per wave (stacked vertically)
   static constexpr int RX = TX;                 // block columns: one tile column
-  static constexpr int WAVES = RY / TY, THREADS = WAVES * 64;
+  static constexpr int WAVES = RY / (TY * TPW), THREADS = WAVES * 64;
   static constexpr int NB = TY + KS - 1;        // key rows of a tile
   static constexpr int HR = RY + KS - 1;        // staged key rows
   static constexpr int HC = 16;                 // staged key columns
@@ -69,7 +73,7 @@ template <int KS, int RY> struct BlockGeom {
   static constexpr int LDS = 4 * WMAT + 2 * KVB + NTAB * 4 + 4 * kC * 4;
   static_assert(TX + KS - 1 <= HC, "key columns do not cover the tile");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
-  static_assert(RY % TY == 0, "blocks hold whole tiles");
+  static_assert(RY % (TY * TPW) == 0, "blocks hold whole waves of tiles");
   static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
 };
 
@@ -151,12 +155,19 @@ __device__ __forceinline__ BlockPos block_pos(int id, int H, int W, const FastDi
 // block), channels 8g..8g+7 and 32+8g..32+8g+7.
 template <typename T, int KS, int RY> struct XOps {
   u32x4 halo[BlockGeom<KS, RY>::RPW][2];
-  u32x4 query[2];
+  u32x4 query[BlockGeom<KS, RY>::TPW][2];
 };
 
+// First query row of tile t of this wave.
+template <int KS, int RY>
+__device__ __forceinline__ int tile_row(const BlockPos &p, int wave, int t) {
+  using G = BlockGeom<KS, RY>;
+  return p.y0 + (wave * G::TPW + t) * G::TY;
+}
+
 template <typename T, int KS, int RY>
-__device__ __forceinline__ void load_x(const T *__restrict__ x, const BlockPos &p, int H, int W,
-                                       int wave, int ql, int g, XOps<T, KS, RY> &o) {
+__device__ __forceinline__ void load_halo(const T *__restrict__ x, const BlockPos &p, int H,
+                                          int W, int wave, int ql, int g, XOps<T, KS, RY> &o) {
   using G = BlockGeom<KS, RY>;
   const int hc = min(p.hx0 + ql, W - 1);
 #pragma unroll
@@ -169,11 +180,20 @@ __device__ __forceinline__ void load_x(const T *__restrict__ x, const BlockPos &
       o.halo[j][1] = src[4];
     }
   }
-  const int qr = min(p.y0 + wave * G::TY + ql / G::TX, p.y1 - 1);
+}
+
+template <typename T, int KS, int RY>
+__device__ __forceinline__ void load_query(const T *__restrict__ x, const BlockPos &p, int W,
+                                           int wave, int ql, int g, XOps<T, KS, RY> &o) {
+  using G = BlockGeom<KS, RY>;
   const int qc = min(p.x0 + ql % G::TX, p.x1 - 1);
-  const u32x4 *src = (const u32x4 *)(x + p.img + ((int64_t)qr * W + qc) * kC) + g;
-  o.query[0] = src[0];
-  o.query[1] = src[4];
+#pragma unroll
+  for (int t = 0; t < G::TPW; ++t) {
+    const int qr = min(tile_row<KS, RY>(p, wave, t) + ql / G::TX, p.y1 - 1);
+    const u32x4 *src = (const u32x4 *)(x + p.img + ((int64_t)qr * W + qc) * kC) + g;
+    o.query[t][0] = src[0];
+    o.query[t][1] = src[4];
+  }
 }
 
 template <typename T>
@@ -190,116 +210,140 @@ __device__ __forceinline__ typename Mma<T>::vec join(u32x2 a, u32x2 b) {
   return __builtin_bit_cast(typename Mma<T>::vec, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// One head's attention for this wave's 2 x 8 query tile: out^T of the head,
-// rounded, as the output projection's operand (channels in order pi).
+// One head's attention for this wave's TPW query tiles (2 x 8 queries each,
+// the first starting at row tci0, the next TY rows further): for each, out^T
+// of the head, rounded, as the output projection's operand (channels in order
+// pi).  One interior-or-edge decision covers all the wave's tiles, so that
+// their independent products and softmax steps share straight-line code the
+// compiler can interleave.
 template <typename T, int KS, int RY>
-__device__ __forceinline__ u32x4 attend(const char *kbuf, const char *vbuf, const float *tab,
-                                        typename Mma<T>::vec qv, const BlockPos &p, int H,
-                                        int W, int wave, int lane) {
+__device__ __forceinline__ void attend(const char *kbuf, const char *vbuf, const float *tab,
+                                       const typename Mma<T>::vec (&qv)[BlockGeom<KS, RY>::TPW],
+                                       const BlockPos &p, int H, int W, int tci0, int lane,
+                                       u32x4 (&out)[BlockGeom<KS, RY>::TPW]) {
   using G = BlockGeom<KS, RY>;
   using vec = typename Mma<T>::vec;
-  constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, R = G::R;
+  constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, R = G::R, TPW = G::TPW;
   const int ql = lane & 15, g = lane >> 4;
   const int qy = ql / TX, qx = ql % TX;
-  const int tci0 = p.y0 + wave * TY;
-  const int Y0 = window_start(tci0, H, KS);
-  const int lrow0 = Y0 - p.hy0;  // the tile's key block starts at staged column 0
+  int Y0[TPW], lrow0[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    Y0[t] = window_start(tci0 + t * TY, H, KS);
+    lrow0[t] = Y0[t] - p.hy0;  // the tile's key block starts at staged column 0
+  }
 
   // S^T rows: key (Y0 + a, hx0 + 4g + i) against query ql, i = 0..3
-  const u32x4 *kb = (const u32x4 *)(kbuf + (lrow0 * G::HC + ql) * 64) + (g ^ ((ql >> 1) & 3));
-  f32x4 sc[NB];
-  const bool inner = tci0 >= R && tci0 + TY - 1 + R <= H - 1 && p.x0 >= R &&
+  const int kofs = ql * 64 + 16 * (g ^ ((ql >> 1) & 3));
+  f32x4 sc[TPW][NB];
+  const bool inner = tci0 >= R && tci0 + TPW * TY - 1 + R <= H - 1 && p.x0 >= R &&
                      p.x0 + TX - 1 + R <= W - 1;
   if (inner) {
     const float *tb = tab + (TY - 1 - qy) * G::IW + (TX + 4 * g - qx);
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      f32x4 cin;
+    for (int t = 0; t < TPW; ++t) {
+      const u32x4 *kb = (const u32x4 *)(kbuf + lrow0[t] * G::HC * 64 + kofs);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cin[i] = tb[a * G::IW + i];
-      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * G::HC * 4]), qv, cin);
+      for (int a = 0; a < NB; ++a) {
+        f32x4 cin;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cin[i] = tb[a * G::IW + i];
+        sc[t][a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * G::HC * 4]), qv[t], cin);
+      }
     }
   } else {
-    // key rows TY-1..k-1 of the key block lie inside every query row's window
-    const int ci = min(tci0 + qy, p.y1 - 1), cj = min(p.x0 + qx, p.x1 - 1);
-    const int sy = window_start(ci, H, KS), sx = window_start(cj, W, KS);
-    const int rowrel = Y0 - sy, colrel = p.hx0 + 4 * g - sx;
-    int bidx = G::BOFF + (Y0 - ci + KS - 1) * SIDE + (p.hx0 + 4 * g - cj + KS - 1);
-    asm volatile("" : "+v"(bidx));  // one base register; the reads use immediate offsets
-    const float *bb = tab + bidx;
-    float ccap[4];  // +inf inside the window's columns, -inf outside
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
-      asm volatile("" : "+v"(ccap[i]));
-    }
+    for (int t = 0; t < TPW; ++t) {
+      const u32x4 *kb = (const u32x4 *)(kbuf + lrow0[t] * G::HC * 64 + kofs);
+      // key rows TY-1..k-1 of the key block lie inside every query row's window
+      const int ci = min(tci0 + t * TY + qy, p.y1 - 1), cj = min(p.x0 + qx, p.x1 - 1);
+      const int sy = window_start(ci, H, KS), sx = window_start(cj, W, KS);
+      const int rowrel = Y0[t] - sy, colrel = p.hx0 + 4 * g - sx;
+      int bidx = G::BOFF + (Y0[t] - ci + KS - 1) * SIDE + (p.hx0 + 4 * g - cj + KS - 1);
+      asm volatile("" : "+v"(bidx));  // one base register; the reads use immediate offsets
+      const float *bb = tab + bidx;
+      float ccap[4];  // +inf inside the window's columns, -inf outside
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const bool rtest = !(a >= TY - 1 && a <= KS - 1);
-      float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
-      if (rtest) asm volatile("" : "+v"(rcap));
-      f32x4 cin;
+      for (int i = 0; i < 4; ++i) {
+        ccap[i] = (unsigned)(colrel + i) < (unsigned)KS ? INFINITY : -INFINITY;
+        asm volatile("" : "+v"(ccap[i]));
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        cin[i] = rtest ? fminf(fminf(bb[a * SIDE + i], ccap[i]), rcap)
-                       : fminf(bb[a * SIDE + i], ccap[i]);
-      sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * G::HC * 4]), qv, cin);
+      for (int a = 0; a < NB; ++a) {
+        const bool rtest = !(a >= TY - 1 && a <= KS - 1);
+        float rcap = (unsigned)(rowrel + a) < (unsigned)KS ? INFINITY : -INFINITY;
+        if (rtest) asm volatile("" : "+v"(rcap));
+        f32x4 cin;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cin[i] = rtest ? fminf(fminf(bb[a * SIDE + i], ccap[i]), rcap)
+                         : fminf(bb[a * SIDE + i], ccap[i]);
+        sc[t][a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * G::HC * 4]), qv[t], cin);
+      }
     }
   }
 
   // softmax numerators exp((S - max) / sqrt(D)); the 4 lane groups hold
   // disjoint keys of the same query
   const float c2 = kLog2e / kSqrtD;
-  float mx = -INFINITY;
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+  for (int t = 0; t < TPW; ++t) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
-  const float mc = group_max(mx) * c2;
+    for (int a = 0; a < NB; ++a)
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][a][i]);
+    const float mc = group_max(mx) * c2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t][a][i] = __builtin_amdgcn_exp2f(fmaf(sc[t][a][i], c2, -mc));
+  }
 
   // out^T = V^T . P^T over pairs of key rows; lane (g, 4k + qd) is the source
   // of channels 4qd..4qd+3 (and 16+4qd..) of key column hx0 + 4g + k
   const int vcol = 4 * g + (ql >> 2), qd = ql & 3, vs = (vcol >> 1) & 3;
-  const char *vrow = vbuf + (lrow0 * G::HC + vcol) * 64 + 8 * (qd & 1);
-  const char *va0 = vrow + 16 * ((qd >> 1) ^ vs);
-  const char *va1 = vrow + 16 * (((qd >> 1) | 2) ^ vs);
+  const int vofs = vcol * 64 + 8 * (qd & 1);
+  const int va0 = vofs + 16 * ((qd >> 1) ^ vs), va1 = vofs + 16 * (((qd >> 1) | 2) ^ vs);
   vec ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = static_cast<T>(1.0f);
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, o2 = o0;
   constexpr int RB = G::HC * 64;  // bytes per staged row
 #pragma unroll
-  for (int j = 0; j < NB / 2; ++j) {
-    vec pb;
+  for (int t = 0; t < TPW; ++t) {
+    const char *vrow = vbuf + lrow0[t] * RB;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, o2 = o0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = static_cast<T>(sc[2 * j][i]);
-      pb[4 + i] = static_cast<T>(sc[2 * j + 1][i]);
+    for (int j = 0; j < NB / 2; ++j) {
+      vec pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = static_cast<T>(sc[t][2 * j][i]);
+        pb[4 + i] = static_cast<T>(sc[t][2 * j + 1][i]);
+      }
+      const char *r0 = vrow + (2 * j) * RB, *r1 = vrow + (2 * j + 1) * RB;
+      const u32x2 a0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(r0 + va0)));
+      const u32x2 a1 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(r1 + va0)));
+      const u32x2 b0 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(r0 + va1)));
+      const u32x2 b1 = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(r1 + va1)));
+      o0 = Mma<T>::run(join<T>(a0, a1), pb, o0);
+      o1 = Mma<T>::run(join<T>(b0, b1), pb, o1);
+      o2 = Mma<T>::run(ones, pb, o2);
     }
-    const u32x2 a0 = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va0 + (2 * j) * RB)));
-    const u32x2 a1 = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va0 + (2 * j + 1) * RB)));
-    const u32x2 b0 = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va1 + (2 * j) * RB)));
-    const u32x2 b1 = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(va1 + (2 * j + 1) * RB)));
-    o0 = Mma<T>::run(join<T>(a0, a1), pb, o0);
-    o1 = Mma<T>::run(join<T>(b0, b1), pb, o1);
-    o2 = Mma<T>::run(ones, pb, o2);
+    const float inv = __builtin_amdgcn_rcpf(o2[0]);
+    const u32x2 w0 = pack4<T>(o0 * inv), w1 = pack4<T>(o1 * inv);
+    out[t] = u32x4{w0[0], w0[1], w1[0], w1[1]};
   }
-  const float inv = __builtin_amdgcn_rcpf(o2[0]);
-  const u32x2 w0 = pack4<T>(o0 * inv), w1 = pack4<T>(o1 * inv);
-  return u32x4{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// Two workgroups per compute unit: 4 waves per SIMD (at most 128 VGPRs).
+// Two workgroups of 4 waves per compute unit: 2 waves per SIMD (at most 256
+// registers each).
 template <typename T, int KS, int RY>
-__global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_kernel(
+__global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 2) void block_fused_kernel(
     const T *__restrict__ x, const T *__restrict__ w_qkv, const T *__restrict__ b_qkv,
     const T *__restrict__ rpb, const T *__restrict__ w_out, const T *__restrict__ b_out,
     T *__restrict__ y, int H, int W, FastDiv fnbx, FastDiv fnby, int nblocks) {
@@ -321,7 +365,7 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
   // ---- once per workgroup: weights, biases, raw bias-table values ----
   XOps<T, KS, RY> xo;
   BlockPos pos = block_pos<KS, RY>(b0, H, W, fnbx, fnby);
-  load_x<T, KS, RY>(x, pos, H, W, wave, ql, g, xo);
+  load_query<T, KS, RY>(x, pos, W, wave, ql, g, xo);
   for (int e = tid; e < 4 * kC * 8; e += G::THREADS) {
     const int mat = e >> 9, r = (e >> 3) & 63, c = e & 7;
     u32x4 val;
@@ -355,35 +399,44 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
         v = Elem<T>::to_f(rpb[h * G::SIDE * G::SIDE + idx]) * kSqrtD;
       traw[h][it] = v;
     }
-
   const char *wq = wts, *wk = wts + G::WMAT, *wv = wts + 2 * G::WMAT, *wo = wts + 3 * G::WMAT;
   const WeightLane wl = weight_lane(ql, g);
   for (int bi = b0; bi < b1; ++bi) {
     const BlockPos p = pos;
+    // the key halo rows of this wave: loaded per head, so that they are not
+    // live across the attention (the second read hits L2)
+    load_halo<T, KS, RY>(x, p, H, W, wave, ql, g, xo);
     __syncthreads();  // weights and biases written (first block); previous block done
 
-    // ---- query projection: Q^T for 64 channels of this lane's query ----
-    vec qop[2];
-    {
-      f32x4 acc[4];
+    // ---- query projection: Q^T for 64 channels of this lane's queries ----
+    vec qop[G::TPW][2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // operands of one channel block at a time (bounds the registers)
-        asm volatile("" ::: "memory");
-        acc[c] = *(const f32x4 *)(bias + 16 * c + 4 * g);
+    for (int hc = 0; hc < 2; ++hc) {  // channel blocks 2hc, 2hc + 1: head hc
+      f32x4 acc[G::TPW][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          acc[c] = Mma<T>::run(*(const vec *)(wq + 16 * c * 128 + (kk ? wl.wl1 : wl.wl0)),
-                               __builtin_bit_cast(vec, xo.query[kk]), acc[c]);
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int c = 2 * hc + c2;
+        const f32x4 b4 = *(const f32x4 *)(bias + 16 * c + 4 * g);
+        const vec a0 = *(const vec *)(wq + 16 * c * 128 + wl.wl0);
+        const vec a1 = *(const vec *)(wq + 16 * c * 128 + wl.wl1);
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) {
+          acc[t][c2] = Mma<T>::run(a0, __builtin_bit_cast(vec, xo.query[t][0]), b4);
+          acc[t][c2] = Mma<T>::run(a1, __builtin_bit_cast(vec, xo.query[t][1]), acc[t][c2]);
+        }
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) qop[h] = join<T>(pack4<T>(acc[2 * h]), pack4<T>(acc[2 * h + 1]));
+      for (int t = 0; t < G::TPW; ++t)
+        qop[t][hc] = join<T>(pack4<T>(acc[t][0]), pack4<T>(acc[t][1]));
     }
 
-    u32x4 ctx[2];
+    u32x4 ctx[G::TPW][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (h == 1) __syncthreads();  // head 0's attention has read kbuf, vbuf, tab
+      if (h == 1) {
+        load_halo<T, KS, RY>(x, p, H, W, wave, ql, g, xo);
+        __syncthreads();  // head 0's attention has read kbuf, vbuf, tab
+      }
       // bias table of head h
 #pragma unroll
       for (int it = 0; it < G::TPT; ++it) {
@@ -428,34 +481,48 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 4) void block_fused_k
         }
       }
       if (h == 1) {
-        // the x operands are consumed: fetch the next block's during head 1's
-        // attention and the output projection
+        // the query operands are consumed: fetch the next block's during head
+        // 1's attention and the output projection
         if (bi + 1 < b1) {
           pos = block_pos<KS, RY>(bi + 1, H, W, fnbx, fnby);
-          load_x<T, KS, RY>(x, pos, H, W, wave, ql, g, xo);
+          load_query<T, KS, RY>(x, pos, W, wave, ql, g, xo);
         }
       }
       __syncthreads();  // K, V and table of head h complete
-      if (p.y0 + wave * G::TY < p.y1)  // tiles past the map's last row idle
-        ctx[h] = attend<T, KS, RY>(kbuf, vbuf, tab, qop[h], p, H, W, wave, lane);
+      const int tci0 = tile_row<KS, RY>(p, wave, 0);
+      if (tci0 < p.y1) {  // waves whose tiles lie past the map's last row idle
+        vec qh[G::TPW];
+        u32x4 ch[G::TPW];
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) qh[t] = qop[t][h];
+        attend<T, KS, RY>(kbuf, vbuf, tab, qh, p, H, W, tci0, lane, ch);
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) ctx[t][h] = ch[t];
+      }
     }
 
-    // ---- output projection of this wave's 16 queries ----
+    // ---- output projection of this wave's queries ----
     // (whole-wave products: every lane supplies its weight row, also lanes
     // whose own query lies outside a ragged block and stores nothing)
-    if (p.y0 + wave * G::TY < p.y1) {
-      const int qr = p.y0 + wave * G::TY + ql / G::TX, qc = p.x0 + ql % G::TX;
-      const bool store = qr < p.y1 && qc < p.x1;
-      T *dst = y + p.img + ((int64_t)qr * W + qc) * kC + 4 * g;
+    {
+      const int qc = p.x0 + ql % G::TX;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        asm volatile("" ::: "memory");
-        f32x4 acc = *(const f32x4 *)(bias + 3 * kC + 16 * c + 4 * g);
+        const f32x4 b4 = *(const f32x4 *)(bias + 3 * kC + 16 * c + 4 * g);
+        const vec a0 = *(const vec *)(wo + 16 * c * 128 + wl.wl0);
+        const vec a1 = *(const vec *)(wo + 16 * c * 128 + wl.wl1);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc = Mma<T>::run(*(const vec *)(wo + 16 * c * 128 + (h ? wl.wl1 : wl.wl0)),
-                            __builtin_bit_cast(vec, ctx[h]), acc);
-        if (store) *(u32x2 *)(dst + 16 * c) = pack4<T>(acc);
+        for (int t = 0; t < G::TPW; ++t) {
+          const int tci0 = tile_row<KS, RY>(p, wave, t);
+          if (tci0 < p.y1) {
+            f32x4 acc = Mma<T>::run(a0, __builtin_bit_cast(vec, ctx[t][0]), b4);
+            acc = Mma<T>::run(a1, __builtin_bit_cast(vec, ctx[t][1]), acc);
+            const int qr = tci0 + ql / G::TX;
+            if (qr < p.y1 && qc < p.x1)
+              *(u32x2 *)(y + p.img + ((int64_t)qr * W + qc) * kC + 16 * c + 4 * g) =
+                  pack4<T>(acc);
+          }
+        }
       }
     }
   }
@@ -478,13 +545,10 @@ hipError_t launch_rt(const void *x, const void *w_qkv, const void *b_qkv, const 
   return hipGetLastError();
 }
 
-// RY = 14 when it tiles the map rows exactly and 16 does not, else 16.
 template <typename T, int KS>
 hipError_t launch_ks(const void *x, const void *w_qkv, const void *b_qkv, const void *rpb,
                      const void *w_out, const void *b_out, void *y, int B, int H, int W,
                      hipStream_t st) {
-  if (H % 16 != 0 && H % 14 == 0)
-    return launch_rt<T, KS, 14>(x, w_qkv, b_qkv, rpb, w_out, b_out, y, B, H, W, st);
   return launch_rt<T, KS, 16>(x, w_qkv, b_qkv, rpb, w_out, b_out, y, B, H, W, st);
 }
 
