@@ -106,3 +106,30 @@ def test_block_full_size_sweep_stage():
                                p.dilation, stored=_stored(p.dtype))
     err = np.abs(y.cpu().double().numpy() - ref) - _ULP[p.dtype] * np.abs(ref)
     assert err.max() <= 2e-2, "excess error %.3g" % err.max()
+
+
+def test_linear_beyond_two_gib_of_rows():
+    # x spans more than 2^31 bytes: the launcher runs the rows in slices; rows
+    # around the slice boundary, the first and the last rows, and a random
+    # sample are checked against float64 products
+    K, N = 32, 16
+    slice_rows = (2 ** 31 // (2 * K)) // 128 * 128
+    M = slice_rows + 1000
+    note("linear M%d N%d K%d bf16 (two row slices)" % (M, N, K))
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=gen) / K ** 0.5).to(torch.bfloat16)
+    b = torch.randn(N, device="cuda", generator=gen).to(torch.bfloat16)
+    y = na2d.linear(x, w, b)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(slice_rows - 130, slice_rows + 130),
+                                     np.arange(M - 64, M), rng.integers(0, M, 2048)]))
+    idx = torch.from_numpy(rows).cuda()
+    xs = x[idx].double().cpu().numpy()
+    ref = xs @ w.double().cpu().numpy().T + b.double().cpu().numpy()
+    got = y[idx].double().cpu().numpy()
+    bound = _ULP["bf16"] * np.abs(ref) + 1e-6 * K * (np.abs(xs) @ np.abs(w.double().cpu().numpy()).T).max()
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    del x, y
+    torch.cuda.empty_cache()

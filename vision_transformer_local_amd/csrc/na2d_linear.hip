@@ -55,18 +55,28 @@ template <int TN> struct ChunkRegs {
 // 16-bit matrix, as staged in LDS: row r at r * 64 bytes, logical 16-byte
 // piece j at position j ^ ((r >> 1) & 3).  The R * 4 pieces are numbered by
 // their LDS position (slot = 4 r + position); the 256 lanes take slots
-// 256 j + tid, R / 64 each.
+// 256 j + tid, R / 64 each.  A lane's byte offsets of its pieces in chunk 0
+// are fixed for the whole K loop (the matrix spans less than 2^31 bytes);
+// chunk c adds the uniform c * 64 bytes, so that a load costs no vector
+// arithmetic.
 template <int R>
-__device__ __forceinline__ void load_rows(const char *src, int64_t n, int K, int64_t r0, int c,
-                                          int tid, u32x4 *v) {
+__device__ __forceinline__ void row_offsets(int64_t n, int K, int64_t r0, int tid,
+                                            uint32_t *off) {
   static_assert(R % 64 == 0, "pieces must split evenly over the workgroup");
 #pragma unroll
   for (int j = 0; j < R / 64; ++j) {
     const int slot = j * kThreads + tid, row = slot >> 2, pos = slot & 3;
     const int lch = pos ^ ((row >> 1) & 3);
     const int64_t rr = min(r0 + row, n - 1);
-    v[j] = *(const u32x4 *)(src + (rr * K + (int64_t)c * kKC + lch * 8) * 2);
+    off[j] = (uint32_t)((rr * K + lch * 8) * 2);
   }
+}
+
+template <int R>
+__device__ __forceinline__ void load_rows(const char *src, int c, const uint32_t *off, u32x4 *v) {
+#pragma unroll
+  for (int j = 0; j < R / 64; ++j)
+    v[j] = *(const u32x4 *)((src + c * (kKC * 2)) + off[j]);
 }
 
 template <int R>
@@ -104,13 +114,16 @@ __device__ __forceinline__ int64_t planar_pixel(uint32_t m, const PlanarOut &po)
   return ((int64_t)bb * po.heads * po.hw.div + p) * po.d.div;
 }
 
+// x, M: a slice of rows (under 2^31 bytes); y: the slice's rows for
+// row-major output, the whole output for head-planar output, whose pixel
+// index adds mbase.
 template <typename T, int TN, bool PLANAR>
 __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restrict__ x,
                                                                const T *__restrict__ w,
                                                                const T *__restrict__ b,
                                                                T *__restrict__ y, int64_t M,
                                                                int N, int K, int ntn,
-                                                               PlanarOut po) {
+                                                               PlanarOut po, int64_t mbase) {
   using G = LinGeom<TN>;
   using vec = typename Mma<T>::vec;
   __shared__ __attribute__((aligned(16))) char xs0[G::XB], ws0[G::WB];
@@ -155,9 +168,12 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
   };
   const char *xc = (const char *)x, *wc = (const char *)w;
   ChunkRegs<TN> r0, r1;  // chunks c + 1 and c + 2 (alternately) in flight
+  uint32_t xoff[kTM / 64], woff[TN / 64];
+  row_offsets<kTM>(M, K, m0, tid, xoff);
+  row_offsets<TN>(N, K, n0, tid, woff);
   auto load = [&](int c, ChunkRegs<TN> &r) {
-    load_rows<kTM>(xc, M, K, m0, c, tid, r.x);
-    load_rows<TN>(wc, N, K, n0, c, tid, r.w);
+    load_rows<kTM>(xc, c, xoff, r.x);
+    load_rows<TN>(wc, c, woff, r.w);
   };
   auto write = [&](const ChunkRegs<TN> &r, char *xs, char *ws) {
     write_rows<kTM>(xs, tid, r.x);
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
   for (int tb = 0; tb < G::TB; ++tb) {
     const int64_t m = m0 + wm * 64 + tb * 16 + ql;
     if (m >= M) continue;
-    const int64_t mofs = PLANAR ? planar_pixel((uint32_t)m, po) : 0;
+    const int64_t mofs = PLANAR ? planar_pixel((uint32_t)(mbase + m), po) : 0;
 #pragma unroll
     for (int fb = 0; fb < G::FB; ++fb) {
       const int f = n0 + wn * G::WN + fb * 16 + 4 * g;
@@ -266,19 +282,30 @@ hipError_t launch_fma(const void *x, const void *w, const void *b, void *y, int6
   return hipGetLastError();
 }
 
+// Launches over slices of at most 2^31 bytes of x (a multiple of the tile
+// rows), so that the kernel's per-lane offsets fit 32 bits.
 template <typename T, int TN>
 hipError_t launch_mfma(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
                        int K, const PlanarOut *po, hipStream_t st) {
-  const int64_t ntm = (M + kTM - 1) / kTM, ntn = (N + TN - 1) / TN;
-  if (ntm * ntn > INT_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(ntm * ntn));
-  if (po != nullptr)
-    linear_mfma_kernel<T, TN, true><<<grid, kThreads, 0, st>>>(
-        (const T *)x, (const T *)w, (const T *)b, (T *)y, M, N, K, (int)ntn, *po);
-  else
-    linear_mfma_kernel<T, TN, false><<<grid, kThreads, 0, st>>>(
-        (const T *)x, (const T *)w, (const T *)b, (T *)y, M, N, K, (int)ntn, PlanarOut{});
-  return hipGetLastError();
+  const int64_t row_bytes = (int64_t)K * sizeof(T);
+  const int64_t slice = ((int64_t(1) << 31) / row_bytes) / kTM * kTM;
+  if (slice < kTM) return hipErrorInvalidValue;  // excluded by linear_supported
+  for (int64_t mb = 0; mb < M; mb += slice) {
+    const int64_t ms = M - mb < slice ? M - mb : slice;
+    const int64_t ntm = (ms + kTM - 1) / kTM, ntn = (N + TN - 1) / TN;
+    if (ntm * ntn > INT_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(ntm * ntn));
+    const T *xs = (const T *)x + mb * K;
+    if (po != nullptr)
+      linear_mfma_kernel<T, TN, true><<<grid, kThreads, 0, st>>>(
+          xs, (const T *)w, (const T *)b, (T *)y, ms, N, K, (int)ntn, *po, mb);
+    else
+      linear_mfma_kernel<T, TN, false><<<grid, kThreads, 0, st>>>(
+          xs, (const T *)w, (const T *)b, (T *)y + mb * N, ms, N, K, (int)ntn, PlanarOut{}, 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T>
@@ -299,7 +326,12 @@ hipError_t launch_tn(const void *x, const void *w, const void *b, void *y, int64
 
 }  // namespace
 
-bool linear_supported(int N, int K) { return N % 16 == 0 && K % kKC == 0; }
+// N % 16: whole 16-feature output blocks; K % 32: whole chunks; the weight
+// (and a 128-row slice of x) spans less than 2^31 bytes.
+bool linear_supported(int N, int K) {
+  return N % 16 == 0 && K % kKC == 0 && (int64_t)N * K * 2 < (int64_t(1) << 31) &&
+         (int64_t)kTM * K * 2 < (int64_t(1) << 31);
+}
 
 hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
                          int K, na2d_dtype_t dt, hipStream_t st) {
