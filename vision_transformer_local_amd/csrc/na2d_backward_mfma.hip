@@ -311,6 +311,9 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
   const int64_t pofs = b.plane * (int64_t)s.H * s.W * kHeadDim;
   const int tci0 = b.y0 + (wave / G::NTX) * TY, tcj0 = b.x0 + (wave % G::NTX) * TX;
   const bool tile_ok = tci0 < Ly && tcj0 < Lx;
+  // every query of the tile has an unclamped window (and the tile is whole)
+  const bool tile_inner = tci0 >= R && tci0 + TY - 1 + R <= Ly - 1 && tcj0 >= R &&
+                          tcj0 + TX - 1 + R <= Lx - 1;
   const int qy = ql / TX, qx = ql % TX;
   const int ci = min(tci0 + qy, Ly - 1), cj = min(tcj0 + qx, Lx - 1);
   const unsigned qpix = pixel_of(s, b, ci, cj);
@@ -342,9 +345,7 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
     const int lr0 = Y0 - hy0, lc0 = X0 - hx0;
     f32x4 sc[NB];
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // every query of the tile has an unclamped window (and the tile is whole)
-    const bool inner = tci0 >= R && tci0 + TY - 1 + R <= Ly - 1 && tcj0 >= R &&
-                       tcj0 + TX - 1 + R <= Lx - 1;
+    const bool inner = tile_inner;
     const char *kb = kbuf + (lr0 * HC + lc0 + ql) * 64 + 16 * (g ^ (((lc0 + ql) >> 1) & 3));
     const char *vb = vbuf + (kb - kbuf);
     if (inner) {
@@ -453,6 +454,22 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
         }
       }
       __builtin_amdgcn_wave_barrier();
+      if (tile_inner) {
+        // every query of the row has an unclamped window: query column x's
+        // slot sits x columns further in the parking, and every query's
+        // slot maps to the same table entry (offset R, R from the slot)
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          if (u * 64 + lane < KS * KS) {
+            float run = 0.f;
+#pragma unroll
+            for (int x = 0; x < TX; ++x) run += park[x * (KS * 16 + 1) + pslot[u]];
+            wt[eslot[u] + R * SIDE + R] += run;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        continue;
+      }
       // the row's queries in column order; the table offset of a slot
       // depends on the query only through its window start (uniform), so
       // consecutive queries with the same start share one running sum
