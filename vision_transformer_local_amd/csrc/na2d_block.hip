@@ -18,10 +18,11 @@
 //     k-position 8g + j stands for head channel pi(8g + j) = 16*(j/4) + 4g +
 //     j%4.  A dot product does not care about the order of its terms, so the
 //     keys are stored in the same order pi and Q never passes through LDS.
-//   * Per head: K^T and V^T of the halo (RY + k - 1 rows x 16 columns, the
-//     tile's key block; columns past the map repeat its last column, rows past
-//     the block's halo repeat the last map row -- finite values that only ever
-//     meet masked scores) are projected into LDS, K in order pi, V in channel
+//   * Per head: K^T and V^T of the halo (up to RY + k - 1 rows x 16 columns,
+//     the tile's key block; columns past the map repeat its last column, and
+//     the one row past the block's halo that a bottom-clamped tile reads
+//     repeats the last map row -- finite values that only ever meet masked
+//     scores) are projected into LDS, K in order pi, V in channel
 //     order, 16-byte pieces XOR-swizzled by column; then each wave runs the
 //     attention of its two query tiles against them as the general matrix-core
 //     kernel does (scores transposed, bias and mask as the accumulator input,
@@ -132,6 +133,7 @@ int block_device_cus() {
 struct BlockPos {
   int64_t img;  // element offset of the image in x and y
   int y0, y1, x0, x1, hy0, hx0;
+  int hrows;    // staged halo rows any live tile reads (rows past them are not projected)
 };
 
 template <int KS, int RY>
@@ -147,6 +149,9 @@ __device__ __forceinline__ BlockPos block_pos(int id, int H, int W, const FastDi
   p.x1 = min(p.x0 + BlockGeom<KS, RY>::RX, W);
   p.hy0 = window_start(p.y0, H, KS);
   p.hx0 = window_start(p.x0, W, KS);
+  // the block's real halo rows, plus the one past them that a tile with a
+  // bottom-clamped window reads as its (masked) last key row
+  p.hrows = min(BlockGeom<KS, RY>::HR, window_start(p.y1 - 1, H, KS) + KS - p.hy0 + 1);
   return p;
 }
 
@@ -173,7 +178,7 @@ __device__ __forceinline__ void load_halo(const T *__restrict__ x, const BlockPo
 #pragma unroll
   for (int j = 0; j < G::RPW; ++j) {
     const int r = wave + j * G::WAVES;
-    if (r < G::HR) {
+    if (r < p.hrows) {
       const int hr = min(p.hy0 + r, H - 1);
       const u32x4 *src = (const u32x4 *)(x + p.img + ((int64_t)hr * W + hc) * kC) + g;
       o.halo[j][0] = src[0];
@@ -462,7 +467,7 @@ __global__ __launch_bounds__((BlockGeom<KS, RY>::THREADS), 2) void block_fused_k
 #pragma unroll
           for (int j = 0; j < G::RPW; ++j) {
             const int r = wave + j * G::WAVES;
-            if (r < G::HR) {
+            if (r < p.hrows) {
               f32x4 ka = kb0, va = vb0;
 #pragma unroll
               for (int kk = 0; kk < 2; ++kk) {
