@@ -34,21 +34,26 @@ using namespace mfma;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-constexpr int kTM = 128;     // pixels per workgroup tile
+constexpr int kTMax = 128;   // largest pixel tile (row slices are multiples of it)
 constexpr int kKC = 32;      // K per chunk (one MFMA)
 constexpr int kThreads = 256;
+constexpr int64_t kSmallGrid = 4 * 256;  // tiles below which 64-pixel tiles are used
 
-template <int TN> struct LinGeom {
-  static constexpr int WN = TN / 2;          // features per wave
+// A TM-pixel x TN-feature tile: the four waves split it TM/64 ways along the
+// pixels and 4 / (TM/64) ways along the features, 64 pixels x WN features each.
+template <int TM, int TN> struct LinGeom {
+  static constexpr int WMW = TM / 64, WNW = 4 / WMW;  // waves along pixels, features
+  static constexpr int WN = TN / WNW;        // features per wave
   static constexpr int FB = WN / 16;         // feature blocks per wave
   static constexpr int TB = 64 / 16;         // pixel blocks per wave
-  static constexpr int XB = kTM * kKC * 2;   // bytes of a staged x chunk
+  static constexpr int XB = TM * kKC * 2;    // bytes of a staged x chunk
   static constexpr int WB = TN * kKC * 2;    // bytes of a staged w chunk
+  static_assert((TM == 64 || TM == 128) && WN % 16 == 0, "tile shape");
 };
 
 // A chunk's x and w pieces held by one lane between its load and its LDS write.
-template <int TN> struct ChunkRegs {
-  u32x4 x[kTM / 64], w[TN / 64];
+template <int TM, int TN> struct ChunkRegs {
+  u32x4 x[TM / 64], w[TN / 64];
 };
 
 // Rows [r0, r0 + R) (clamped to n - 1) x K-chunk c of a row-major [n, K]
@@ -117,23 +122,24 @@ __device__ __forceinline__ int64_t planar_pixel(uint32_t m, const PlanarOut &po)
 // x, M: a slice of rows (under 2^31 bytes); y: the slice's rows for
 // row-major output, the whole output for head-planar output, whose pixel
 // index adds mbase.
-template <typename T, int TN, bool PLANAR>
+template <typename T, int TM, int TN, bool PLANAR>
 __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restrict__ x,
                                                                const T *__restrict__ w,
                                                                const T *__restrict__ b,
                                                                T *__restrict__ y, int64_t M,
                                                                int N, int K, int ntn,
                                                                PlanarOut po, int64_t mbase) {
-  using G = LinGeom<TN>;
+  using G = LinGeom<TM, TN>;
   using vec = typename Mma<T>::vec;
   __shared__ __attribute__((aligned(16))) char xs0[G::XB], ws0[G::WB];
   __shared__ __attribute__((aligned(16))) char xs1[G::XB], ws1[G::WB];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
   const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t m0 = (tile / ntn) * kTM;
+  const int64_t m0 = (tile / ntn) * TM;
   const int n0 = (int)(tile % ntn) * TN;
-  const int wm = wave >> 1, wn = wave & 1;  // this wave: pixels m0 + 64wm.., features n0 + WN wn..
+  // this wave: pixels m0 + 64wm.., features n0 + WN wn..
+  const int wm = wave / G::WNW, wn = wave % G::WNW;
   const int nchunks = K / kKC;
 
   // accumulators start at the bias of their features
@@ -167,16 +173,16 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
       for (int fb = 0; fb < G::FB; ++fb) acc[tb][fb] = Mma<T>::run(a[fb], bx[tb], acc[tb][fb]);
   };
   const char *xc = (const char *)x, *wc = (const char *)w;
-  ChunkRegs<TN> r0, r1;  // chunks c + 1 and c + 2 (alternately) in flight
-  uint32_t xoff[kTM / 64], woff[TN / 64];
-  row_offsets<kTM>(M, K, m0, tid, xoff);
+  ChunkRegs<TM, TN> r0, r1;  // chunks c + 1 and c + 2 (alternately) in flight
+  uint32_t xoff[TM / 64], woff[TN / 64];
+  row_offsets<TM>(M, K, m0, tid, xoff);
   row_offsets<TN>(N, K, n0, tid, woff);
-  auto load = [&](int c, ChunkRegs<TN> &r) {
-    load_rows<kTM>(xc, c, xoff, r.x);
+  auto load = [&](int c, ChunkRegs<TM, TN> &r) {
+    load_rows<TM>(xc, c, xoff, r.x);
     load_rows<TN>(wc, c, woff, r.w);
   };
-  auto write = [&](const ChunkRegs<TN> &r, char *xs, char *ws) {
-    write_rows<kTM>(xs, tid, r.x);
+  auto write = [&](const ChunkRegs<TM, TN> &r, char *xs, char *ws) {
+    write_rows<TM>(xs, tid, r.x);
     write_rows<TN>(ws, tid, r.w);
   };
   // chunk c sits in LDS buffer c % 2 and, before that, in registers r(c % 2);
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void linear_mfma_kernel(const T *__restri
   // inside (chunks c + 1 and c + 3 exist), which keeps the compiler's waits
   // for the loads exact; the last steps follow it.
   auto step = [&](int c, const char *xs, const char *ws, char *xn, char *wn2,
-                  ChunkRegs<TN> &rn) {
+                  ChunkRegs<TM, TN> &rn) {
     compute(xs, ws);
     if (c + 1 < nchunks) write(rn, xn, wn2);
     if (c + 3 < nchunks) load(c + 3, rn);
@@ -284,28 +290,41 @@ hipError_t launch_fma(const void *x, const void *w, const void *b, void *y, int6
 
 // Launches over slices of at most 2^31 bytes of x (a multiple of the tile
 // rows), so that the kernel's per-lane offsets fit 32 bits.
-template <typename T, int TN>
-hipError_t launch_mfma(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
-                       int K, const PlanarOut *po, hipStream_t st) {
+template <typename T, int TM, int TN>
+hipError_t launch_mfma_tm(const void *x, const void *w, const void *b, void *y, int64_t M,
+                          int N, int K, const PlanarOut *po, hipStream_t st) {
   const int64_t row_bytes = (int64_t)K * sizeof(T);
-  const int64_t slice = ((int64_t(1) << 31) / row_bytes) / kTM * kTM;
-  if (slice < kTM) return hipErrorInvalidValue;  // excluded by linear_supported
+  const int64_t slice = ((int64_t(1) << 31) / row_bytes) / kTMax * kTMax;
+  if (slice < kTMax) return hipErrorInvalidValue;  // excluded by linear_supported
   for (int64_t mb = 0; mb < M; mb += slice) {
     const int64_t ms = M - mb < slice ? M - mb : slice;
-    const int64_t ntm = (ms + kTM - 1) / kTM, ntn = (N + TN - 1) / TN;
+    const int64_t ntm = (ms + TM - 1) / TM, ntn = (N + TN - 1) / TN;
     if (ntm * ntn > INT_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(ntm * ntn));
     const T *xs = (const T *)x + mb * K;
     if (po != nullptr)
-      linear_mfma_kernel<T, TN, true><<<grid, kThreads, 0, st>>>(
+      linear_mfma_kernel<T, TM, TN, true><<<grid, kThreads, 0, st>>>(
           xs, (const T *)w, (const T *)b, (T *)y, ms, N, K, (int)ntn, *po, mb);
     else
-      linear_mfma_kernel<T, TN, false><<<grid, kThreads, 0, st>>>(
+      linear_mfma_kernel<T, TM, TN, false><<<grid, kThreads, 0, st>>>(
           xs, (const T *)w, (const T *)b, (T *)y + mb * N, ms, N, K, (int)ntn, PlanarOut{}, 0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// 64-pixel tiles when 128-pixel ones would not give every compute unit
+// several workgroups and K is short (at most 256: a few chunks per tile, so
+// that more workgroups in flight pay off; with longer K the doubled weight
+// reads of the smaller tiles measured slower), 128 otherwise.
+template <typename T, int TN>
+hipError_t launch_mfma(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
+                       int K, const PlanarOut *po, hipStream_t st) {
+  const int64_t tiles128 = (M + 127) / 128 * ((N + TN - 1) / TN);
+  if (tiles128 < kSmallGrid && K <= 256)
+    return launch_mfma_tm<T, 64, TN>(x, w, b, y, M, N, K, po, st);
+  return launch_mfma_tm<T, 128, TN>(x, w, b, y, M, N, K, po, st);
 }
 
 template <typename T>
@@ -330,7 +349,7 @@ hipError_t launch_tn(const void *x, const void *w, const void *b, void *y, int64
 // (and a 128-row slice of x) spans less than 2^31 bytes.
 bool linear_supported(int N, int K) {
   return N % 16 == 0 && K % kKC == 0 && (int64_t)N * K * 2 < (int64_t(1) << 31) &&
-         (int64_t)kTM * K * 2 < (int64_t(1) << 31);
+         (int64_t)kTMax * K * 2 < (int64_t(1) << 31);
 }
 
 hipError_t launch_linear(const void *x, const void *w, const void *b, void *y, int64_t M, int N,
