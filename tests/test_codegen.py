@@ -9,7 +9,8 @@ hipcc cross-compiles to assembly, nothing runs).
   steps), it makes the read wait for that copy, which stalls every tile on
   the next block's loads.  (The fused block kernel loads its x operands into
   registers for its own next products; waits for those are expected.)
-* No vector-register spills and no scratch memory (scalar registers may
+* No vector-register spills and no scratch memory (every matrix-core kernel:
+  forward, projection, fused block, backward) (scalar registers may
   spill into vector-register lanes, which costs no memory traffic).
 * No LDS access through flat (generic) addresses.
 * No packed-FP32 arithmetic (the build disables it).
@@ -23,10 +24,11 @@ import pytest
 
 from vision_transformer_local_amd import build as B
 
-SOURCES = ["na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip", "na2d_block.hip"]
+SOURCES = ["na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip", "na2d_block.hip",
+           "na2d_backward_mfma.hip"]
 PIPELINED = {"na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip"}
-KERNEL = re.compile(r"^(_ZN4na2d12_GLOBAL__N_1\d+\w*(?:mfma_kernel|block_fused_kernel)\S*):",
-                    re.M)
+KERNEL = re.compile(r"^(_ZN4na2d12_GLOBAL__N_1\d+\w*(?:mfma_kernel|block_fused_kernel|"
+                    r"bwd_query_mfma|bwd_key_mfma)\S*):", re.M)
 
 
 def _asm(src, tmp_path):
