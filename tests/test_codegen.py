@@ -9,9 +9,9 @@ hipcc cross-compiles to assembly, nothing runs).
   steps), it makes the read wait for that copy, which stalls every tile on
   the next block's loads.  (The fused block kernel loads its x operands into
   registers for its own next products; waits for those are expected.)
-* No vector-register spills and no scratch memory (every matrix-core kernel:
-  forward, projection, fused block, backward) (scalar registers may
-  spill into vector-register lanes, which costs no memory traffic).
+* No vector-register spills and no scratch memory, in every matrix-core
+  kernel: forward, projection, fused block, backward.  (Scalar registers may
+  spill into vector-register lanes, which costs no memory traffic.)
 * No LDS access through flat (generic) addresses.
 * No packed-FP32 arithmetic (the build disables it).
 """
