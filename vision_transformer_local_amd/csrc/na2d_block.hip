@@ -2,8 +2,9 @@
 // q/k/v projection with bias, per-head 2D neighborhood attention with the
 // relative-position bias, output projection with bias (DiNAT walk-through
 // blog, "What is DiNAT": the module projects the channels-last features to
-// queries, keys and values, runs natten2dqkrpb -> softmax -> natten2dav per
-// head, and projects the heads' outputs back).  This kernel covers C = 64
+// queries, keys and values with bias and runs natten2dqkrpb -> softmax ->
+// natten2dav per head; the heads' outputs then pass the block's output
+// projection, the usual close of an attention block).  This kernel covers C = 64
 // channels in 2 heads of 32, k in {3, 5, 7}, no dilation, maps of at least
 // k x k (no padding); other blocks take the three-launch path.
 //
@@ -11,7 +12,9 @@
 // query tiles), with both heads:
 //   * x is read straight into MFMA operands (lane (g, i) holds 8 channels of
 //     pixel i), never staged: the halo rows of the block for the key/value
-//     projection, the block's own pixels for the query projection.
+//     projection (loaded once per head, so that they are not live across the
+//     attention), the block's own pixels for the query projection (fetched
+//     for the next block during the current one's second head).
 //   * Q^T = Wq . x^T: lane (g, i) ends with channels 16c + 4g..+3 of query i
 //     for the four 16-channel blocks c.  For head h the lane's two blocks
 //     2h, 2h+1 form the 8-element operand of the score product as they are:
