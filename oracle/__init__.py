@@ -51,7 +51,7 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_int, ctypes.c_int,
             i64p, ctypes.c_int64,
-            dp, dp, dp, i32p, i32p, ctypes.c_int]
+            dp, dp, dp, dp, i32p, i32p, ctypes.c_int]
         lib.na2d_oracle_backward.restype = ctypes.c_int
         lib.na2d_oracle_backward.argtypes = [
             dp, dp, dp, dp, dp,
@@ -92,8 +92,8 @@ def valid(H: int, W: int, kernel_size: int, dilation: int) -> bool:
 
 
 def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
-            scores: bool = False, probs: bool = False, neighbours: bool = False,
-            argmax: bool = False, threads: int | None = None):
+            scores: bool = False, probs: bool = False, lse: bool = False,
+            neighbours: bool = False, argmax: bool = False, threads: int | None = None):
     """Oracle forward pass.
 
     q, k, v: [B, heads, H, W, D]; rpb: [heads, 2k-1, 2k-1] or None (zero bias).
@@ -101,7 +101,8 @@ def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
     results are then returned for those queries only, in that order.
 
     Returns a dict with ``out`` (shape [B, heads, H, W, D], or [len(idx), D])
-    and, on request, ``scores``/``probs`` ([..., k*k]), ``neighbours`` (flat
+    and, on request, ``scores``/``probs`` ([..., k*k]), ``lse`` ([...], the
+    natural log of each query's softmax denominator), ``neighbours`` (flat
     pixel index i*W + j of each window slot n = a*k + c) and ``argmax``.
     """
     lib = _load()
@@ -126,6 +127,7 @@ def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
     out = np.empty(lead + (D,), dtype=np.float64)
     s = np.empty(lead + (nk,), dtype=np.float64) if scores else None
     p = np.empty(lead + (nk,), dtype=np.float64) if probs else None
+    ls = np.empty(lead, dtype=np.float64) if lse else None
     nb = np.empty(lead + (nk,), dtype=np.int32) if neighbours else None
     am = np.empty(lead, dtype=np.int32) if argmax else None
     rc = lib.na2d_oracle_forward(
@@ -134,6 +136,7 @@ def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
         B, heads, H, W, D, ks, dil,
         _ptr(idx, ctypes.c_int64), nq,
         _ptr(out, ctypes.c_double), _ptr(s, ctypes.c_double), _ptr(p, ctypes.c_double),
+        _ptr(ls, ctypes.c_double),
         _ptr(nb, ctypes.c_int32), _ptr(am, ctypes.c_int32),
         threads if threads else default_threads())
     if rc != 0:
@@ -143,6 +146,8 @@ def forward(q, k, v, rpb, kernel_size: int, dilation: int, *, idx=None,
         res["scores"] = s
     if probs:
         res["probs"] = p
+    if lse:
+        res["lse"] = ls
     if neighbours:
         res["neighbours"] = nb
     if argmax:

@@ -48,9 +48,13 @@
  *   4. Output (same passage, natten2dav(attn, value, kernel_size, dilation)):
  *        out[e] = sum_n P[n] * value_n[e].
  *
+ *   5. Log-sum-exp (optional): the natural log of step 3's denominator,
+ *        lse = ln sum_n exp(S[n]) = Smax + ln sum_n exp(S[n] - Smax).
+ *
  * The function returns, per requested query, the output row and optionally
- * the scores S, the probabilities P, the flat neighbour pixel index of every
- * window slot and the arg-max of S (lowest n wins ties).
+ * the scores S, the probabilities P, the log-sum-exp, the flat neighbour
+ * pixel index of every window slot and the arg-max of S (lowest n wins
+ * ties).
  */
 #include <math.h>
 #include <pthread.h>
@@ -80,7 +84,7 @@ typedef struct {
     int B, heads, H, W, D, ks, dil;
     const int64_t *qidx;
     int64_t first, last; /* range of positions in the query list */
-    double *out, *scores, *probs;
+    double *out, *scores, *probs, *lse;
     int32_t *nbr, *argmax;
 } oracle_job;
 
@@ -138,6 +142,8 @@ static void oracle_one_query(const oracle_job *jb, int64_t pos, double *s, doubl
     }
     for (int n = 0; n < nk; ++n)
         p[n] /= sum;
+    if (jb->lse)
+        jb->lse[pos] = smax + log(sum);
 
     double *orow = jb->out + pos * D;
     for (int e = 0; e < D; ++e)
@@ -178,13 +184,13 @@ static void *oracle_worker(void *arg)
  * q, k, v: [B, heads, H, W, D] doubles, contiguous.  rpb: [heads, 2k-1, 2k-1]
  * or NULL.  qidx: nq flat query indices in [0, B*heads*H*W), or NULL for all
  * queries in order.  Outputs are indexed by position in that list:
- * out [nq, D]; scores, probs [nq, k*k] (optional); nbr [nq, k*k] flat pixel
- * index i*W+j (optional); argmax [nq] (optional).
+ * out [nq, D]; scores, probs [nq, k*k] (optional); lse [nq] (optional);
+ * nbr [nq, k*k] flat pixel index i*W+j (optional); argmax [nq] (optional).
  */
 int na2d_oracle_forward(const double *q, const double *k, const double *v, const double *rpb,
                         int B, int heads, int H, int W, int D, int ks, int dil,
                         const int64_t *qidx, int64_t nq,
-                        double *out, double *scores, double *probs,
+                        double *out, double *scores, double *probs, double *lse,
                         int32_t *nbr, int32_t *argmax, int nthreads)
 {
     if (!q || !k || !v || !out || B < 1 || heads < 1 || H < 1 || W < 1 || D < 1 ||
@@ -218,7 +224,7 @@ int na2d_oracle_forward(const double *q, const double *k, const double *v, const
         jb->ks = ks; jb->dil = dil; jb->qidx = qidx;
         jb->first = (int64_t)t * chunk;
         jb->last = jb->first + chunk < nq ? jb->first + chunk : nq;
-        jb->out = out; jb->scores = scores; jb->probs = probs;
+        jb->out = out; jb->scores = scores; jb->probs = probs; jb->lse = lse;
         jb->nbr = nbr; jb->argmax = argmax;
         created[t] = 0;
         if (jb->first >= jb->last)
