@@ -16,7 +16,11 @@ rotate through enough input/output replicas to touch >= 1 GiB.  The K timed
 launches are captured once in a HIP graph and replayed (launch overhead off
 the host); wall time brackets the replay with device synchronisations, and
 HIP events recorded on the same stream give the per-launch kernel time used
-for the roofline figure.
+for the roofline figure.  After the replay, 100 eager steps are timed one by
+one with their own HIP events (median, p10, p90 in per_launch_us).  The
+default fused forward also times the unfused three-kernel path the same way
+(the "unfused" object), and the float64 oracle runs on all host cores
+(cpu_baseline) and on one (cpu_baseline_1core).
 
 Prints ONE JSON line (rank 0).  --gpus N > 1 is refused: this library's
 benchmark runs on a single GPU.
@@ -115,12 +119,12 @@ def measured_traffic(workload: str, path: str):
 
 
 def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500, backward=False,
-                 pads=None):
-    """The float64 oracle on the host cores: whole-workload passes repeated
-    until about budget_s seconds of CPU work, median pass time.  pads: the
-    (pad_k, pad_v) of a padded forward."""
+                 pads=None, threads=None):
+    """The float64 oracle on the host cores (all of them, or `threads`):
+    whole-workload passes repeated until about budget_s seconds of CPU work,
+    median pass time.  pads: the (pad_k, pad_v) of a padded forward."""
     import oracle
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     arrs = [t.to(torch.float64).numpy() for t in cpu_inputs]
     fn = oracle.backward if backward else oracle.forward
     if pads is not None:
@@ -182,6 +186,8 @@ def main(argv=None):
                          "[B, H, W, heads*D] through na2d_forward_strided")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip timing the unfused path beside the fused forward")
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the device-copy bandwidth measurement")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
@@ -292,7 +298,7 @@ def main(argv=None):
         if r != 0:
             raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
 
-    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+    ms_per_step, kernel_ms, per_launch = time_steps(args, launch, dev)
     K = args.steps
 
     # sanity: a sample of the first replica's output against the oracle
@@ -339,24 +345,89 @@ def main(argv=None):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},
         "kernel_ms": kernel_ms,
+        "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.path == "fused" and not (cl or args.padded) and not args.no_unfused:
+        rec["unfused"] = unfused_beside(args, p, dev, L, cpu)
     if not args.no_copy_reference:
         copy_gbs = copy_bandwidth(dev)
         rec["copy_reference"] = {"copy_gbs": copy_gbs, "achieved_over_copy": achieved / copy_gbs,
                                  "what": "torch device copy of 1 GiB, read+write bytes"}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(
-            p, cpu, pads=(pad_k.cpu(), pad_v.cpu()) if args.padded else None)
+        pads = (pad_k.cpu(), pad_v.cpu()) if args.padded else None
+        rec["cpu_baseline"] = cpu_baseline(p, cpu, pads=pads)
+        rec["cpu_baseline_1core"] = cpu_baseline(p, cpu, pads=pads, threads=1, budget_s=8.0)
     print(json.dumps(rec), flush=True)
     return 0
 
 
+def unfused_beside(args, p, dev, L, cpu):
+    """The unfused three-kernel path (scores + bias, softmax, weighted sum of
+    values through an fp32 [.., k*k] tensor) on the same workload and inputs,
+    timed with the same protocol, for the comparison beside the fused one."""
+    q0, k0, v0, rpb0 = cpu
+    B, heads, H, W, D = p.shape
+    ks, dil = p.kernel_size, p.dilation
+    dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
+    tbytes = q0.numel() * q0.element_size()
+    attn_bytes = p.n_query_heads * ks * ks * 4
+    R = max(2, math.ceil(args.rotate_bytes / (4 * tbytes + attn_bytes)))
+    rpb = rpb0.to(dev)
+    reps = [tuple(t.to(dev) for t in (q0, k0, v0)) +
+            (torch.empty_like(q0, device=dev),
+             torch.empty(p.shape[:4] + (ks * ks,), dtype=torch.float32, device=dev))
+            for _ in range(R)]
+
+    def launch(i, stream):
+        q, k, v, out, attn = reps[i % R]
+        st = ctypes.c_void_p(stream)
+        r = L.na2d_qkrpb(q.data_ptr(), k.data_ptr(), rpb.data_ptr(), attn.data_ptr(),
+                         B, heads, H, W, D, ks, dil, dt_code, st)
+        r = r or L.na2d_softmax(attn.data_ptr(), attn.data_ptr(), B, heads, H, W, ks, st)
+        r = r or L.na2d_av(attn.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           B, heads, H, W, D, ks, dil, dt_code, st)
+        if r != 0:
+            raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
+
+    ms_per_step, kernel_ms, per_launch = time_steps(args, launch, dev)
+    abytes = algorithmic_bytes(p) + 4 * attn_bytes  # fp32 attn written, read, written, read
+    achieved = abytes / (kernel_ms / 1e3) / 1e9
+    del reps
+    torch.cuda.empty_cache()
+    return {"path": "unfused (qkrpb -> softmax -> av, three launches)",
+            "value": p.n_query_heads / (ms_per_step / 1e3), "unit": "queries*heads/s",
+            "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "per_launch_us": per_launch,
+            "achieved_gbs": achieved, "frac": achieved / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_step": abytes, "replicas": R}
+
+
+def per_launch_us(launch, stream, n=100, warm=10):
+    """Eager launches, each bracketed by its own pair of HIP events on the
+    launch stream: median, p10 and p90 of the n durations in microseconds
+    (steps rotate through the replicas as in the timed region)."""
+    import numpy as np
+    for i in range(warm):
+        launch(i, stream.cuda_stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(warm + i, stream.cuda_stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "n": n,
+            "what": "HIP events around each of %d eager steps after %d warm-up steps" % (n, warm)}
+
+
 def time_steps(args, launch, dev):
     """Warm up, capture K launches in a graph (or not), time them: returns
-    (wall ms per step, event ms per step)."""
+    (wall ms per step, event ms per step, per-launch statistics)."""
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
         launch(i, stream.cuda_stream)
@@ -388,7 +459,8 @@ def time_steps(args, launch, dev):
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K
+    del graph
+    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K, per_launch_us(launch, stream)
 
 
 def block_algorithmic_bytes(p) -> int:
@@ -442,7 +514,7 @@ def bench_block(args, dev, L):
         if r != 0:
             raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
 
-    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+    ms_per_step, kernel_ms, per_launch = time_steps(args, launch, dev)
 
     # sanity: a sample of pixels of the first replica against the oracle
     import oracle
@@ -479,6 +551,7 @@ def bench_block(args, dev, L):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload, "block")},
         "kernel_ms": kernel_ms,
+        "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
         "kernel_source_hash": kernel_source_hash("block"),
@@ -517,7 +590,7 @@ def bench_backward(args, p, dev, L):
         if r != 0:
             raise RuntimeError("launch failed: " + na2d.na2d_status_string(r))
 
-    ms_per_step, kernel_ms = time_steps(args, launch, dev)
+    ms_per_step, kernel_ms, per_launch = time_steps(args, launch, dev)
 
     # sanity: the first replica's gradients against the oracle (skipped on the
     # largest maps, where the parity tests cover them)
@@ -552,6 +625,7 @@ def bench_backward(args, p, dev, L):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(args.workload, "backward")},
         "kernel_ms": kernel_ms,
+        "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
         "kernel_source_hash": kernel_source_hash("backward"),

@@ -93,6 +93,28 @@ na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, con
                                 na2d_algo_t algo, hipStream_t stream);
 
 /*
+ * na2d_forward that also writes each query's log-sum-exp: the natural log of
+ * the softmax's denominator over its k*k window,
+ *   lse[b,h,i,j] = ln sum_n exp(q[b,h,i,j].k[neighbour n] / sqrt(D) + rpb[h][offset of n]),
+ * the score row of the blog's natten2dqkrpb step (DiNAT walk-through blog,
+ * "What is DiNAT") reduced the way its softmax(dim=-1) normalises it.  With
+ * it the softmax weights exp(score - lse) are recoverable from q, k and rpb
+ * alone, which is what a gradient pass needs.
+ *
+ *   lse  written, fp32, dense [B, heads, H, W]; device memory, 16-byte
+ *        aligned; must not overlap out or any input
+ *
+ * lse is computed in fp32 from the same scores as out (the matrix-core
+ * kernels take the weights' fp32 sum before they are rounded for the value
+ * product).  out is bit-identical to na2d_forward's.  Other arguments, rules
+ * and status codes as na2d_forward (kernel family NA2D_ALGO_AUTO).
+ */
+na2d_status_t na2d_forward_lse(const void *q, const void *k, const void *v, const void *rpb,
+                               void *out, float *lse, int B, int heads, int H, int W, int D,
+                               int kernel_size, int dilation, na2d_dtype_t dtype,
+                               hipStream_t stream);
+
+/*
  * na2d_forward on strided views: the same operator, with q, k, v and out
  * addressed as [B, heads, H, W, D] views whose element (b, h, i, j, e) sits
  * at  b*s[0] + h*s[1] + i*s[2] + j*s[3] + e  (D channels contiguous).  This

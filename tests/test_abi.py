@@ -87,6 +87,7 @@ def test_forward_validation(args, expect):
                                    algo, S) == expect
     assert L.na2d_qkrpb(P[0], P[1], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == expect
     assert L.na2d_av(P[4], P[2], P[5], B, h, H, W, D, ks, d, dt, S) == expect
+    assert L.na2d_forward_lse(*P[:6], B, h, H, W, D, ks, d, dt, S) == expect
 
 
 VALID = (1, 2, 14, 14, 32, 7, 1, BF16)
@@ -114,6 +115,30 @@ def test_forward_rejects_overlapping_output():
     out = ctypes.c_void_p(P[0].value + 1024)
     assert L.na2d_forward(P[0], P[1], P[2], P[3], out, *VALID, S) == INVALID
     assert L.na2d_forward(P[0], P[1], P[2], P[3], P[0], *VALID, S) == INVALID
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 4, 5])
+def test_forward_lse_pointer_rules(slot):
+    L = na2d.lib()
+    ptrs = list(P[:6])
+    assert L.na2d_forward_lse(*ptrs[:5], NULL, *VALID, S) == INVALID
+    ptrs[slot] = NULL
+    assert L.na2d_forward_lse(*ptrs, *VALID, S) == INVALID
+    ptrs = list(P[:6])
+    ptrs[slot] = ctypes.c_void_p(ptrs[slot].value + 4)
+    assert L.na2d_forward_lse(*ptrs, *VALID, S) == INVALID
+
+
+def test_forward_lse_rejects_overlaps():
+    L = na2d.lib()
+    B, h, H, W = VALID[:4]
+    # lse ([B, heads, H, W] fp32) starting inside each input and inside out
+    for src in range(5):
+        inside = ctypes.c_void_p(P[src].value + 256)
+        assert L.na2d_forward_lse(*P[:5], inside, *VALID, S) == INVALID, src
+    # out starting 16 bytes before the end of lse
+    out = ctypes.c_void_p(P[5].value + B * h * H * W * 4 - 16)
+    assert L.na2d_forward_lse(*P[:4], out, P[5], *VALID, S) == INVALID
 
 
 def test_forward_rejects_bad_algo_and_mfma_fp32():

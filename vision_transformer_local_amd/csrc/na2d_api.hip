@@ -80,24 +80,26 @@ bool injective(const na2d::Strides &t, const na2d::Shape &s) {
   return true;
 }
 
-// The forward pass for checked shapes, pointers, strides and padding.
+// The forward pass for checked shapes, pointers, strides and padding; lse
+// (optional) receives the per-query log-sum-exp.
 na2d_status_t forward_checked(const void *q, const void *k, const void *v, const void *rpb,
                               void *out, const na2d::Shape &s, const na2d::Strides &in,
                               const na2d::Strides &os, const na2d::Pad &pad,
-                              na2d_dtype_t dtype, na2d_algo_t algo, hipStream_t stream) {
+                              na2d_dtype_t dtype, na2d_algo_t algo, hipStream_t stream,
+                              float *lse = nullptr) {
   const bool automatic = algo == NA2D_ALGO_AUTO;
   if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
   if (algo == NA2D_ALGO_MFMA) {
     if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
     bool supported = true;
     hipError_t e =
-        na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, &supported);
+        na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, &supported, lse);
     if (supported) return from_hip(e);
     if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
     // planes too large for 32-bit in-plane offsets, and padded maps that are
     // not k*d square: the FMA kernel handles them
   }
-  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, pad, dtype, stream));
+  return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, lse));
 }
 
 }  // namespace
@@ -209,6 +211,36 @@ na2d_status_t na2d_forward(const void *q, const void *k, const void *v, const vo
                            hipStream_t stream) {
   return na2d_forward_algo(q, k, v, rpb, out, B, heads, H, W, D, kernel_size, dilation, dtype,
                            NA2D_ALGO_AUTO, stream);
+}
+
+na2d_status_t na2d_forward_lse(const void *q, const void *k, const void *v, const void *rpb,
+                               void *out, float *lse, int B, int heads, int H, int W, int D,
+                               int kernel_size, int dilation, na2d_dtype_t dtype,
+                               hipStream_t stream) {
+  na2d::Shape s;
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  if (st != NA2D_SUCCESS) return st;
+  if (!q || !k || !v || !out || !lse) return NA2D_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) ||
+      (rpb && !aligned16(rpb)))
+    return NA2D_ERROR_INVALID_VALUE;
+  const int64_t tbytes = s.n_query * D * elem_bytes(dtype), lbytes = s.n_query * 4;
+  const int64_t rbytes = rpb ? (int64_t)heads * (2 * kernel_size - 1) * (2 * kernel_size - 1) *
+                                   elem_bytes(dtype)
+                             : 0;
+  struct Span {
+    const void *p;
+    int64_t n;
+  };
+  const Span read[] = {{q, tbytes}, {k, tbytes}, {v, tbytes}, {rpb, rbytes}};
+  for (const Span &r : read)
+    if (overlaps(out, tbytes, r.p, r.n) || overlaps(lse, lbytes, r.p, r.n))
+      return NA2D_ERROR_INVALID_VALUE;
+  if (overlaps(out, tbytes, lse, lbytes)) return NA2D_ERROR_INVALID_VALUE;
+  const na2d::Strides pl = na2d::planar_strides(s);
+  return forward_checked(q, k, v, rpb, out, s, pl, pl, na2d::no_pad(s), dtype, NA2D_ALGO_AUTO,
+                         stream, lse);
 }
 
 na2d_status_t na2d_linear(const void *x, const void *w, const void *b, void *y, int64_t M,

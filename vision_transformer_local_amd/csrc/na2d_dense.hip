@@ -95,12 +95,12 @@ __device__ __forceinline__ DenseBlock dense_block(int id, const FastDiv &f, int 
 // PAD: the map is padded to k*d x k*d (maybe_pad); pixels at row >= s.H or
 // column >= s.W are staged from the head's pad vectors and their queries are
 // neither read nor written.
-template <typename T, int KS, bool PAD>
+template <typename T, int KS, bool PAD, bool LSE>
 __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
     FastDiv fblk, bool hfast, int per_head, int nblocks, int log2d,
-    const T *__restrict__ pad_k, const T *__restrict__ pad_v) {
+    const T *__restrict__ pad_k, const T *__restrict__ pad_v, float *__restrict__ lse) {
   using G = DenseGeometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int N = G::N, NT = G::NT, NKB = G::NKB, NK = G::NK, TPW = G::TPW, SG = G::SG;
@@ -234,8 +234,10 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     asm volatile("" : "+v"(x));
     return x;
   };
-  // one tile: returns the lane's 8 output channels, rounded
-  auto tile = [&](const char *kb, const char *vb, int u, u32x4 qraw, int slot) -> u32x4 {
+  // one tile: returns the lane's 8 output channels, rounded, and (when lse
+  // is given) the query's log-sum-exp in tlse
+  auto tile = [&](const char *kb, const char *vb, int u, u32x4 qraw, int slot,
+                  float &tlse) -> u32x4 {
     const int t = wave * TPW + u, c = t / NT, tt = t % NT;
     const vec qv = __builtin_bit_cast(vec, qraw);
     // key slot kbk*16 + ql, logical chunk g (the swizzle does not depend on kbk)
@@ -259,6 +261,14 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[kbk][i] = __builtin_amdgcn_exp2f(fmaf(sc[kbk][i], c2, -mc));
+    if constexpr (LSE) {  // the fp32 weights' sum (not the 16-bit one the output is divided by)
+      float l = 0.f;
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l += sc[kbk][i];
+      tlse = window_lse(mc, group_sum(l));
+    }
     // out^T = V^T . P^T, 32 keys per MFMA: P^T rows 8g'..8g'+7 are key slots
     // 32j + 4g' + 0..3 and 32j + 16 + 4g' + 0..3.  As a source of the
     // transposing read, lane (g, 4kk + qd) reads channels 4qd..4qd+3 (+16
@@ -308,11 +318,15 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     if constexpr (PAD) ok = ok && real(bk.j0 + min(c, bk.n - 1), qrow[u], qcol[u]);
     return ok;
   };
-  auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok) {
+  auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok, float tlse) {
     if (ok) {
       char *o = (char *)out + tile_base(bk, u, so) + ooff[u] + g * 8u;
       *(u32x2 *)o = u32x2{val[0], val[1]};
       *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{val[2], val[3]};
+      // with dense q, the query's index in [B, heads, H, W] order is its q
+      // byte offset over the pixel's D channels
+      if (LSE && g == 0)
+        lse[(tile_base(bk, u, si) + qoff[u]) / (kHeadDim * sizeof(T))] = tlse;
     }
   };
 
@@ -330,6 +344,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
 
   u32x4 res[TPW];
   bool rok[TPW];
+  float rlse[TPW];
   // One block from (kc, vc) while the next is staged into (kn, vn); called
   // with fixed arrays so that the compiler can tell the DMA target from the
   // buffer being read.
@@ -346,7 +361,8 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       rok[u] = tile_ok(cur, u);
-      res[u] = (wave * TPW + u) / NT < cur.n ? tile(kc, vc, u, qcur[u], cur.h & 1)
+      rlse[u] = 0.f;
+      res[u] = (wave * TPW + u) / NT < cur.n ? tile(kc, vc, u, qcur[u], cur.h & 1, rlse[u])
                                              : u32x4{0u, 0u, 0u, 0u};
     }
     if (!more) return;
@@ -360,7 +376,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // results leave after the barrier, whose wait then covers only the loads
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u]);
+    for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u], rlse[u]);
     cur = nxt;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) qcur[u] = qnxt[u];
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     step(bi + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u]);  // the last block
+  for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u], rlse[u]);  // the last block
 }
 
 int dense_cus() {
@@ -390,7 +406,7 @@ int dense_cus() {
 template <typename T, int KS>
 hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, const ByteStrides &si, const ByteStrides &so,
-                        const Pad &pad, hipStream_t st) {
+                        const Pad &pad, hipStream_t st, float *lse) {
   using G = DenseGeometry<KS>;
   const int64_t per_head = (int64_t)s.B * s.dil * s.dil;  // classes of one head
   const int64_t bph = (per_head + G::SG - 1) / G::SG;      // blocks per head
@@ -402,11 +418,14 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   // heads interleaved within pixels: alternate heads between blocks
   const bool hfast = s.heads > 1 && (uint64_t)si.h < si.x;
   const bool padded = pad.Hp > s.H || pad.Wp > s.W;
-  auto kernel = padded ? dense_mfma_kernel<T, KS, true> : dense_mfma_kernel<T, KS, false>;
+  // (padded maps come without lse: the caller checks)
+  auto kernel = padded ? dense_mfma_kernel<T, KS, true, false>
+                       : (lse ? dense_mfma_kernel<T, KS, false, true>
+                              : dense_mfma_kernel<T, KS, false, false>);
   kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, si, so,
       make_fastdiv((uint32_t)(hfast ? s.heads : bph)), hfast, (int)per_head, (int)nblocks, log2d,
-      (const T *)pad.k, (const T *)pad.v);
+      (const T *)pad.k, (const T *)pad.v, lse);
   return hipGetLastError();
 }
 
@@ -415,26 +434,27 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const ByteStrides &si,
                              const ByteStrides &so, const Pad &pad, na2d_dtype_t dt,
-                             hipStream_t st, bool *supported) {
+                             hipStream_t st, bool *supported, float *lse) {
   *supported = true;
   const bool pow2_dil = (s.dil & (s.dil - 1)) == 0;
   // the (padded) map must be exactly k*d square: every class k x k
   if ((int64_t)s.ks * s.dil != pad.Hp || (int64_t)s.ks * s.dil != pad.Wp || !pow2_dil ||
-      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32) {
+      (s.ks != 3 && s.ks != 5 && s.ks != 7) || dt == NA2D_DTYPE_F32 ||
+      (lse != nullptr && (pad.Hp > s.H || pad.Wp > s.W))) {
     *supported = false;
     return hipSuccess;
   }
   if (dt == NA2D_DTYPE_BF16) {
     switch (s.ks) {
-      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, si, so, pad, st);
-      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, si, so, pad, st);
-      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, si, so, pad, st);
+      case 3: return launch_dense<__bf16, 3>(q, k, v, rpb, out, s, si, so, pad, st, lse);
+      case 5: return launch_dense<__bf16, 5>(q, k, v, rpb, out, s, si, so, pad, st, lse);
+      default: return launch_dense<__bf16, 7>(q, k, v, rpb, out, s, si, so, pad, st, lse);
     }
   }
   switch (s.ks) {
-    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, si, so, pad, st);
-    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, si, so, pad, st);
-    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, si, so, pad, st);
+    case 3: return launch_dense<_Float16, 3>(q, k, v, rpb, out, s, si, so, pad, st, lse);
+    case 5: return launch_dense<_Float16, 5>(q, k, v, rpb, out, s, si, so, pad, st, lse);
+    default: return launch_dense<_Float16, 7>(q, k, v, rpb, out, s, si, so, pad, st, lse);
   }
 }
 

@@ -119,14 +119,18 @@ inline Pad no_pad(const Shape &s) { return Pad{nullptr, nullptr, s.H, s.W}; }
 
 // Launchers (one per kernel family); each returns hipSuccess or the launch
 // error.  Argument checking happens before these are reached.  q, k and v
-// share the strides `in`; out has its own.
+// share the strides `in`; out has its own.  lse (optional, fp32, one value
+// per query in dense [B, heads, H, W] order) receives each query's natural
+// log-sum-exp of its window scores; the matrix-core launchers take it for
+// dense [B, heads, H, W, D] q/k/v only (else *supported = false).
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
                             void *out, const Shape &s, const Strides &in, const Strides &out_st,
-                            const Pad &pad, na2d_dtype_t dt, hipStream_t st);
+                            const Pad &pad, na2d_dtype_t dt, hipStream_t st,
+                            float *lse = nullptr);
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
                              const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
-                             hipStream_t st, bool *supported);
+                             hipStream_t st, bool *supported, float *lse = nullptr);
 // Whole-sub-grid kernel (H == W == k*d); sets *supported = false when the
 // problem is not of that kind.  Strides in bytes (mfma::ByteStrides).
 namespace mfma {
@@ -135,7 +139,8 @@ struct ByteStrides;
 hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const mfma::ByteStrides &in,
                              const mfma::ByteStrides &out_st, const Pad &pad,
-                             na2d_dtype_t dt, hipStream_t st, bool *supported);
+                             na2d_dtype_t dt, hipStream_t st, bool *supported,
+                             float *lse = nullptr);
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st);
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st);

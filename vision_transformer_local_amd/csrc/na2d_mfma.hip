@@ -348,16 +348,19 @@ __device__ __forceinline__ u32x4 load_q(const T *__restrict__ q, int64_t pofs, u
 }
 
 // A lane's share of a tile's output: channels 4g..4g+3 and 16+4g..16+4g+3
-// of its query, rounded; ok is false for queries outside a ragged block.
+// of its query, rounded; ok is false for queries outside a ragged block;
+// lse: the query's log-sum-exp (when requested).
 struct TileOut {
   u32x4 val;
   bool ok;
+  float lse;
 };
 
 // Unnormalised softmax weights over the query's k*k keys, in place (the 4
 // lane groups hold disjoint keys; the denominator comes from the PV step).
+// Returns the reference mc the weights are taken against.
 template <int KS>
-__device__ __forceinline__ void softmax_weights(f32x4 (&sc)[Geometry<KS>::NB]) {
+__device__ __forceinline__ float softmax_weights(f32x4 (&sc)[Geometry<KS>::NB]) {
   constexpr int NB = Geometry<KS>::NB;
   const float c2 = kLog2e / kSqrtD;  // exp(S - Smax) = exp2((acc - accmax) * c2)
   float mx = -INFINITY;
@@ -371,6 +374,7 @@ __device__ __forceinline__ void softmax_weights(f32x4 (&sc)[Geometry<KS>::NB]) {
   for (int a = 0; a < NB; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[a][i] = __builtin_amdgcn_exp2f(fmaf(sc[a][i], c2, -mc));
+  return mc;
 }
 
 // 16-bit P^T operand of key rows 2j and 2j+1.
@@ -403,7 +407,7 @@ __device__ __forceinline__ void pv_step(PVAcc &acc, typename Mma<T>::vec w0,
 }
 
 template <typename T>
-__device__ __forceinline__ TileOut finish(const PVAcc &acc, bool ok) {
+__device__ __forceinline__ TileOut finish(const PVAcc &acc, bool ok, float lse) {
   const float inv = __builtin_amdgcn_rcpf(acc.o2[0]);
   typedef __attribute__((ext_vector_type(4))) T vec4;
   vec4 r0, r1;
@@ -413,11 +417,12 @@ __device__ __forceinline__ TileOut finish(const PVAcc &acc, bool ok) {
     r1[i] = static_cast<T>(acc.o1[i] * inv);
   }
   const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
-  return TileOut{{w0[0], w0[1], w1[0], w1[1]}, ok};
+  return TileOut{{w0[0], w0[1], w1[0], w1[1]}, ok, lse};
 }
 
-// One 16-query tile of a block (this wave's), from one LDS buffer.
-template <typename T, int KS>
+// One 16-query tile of a block (this wave's), from one LDS buffer; LSE: also
+// the query's log-sum-exp.
+template <typename T, int KS, bool LSE>
 __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart &c,
                                                 const char *kbuf, const char *vbuf,
                                                 const float *tab, u32x4 qraw, int lane) {
@@ -427,7 +432,7 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
   const int ql = lane & 15, g = lane >> 4;
   const int qy = ql / TX, qx = ql % TX;
   const int tci0 = r.tci0, tcj0 = c.tcj0;
-  if (tci0 >= r.rc1 || tcj0 >= c.cc1) return TileOut{{0u, 0u, 0u, 0u}, false};  // outside
+  if (tci0 >= r.rc1 || tcj0 >= c.cc1) return TileOut{{0u, 0u, 0u, 0u}, false, 0.f};  // outside
   const int Y0 = r.Y0, X0 = c.X0;
   const int lrow0 = Y0 - r.hy0, lcol0 = X0 - c.hx0;
   const vec qv = __builtin_bit_cast(vec, qraw);
@@ -478,7 +483,16 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
     }
   }
 
-  softmax_weights<KS>(sc);
+  const float mc = softmax_weights<KS>(sc);
+  float lse = 0.f;
+  if constexpr (LSE) {  // the fp32 weights' sum (not the 16-bit one the output is divided by)
+    float l = 0.f;
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l += sc[a][i];
+    lse = window_lse(mc, group_sum(l));
+  }
 
   // out^T = V^T . P^T over pairs of key rows (32 keys per MFMA).  As a source
   // of the transposing read, lane (g, 4k + qd) reads channels 4qd..4qd+3
@@ -503,7 +517,7 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
     pv_step<T>(acc, __builtin_bit_cast(vec, u32x4{a0[0], a0[1], a1[0], a1[1]}),
                __builtin_bit_cast(vec, u32x4{b0[0], b0[1], b1[0], b1[1]}), pb);
   }
-  return finish<T>(acc, tci0 + qy < r.rc1 && tcj0 + qx < c.cc1);
+  return finish<T>(acc, tci0 + qy < r.rc1 && tcj0 + qx < c.cc1, lse);
 }
 
 // Writes a lane's TileOut to the query at in-plane byte offset off of out.
@@ -522,12 +536,22 @@ __device__ __forceinline__ void store_out(T *__restrict__ out, int64_t pofs, uns
   }
 }
 
+// Writes a query's log-sum-exp (one lane of its 4): with dense q its index in
+// [B, heads, H, W] order is its q byte offset over the pixel's D channels.
+template <typename T>
+__device__ __forceinline__ void store_lse(float *__restrict__ lse, int64_t pofs, unsigned off,
+                                          int g, const TileOut &t) {
+  if (g == 0 && t.ok) lse[(pofs + off) / (kHeadDim * sizeof(T))] = t.lse;
+}
+
 // STREAM: Q and out accesses are non-temporal (dense maps without dilation).
-template <typename T, int KS, int RY, bool STREAM>
+// LSE: each query's log-sum-exp goes to lse (dense q only).
+template <typename T, int KS, int RY, bool STREAM, bool LSE>
 __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
-    FastDiv fdil, FastDiv fnbx, FastDiv fnby, FastDiv fheads, int nblocks) {
+    FastDiv fdil, FastDiv fnbx, FastDiv fnby, FastDiv fheads, int nblocks,
+    float *__restrict__ lse) {
   using G = Geometry<KS, RY>;
   __shared__ __attribute__((aligned(16))) char kbuf0[G::PIX * 64], vbuf0[G::PIX * 64];
   __shared__ __attribute__((aligned(16))) char kbuf1[G::PIX * 64], vbuf1[G::PIX * 64];
@@ -581,8 +605,8 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     if (newtab) load_tables<T, KS, RY>(rpb, rnxt.h, tid, treg);
     if (more && rnxt.ok && cnxt.ok)
       stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, si, kn, vn, wave, lane);
-    res = TileOut{{0u, 0u, 0u, 0u}, false};
-    if (rcur.ok && ccur.ok) res = compute_tile<T, KS>(rcur, ccur, kc, vc, tc, qcur, lane);
+    res = TileOut{{0u, 0u, 0u, 0u}, false, 0.f};
+    if (rcur.ok && ccur.ok) res = compute_tile<T, KS, LSE>(rcur, ccur, kc, vc, tc, qcur, lane);
     if (!more) return;
     if (newtab) {
       store_tables<T, KS, RY>(tn, tid, has_rpb, treg);
@@ -594,6 +618,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     // (STREAM runs dense maps only: out has q's strides)
     if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
     else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
+    if constexpr (LSE) store_lse<T>(lse, rcur.pofs, pcur.q, g, res);
     rcur = rnxt;
     ccur = cnxt;
     pcur = pnxt;
@@ -609,6 +634,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   // the last block
   if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
   else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
+  if constexpr (LSE) store_lse<T>(lse, rcur.pofs, pcur.q, g, res);
 }
 
 // Compute units of the current device (queried once per device).
@@ -625,11 +651,13 @@ int device_cus() {
   return cache[dev];
 }
 
-// Host-side view of the strides of a launch: bytes, and whether q, k, v and
-// out are all dense [B, heads, H, W, D].
+// Host-side view of a launch's layout: strides in bytes, whether q, k, v and
+// out are all dense [B, heads, H, W, D], and the optional log-sum-exp output
+// (dense maps only).
 struct Layout {
   ByteStrides in, out;
   bool planar;
+  float *lse;
 };
 
 template <typename T, int KS, int RY>
@@ -644,12 +672,15 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
   // Non-temporal Q/out only when each line belongs to one block: dense maps
   // without dilation (channels-last maps interleave the heads' channels).
-  auto kernel = s.dil == 1 && lay.planar ? fused_mfma_kernel<T, KS, RY, true>
-                                         : fused_mfma_kernel<T, KS, RY, false>;
+  auto kernel = s.dil == 1 && lay.planar
+                    ? (lay.lse ? fused_mfma_kernel<T, KS, RY, true, true>
+                               : fused_mfma_kernel<T, KS, RY, true, false>)
+                    : (lay.lse ? fused_mfma_kernel<T, KS, RY, false, true>
+                               : fused_mfma_kernel<T, KS, RY, false, false>);
   kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, lay.in, lay.out,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
-      make_fastdiv((uint32_t)s.heads), (int)nblocks);
+      make_fastdiv((uint32_t)s.heads), (int)nblocks, lay.lse);
   return hipGetLastError();
 }
 
@@ -685,7 +716,7 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
                              const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
-                             hipStream_t st, bool *supported) {
+                             hipStream_t st, bool *supported, float *lse) {
   *supported = true;
   if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) {
     *supported = false;
@@ -693,12 +724,18 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
   }
   Layout lay;
   lay.planar = is_planar(in, s) && is_planar(out_st, s);
+  lay.lse = lse;
+  if (lse != nullptr && !is_planar(in, s)) {  // its index comes from q's dense offsets
+    *supported = false;
+    return hipSuccess;
+  }
   const int64_t elem = 2;
   if (!mfma::byte_strides(in, s, elem, &lay.in) || !mfma::byte_strides(out_st, s, elem, &lay.out)) {
     *supported = false;
     return hipSuccess;
   }
-  hipError_t e = launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, pad, dt, st, supported);
+  hipError_t e =
+      launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, pad, dt, st, supported, lse);
   if (*supported) return e;
   // the general kernel runs unpadded maps only
   if (pad.Hp > s.H || pad.Wp > s.W) {

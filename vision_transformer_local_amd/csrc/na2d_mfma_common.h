@@ -57,5 +57,24 @@ __device__ __forceinline__ float group_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Sum over the 4 lane groups (lanes l, l^16, l^32, l^48); every lane of a
+// group gets the same value.
+__device__ __forceinline__ float group_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Natural log-sum-exp of a query's window scores z = acc / sqrt(D) from the
+// softmax's reference mc = max(acc) * log2(e) / sqrt(D) and the sum l of
+// exp2(acc * log2(e) / sqrt(D) - mc) over the window (l >= 1: the maximum
+// contributes 1): ln sum exp(z) = (mc + log2 l) * ln 2.
+__device__ __forceinline__ float window_lse(float mc, float l) {
+  return (mc + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
 }  // namespace mfma
 }  // namespace na2d

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
                                                         const T *__restrict__ v,
                                                         const T *__restrict__ rpb,
                                                         T *__restrict__ out, Shape s,
-                                                        Strides si, Strides so, Pad pad) {
+                                                        Strides si, Strides so, Pad pad,
+                                                        float *__restrict__ lse) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= s.n_query) return;
   const QueryPos p = decode_query(t, s, pad.Hp, pad.Wp);
@@ -126,6 +127,8 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
       for (int e = 0; e < D; ++e) acc[e] = fmaf(pr, vr[e], acc[e]);
     }
   }
+  // t is the query's index in dense [B, heads, H, W] order
+  if (lse) lse[t] = m + logf(l);
   const float inv = 1.0f / l;
   T *o = out + bb * so.b + p.h * so.h + p.i * so.y + p.j * so.x;
 #pragma unroll
@@ -227,24 +230,24 @@ bool grid_for(int64_t work, int per_block, dim3 *grid) {
 
 hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const void *rpb,
                             void *out, const Shape &s, const Strides &in, const Strides &out_st,
-                            const Pad &pad, na2d_dtype_t dt, hipStream_t st) {
+                            const Pad &pad, na2d_dtype_t dt, hipStream_t st, float *lse) {
   dim3 grid;
   if (!grid_for(s.n_query, 256, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
     case NA2D_DTYPE_F32:
       fused_fma_kernel<float><<<grid, 256, 0, st>>>((const float *)q, (const float *)k,
                                                    (const float *)v, (const float *)rpb,
-                                                   (float *)out, s, in, out_st, pad);
+                                                   (float *)out, s, in, out_st, pad, lse);
       break;
     case NA2D_DTYPE_BF16:
       fused_fma_kernel<__bf16><<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
                                                     (const __bf16 *)v, (const __bf16 *)rpb,
-                                                    (__bf16 *)out, s, in, out_st, pad);
+                                                    (__bf16 *)out, s, in, out_st, pad, lse);
       break;
     case NA2D_DTYPE_F16:
       fused_fma_kernel<_Float16><<<grid, 256, 0, st>>>(
           (const _Float16 *)q, (const _Float16 *)k, (const _Float16 *)v, (const _Float16 *)rpb,
-          (_Float16 *)out, s, in, out_st, pad);
+          (_Float16 *)out, s, in, out_st, pad, lse);
       break;
   }
   return hipGetLastError();

@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.na2d_forward.restype = i
         L.na2d_forward.argtypes = [vp] * 5 + [i] * 8 + [vp]
         L.na2d_forward_algo.restype = i
+        L.na2d_forward_lse.restype = i
+        L.na2d_forward_lse.argtypes = [vp] * 6 + [i] * 8 + [vp]
         L.na2d_forward_algo.argtypes = [vp] * 5 + [i] * 9 + [vp]
         i64p = ctypes.POINTER(ctypes.c_int64)
         L.na2d_forward_strided.restype = i
@@ -140,6 +142,21 @@ def na2d_forward_algo(q, k, v, rpb, out, kernel_size: int, dilation: int, algo: 
                                  _DTYPE_CODES[q.dtype], ALGOS[algo], _stream(q))
     _check(st, "na2d_forward_algo")
     return out
+
+
+def na2d_forward_lse(q, k, v, rpb, out, lse, kernel_size: int, dilation: int):
+    """Fused forward into ``out`` plus each query's log-sum-exp into ``lse``
+    (fp32 [B, heads, H, W])."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, q.shape)
+    _need(lse, "lse", torch.float32, (B, heads, H, W))
+    _rpb_check(rpb, q, heads, kernel_size)
+    st = lib().na2d_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(out), _ptr(lse),
+                                B, heads, H, W, D, int(kernel_size), int(dilation),
+                                _DTYPE_CODES[q.dtype], _stream(q))
+    _check(st, "na2d_forward_lse")
+    return out, lse
 
 
 def heads_view(x: torch.Tensor, heads: int) -> torch.Tensor:
@@ -301,6 +318,14 @@ def na2d_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, workspace, kernel_size: 
 def forward(q, k, v, rpb, kernel_size: int, dilation: int, algo: str = "auto"):
     out = torch.empty_like(q)
     return na2d_forward_algo(q, k, v, rpb, out, kernel_size, dilation, algo)
+
+
+def forward_lse(q, k, v, rpb, kernel_size: int, dilation: int):
+    """Allocating forward that also returns the per-query log-sum-exp."""
+    B, heads, H, W, _ = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, heads, H, W), dtype=torch.float32, device=q.device)
+    return na2d_forward_lse(q, k, v, rpb, out, lse, kernel_size, dilation)
 
 
 def forward_unfused(q, k, v, rpb, kernel_size: int, dilation: int):
