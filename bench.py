@@ -186,6 +186,8 @@ def main(argv=None):
                          "[B, H, W, heads*D] through na2d_forward_strided")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-launch", type=int, default=100,
+                    help="eager steps timed one by one after the timed region (0: none)")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip timing the unfused path beside the fused forward")
     ap.add_argument("--no-copy-reference", action="store_true",
@@ -460,7 +462,8 @@ def time_steps(args, launch, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     del graph
-    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K, per_launch_us(launch, stream)
+    per_launch = per_launch_us(launch, stream, n=args.per_launch) if args.per_launch > 0 else None
+    return (t1 - t0) * 1e3 / K, ev0.elapsed_time(ev1) / K, per_launch
 
 
 def block_algorithmic_bytes(p) -> int:
