@@ -184,6 +184,9 @@ def main(argv=None):
     ap.add_argument("--layout", default="dense", choices=["dense", "channels_last"],
                     help="forward I/O layout: dense [B, heads, H, W, D], or channels-last "
                          "[B, H, W, heads*D] through na2d_forward_strided")
+    ap.add_argument("--lse", action="store_true",
+                    help="forward through na2d_forward_lse (also writes each query's fp32 "
+                         "log-sum-exp)")
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-launch", type=int, default=100,
@@ -242,6 +245,9 @@ def main(argv=None):
     if cl and args.padded:
         print("--padded takes the dense layout", file=sys.stderr)
         return 2
+    if args.lse and (cl or args.padded or args.path != "fused"):
+        print("--lse takes the fused path on the dense layout", file=sys.stderr)
+        return 2
     span = p.kernel_size * p.dilation
     if not args.padded and (p.H < span or p.W < span):
         print("workload %s needs --padded (map below kernel*dilation)" % args.workload,
@@ -269,6 +275,8 @@ def main(argv=None):
             out = torch.empty_like(q)
         attn = (torch.empty(p.shape[:4] + (p.kernel_size ** 2,), dtype=torch.float32,
                             device=dev) if args.path == "unfused" else None)
+        if args.lse:  # the per-query log-sum-exp output rides in the attn slot
+            attn = torch.empty(p.shape[:4], dtype=torch.float32, device=dev)
         reps.append((q, k, v, out, attn))
 
     gen = torch.Generator("cpu").manual_seed(500)
@@ -289,6 +297,10 @@ def main(argv=None):
             r = L.na2d_forward_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
                                       pad_k.data_ptr(), pad_v.data_ptr(), out.data_ptr(), B,
                                       heads, H, W, D, ks, dil, dt_code, st)
+        elif args.lse:
+            r = L.na2d_forward_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
+                                   out.data_ptr(), attn.data_ptr(), B, heads, H, W, D, ks, dil,
+                                   dt_code, st)
         elif cl:
             r = L.na2d_forward_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), rpb.data_ptr(),
                                        out.data_ptr(), B, heads, H, W, D, ks, dil, si, so,
@@ -312,18 +324,26 @@ def main(argv=None):
         ref = oracle.forward_padded(q0, k0, v0, rpb0, pad_k.cpu(), pad_v.cpu(), ks,
                                     dil).reshape(-1, D)[idx]
     else:
-        ref = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx)["out"]
+        r = oracle.forward(q0, k0, v0, rpb0, ks, dil, idx=idx, lse=args.lse)
+        ref = r["out"]
     got = reps[0][3].contiguous().reshape(-1, D)[torch.from_numpy(idx).to(dev)]
     got = got.double().cpu().numpy()
     max_err = float(np.abs(got - ref).max())
+    lse_err = None
+    if args.lse:
+        gl = reps[0][4].reshape(-1)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
+        lse_err = float(np.abs(gl - r["lse"]).max())
 
     value = p.n_query_heads / (ms_per_step / 1e3)
     abytes = algorithmic_bytes(p)
     if args.path == "unfused":
         abytes += 4 * p.n_query_heads * p.kernel_size ** 2 * 4  # fp32 attn w, r, w, r
+    if args.lse:
+        abytes += 4 * p.n_query_heads  # the fp32 log-sum-exp written
     achieved = abytes / (kernel_ms / 1e3) / 1e9
     traffic = measured_traffic(args.workload,
-                               "strided" if cl else ("padded" if args.padded else args.path))
+                               "strided" if cl else ("padded" if args.padded else
+                                                     ("lse" if args.lse else args.path)))
 
     rec = {
         "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
@@ -341,7 +361,7 @@ def main(argv=None):
         "config": {"workload": "%s: %s" % (args.workload, p.describe()),
                    "B": B, "heads": heads, "H": H, "W": W, "D": D,
                    "kernel_size": ks, "dilation": dil, "path": args.path,
-                   "layout": args.layout, "padded": args.padded,
+                   "layout": args.layout, "padded": args.padded, "lse": args.lse,
                    "timing": args.mode, "replicas": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -352,7 +372,9 @@ def main(argv=None):
         "sample_max_abs_err": max_err,
         "kernel_source_hash": kernel_source_hash(),
     }
-    if args.path == "fused" and not (cl or args.padded) and not args.no_unfused:
+    if args.lse:
+        rec["sample_max_abs_err_lse"] = lse_err
+    if args.path == "fused" and not (cl or args.padded or args.lse) and not args.no_unfused:
         rec["unfused"] = unfused_beside(args, p, dev, L, cpu)
     if not args.no_copy_reference:
         copy_gbs = copy_bandwidth(dev)
