@@ -202,22 +202,36 @@ __device__ __forceinline__ typename Mma<T>::vec halo_tr(const char *buf, int r0,
   return __builtin_bit_cast(typename Mma<T>::vec, u32x4{a[0], a[1], c[0], c[1]});
 }
 
+// x, made opaque to the optimiser where it is defined.  Values that are later
+// split by split_operand go through this: otherwise the compiler may fold the
+// product that made x into mixed-precision FMAs for one of the two roundings
+// only (fp16), and hi + lo then misses x by a 16-bit ulp.  Pinning at the
+// definition (rather than inside the split) costs no copies when x stays live.
+__device__ __forceinline__ float pinned(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // 16-bit B operand (rows 2j, 2j+1 of a tile) split into a rounded head and
-// the rounded remainder: hi + lo equals x to about 16 significant bits.  The
-// fp32 values are pinned first: otherwise the compiler may fold the product
-// that made them into mixed-precision FMAs for one of the two roundings
-// only (fp16), and hi + lo then misses x by a 16-bit ulp.
+// the rounded remainder: hi + lo equals x to about 16 significant bits.  Two
+// values at a time: one packed conversion gives both heads, whose fp32 values
+// come back exactly from the packed bits, and one packed conversion the two
+// remainders.  The inputs must come from pinned().
 template <typename T>
 __device__ __forceinline__ void split_operand(f32x4 s0, f32x4 s1, typename Mma<T>::vec &hi,
                                               typename Mma<T>::vec &lo) {
+  typedef __attribute__((ext_vector_type(2))) T t2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    asm volatile("" : "+v"(s0[i]), "+v"(s1[i]));
-    const T h0 = static_cast<T>(s0[i]), h1 = static_cast<T>(s1[i]);
-    hi[i] = h0;
-    hi[4 + i] = h1;
-    lo[i] = static_cast<T>(s0[i] - static_cast<float>(h0));
-    lo[4 + i] = static_cast<T>(s1[i] - static_cast<float>(h1));
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 &src = j < 2 ? s0 : s1;
+    const int e = 2 * (j & 1), o = 4 * (j >> 1) + e;  // source element, operand slot
+    const f32x2 x = {src[e], src[e + 1]};
+    const t2 h = __builtin_convertvector(x, t2);
+    const t2 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), t2);
+    hi[o] = h[0];
+    hi[o + 1] = h[1];
+    lo[o] = l[0];
+    lo[o + 1] = l[1];
   }
 }
 
@@ -397,14 +411,14 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
       }
     l = group_sum(l);
     pd = group_sum(pd);
-    const float inv = 1.0f / l;
-    const float dqd = pd * inv;  // Dq = sum P dP
+    const float inv = __builtin_amdgcn_rcpf(l);  // l >= 1 (the maximum contributes 1)
+    const float dqd = pd * inv;                   // Dq = sum P dP
     const float ninvd = -inv * dqd;
     // dS = P (dP - Dq) = p (inv dP - inv Dq)
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dp[a][i] = sc[a][i] * fmaf(dp[a][i], inv, ninvd);
+      for (int i = 0; i < 4; ++i) dp[a][i] = pinned(sc[a][i] * fmaf(dp[a][i], inv, ninvd));
     // dq^T = K^T . dS^T over pairs of key rows
     f32x4 o0 = zero, o1 = zero;
     const int tc = lc0 + 4 * g + (ql >> 2);
@@ -600,8 +614,8 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_key_mfma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x2 ld = lr[lcol[i]];
-        P[u][i] = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ld[0]));
-        dS[u][i] = P[u][i] * (dpv[i] - ld[1]);
+        P[u][i] = pinned(__builtin_amdgcn_exp2f(fmaf(sv[i], c2, -ld[0])));
+        dS[u][i] = pinned(P[u][i] * (dpv[i] - ld[1]));
       }
     }
     typename Mma<T>::vec phi, plo, shi, slo;
