@@ -136,52 +136,220 @@ __global__ __launch_bounds__(256) void fused_fma_kernel(const T *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Unfused step 1: one lane per (query, neighbour slot); slot fastest so the
-// fp32 score stores are contiguous.
+// Unfused path.  Each workgroup owns a run of query pixels of one (batch,
+// head) plane: the plane comes from the workgroup id (one fixed-divisor
+// division per workgroup), the pixel from the lane, so no lane divides a
+// 64-bit index.  Planes must hold fewer than 2^31 pixels.
+
+typedef __attribute__((ext_vector_type(4))) float f32x4v;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v;
+
+// Workgroup numbering of an unfused launch: `per` queries per workgroup,
+// `chunks` workgroups per plane.
+struct UnfusedGrid {
+  FastDiv chunks, W, dil, heads, ks;
+  int per;
+};
+
+// Sub-grid position and window of in-plane pixel pix (32-bit arithmetic).
+struct PixPos {
+  int i, j, ry, rx, ci, cj, sy, sx;
+};
+
+__device__ __forceinline__ PixPos decode_pixel(int pix, const Shape &s, const UnfusedGrid &g) {
+  PixPos p;
+  p.i = (int)fast_div((uint32_t)pix, g.W);
+  p.j = pix - p.i * s.W;
+  p.ci = (int)fast_div((uint32_t)p.i, g.dil);
+  p.ry = p.i - p.ci * s.dil;
+  p.cj = (int)fast_div((uint32_t)p.j, g.dil);
+  p.rx = p.j - p.cj * s.dil;
+  const int Ly = (int)fast_div((uint32_t)(s.H - p.ry + s.dil - 1), g.dil);
+  const int Lx = (int)fast_div((uint32_t)(s.W - p.rx + s.dil - 1), g.dil);
+  p.sy = window_start(p.ci, Ly, s.ks);
+  p.sx = window_start(p.cj, Lx, s.ks);
+  return p;
+}
+
+// Dot product of eight consecutive channels: 16-bit data two channels per
+// instruction (fp32 accumulation), fp32 data one fused multiply-add per
+// channel.  (The 32-bit words are copied out of their vectors before the bit
+// cast: casting a vector element in place was compiled as if every element
+// were the first.)
+template <typename T> struct Dot8;
+template <> struct Dot8<float> {
+  f32x4v lo, hi;
+  __device__ __forceinline__ void load(const float *p) {
+    lo = ((const f32x4v *)p)[0];
+    hi = ((const f32x4v *)p)[1];
+  }
+  __device__ __forceinline__ float dot(const float *k) const {
+    const f32x4v a = ((const f32x4v *)k)[0], b = ((const f32x4v *)k)[1];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(lo[i], a[i], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(hi[i], b[i], acc);
+    return acc;
+  }
+};
+template <typename T> struct Dot8Half {
+  u32x4v r;
+  __device__ __forceinline__ void load(const T *p) { r = *(const u32x4v *)p; }
+  __device__ __forceinline__ float dot(const T *k) const {
+    const u32x4v kv = *(const u32x4v *)k;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned int qw = r[i], kw = kv[i];
+      if constexpr (sizeof(T) == 2 && __is_same(T, __bf16))
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, qw),
+                                              __builtin_bit_cast(bf16x2v, kw), acc, false);
+      else
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2v, qw), __builtin_bit_cast(f16x2v, kw),
+                                     acc, false);
+    }
+    return acc;
+  }
+};
+template <> struct Dot8<__bf16> : Dot8Half<__bf16> {};
+template <> struct Dot8<_Float16> : Dot8Half<_Float16> {};
+
+// Sum over the 4 lanes of a quad (lanes 4m .. 4m+3); every lane gets it.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// Eight consecutive channels, widened to fp32 / narrowed with RNE.
 template <typename T>
+__device__ __forceinline__ void load8(const T *p, float (&f)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    const f32x4v a = ((const f32x4v *)p)[0], b = ((const f32x4v *)p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = a[i];
+      f[4 + i] = b[i];
+    }
+  } else {
+    typedef __attribute__((ext_vector_type(8))) T t8;
+    const t8 w = *(const t8 *)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(w[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float (&f)[8]) {
+  if constexpr (sizeof(T) == 4) {
+    ((f32x4v *)p)[0] = f32x4v{f[0], f[1], f[2], f[3]};
+    ((f32x4v *)p)[1] = f32x4v{f[4], f[5], f[6], f[7]};
+  } else {
+    typedef __attribute__((ext_vector_type(8))) T t8;
+    t8 w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = static_cast<T>(f[i]);
+    *(t8 *)p = w;
+  }
+}
+
+// The k*k scores of the query at in-plane pixel pix, for lane j of its quad
+// (see qkrpb_kernel): lane j writes the scores of window columns c = j
+// (mod 4) to out[a*k + c].
+template <typename T, int KS>
+__device__ __forceinline__ void score_window(const T *__restrict__ q, const T *__restrict__ k,
+                                             const T *__restrict__ rpb, const Shape &s,
+                                             const UnfusedGrid &g, uint32_t plane, int hw,
+                                             int pix, int j, float *out) {
+  const PixPos p = decode_pixel(pix, s, g);
+  const int h = (int)(plane - fast_div(plane, g.heads) * (uint32_t)s.heads);
+  const int64_t pq = (int64_t)plane * hw + pix;  // query index
+  Dot8<T> qs;
+  qs.load(q + pq * D + 8 * j);
+  const T *kp = k + ((int64_t)plane * hw + p.rx + p.sx * s.dil) * D + 8 * j;
+  const int64_t step = (int64_t)s.dil * D;
+  constexpr int side = 2 * KS - 1;
+  const T *br = rpb != nullptr ? rpb + ((int64_t)h * side + (p.sy - p.ci + KS - 1)) * side +
+                                     (p.sx - p.cj + KS - 1)
+                               : nullptr;
+  const float scale = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int a = 0; a < KS; ++a) {
+    const T *kr = kp + (int64_t)(p.ry + (p.sy + a) * s.dil) * s.W * D;
+    float dot[KS];
+#pragma unroll
+    for (int c = 0; c < KS; ++c) dot[c] = quad_sum(qs.dot(kr + c * step));
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      if ((c & 3) == j) {
+        const float bias = br != nullptr ? Elem<T>::to_f(br[a * side + c]) : 0.f;
+        out[a * KS + c] = dot[c] * scale + bias;
+      }
+    }
+  }
+}
+
+// Unfused step 1 (scores + bias): a quad of lanes per query, lane j of the
+// quad owning channels 8j .. 8j+7, so that a load instruction reads whole
+// 64-byte key pixels of consecutive queries; the quad sums its partial dot
+// products, and lane j puts the scores of window columns c = j (mod 4) into
+// LDS, from where the workgroup writes its 64 queries' score rows
+// (contiguous in attn) with consecutive lanes on consecutive floats.  KS = k
+// (the window loops unroll).
+template <typename T, int KS>
 __global__ __launch_bounds__(256) void qkrpb_kernel(const T *__restrict__ q,
                                                     const T *__restrict__ k,
                                                     const T *__restrict__ rpb,
-                                                    float *__restrict__ attn, Shape s) {
-  const int nk = s.ks * s.ks;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= s.n_query * nk) return;
-  const int64_t qi = t / nk;
-  const int n = (int)(t - qi * nk);
-  const int a = n / s.ks, c = n - a * s.ks;
-  const QueryPos p = decode_query(qi, s);
-  const int64_t hw = (int64_t)s.H * s.W;
-  const int row = p.ry + (p.sy + a) * s.dil;
-  const int col = p.rx + (p.sx + c) * s.dil;
-  const T *kr = k + p.plane * hw * D + ((int64_t)row * s.W + col) * D;
-  const T *qr = q + qi * D;
-  float dot = 0.f;
-#pragma unroll
-  for (int e = 0; e < D; ++e) dot = fmaf(Elem<T>::to_f(qr[e]), Elem<T>::to_f(kr[e]), dot);
-  attn[t] = dot * (1.0f / sqrtf((float)D)) + bias_of(rpb, p, s, a, c);
+                                                    float *__restrict__ attn, Shape s,
+                                                    UnfusedGrid g) {
+  constexpr int KK = KS * KS;
+  __shared__ float rows[64 * KK];
+  const int tid = threadIdx.x, j = tid & 3, lq = tid >> 2;
+  const uint32_t plane = fast_div(blockIdx.x, g.chunks);
+  const int chunk = (int)(blockIdx.x - plane * g.chunks.div);
+  const int hw = s.H * s.W;
+  const int nq = min(64, hw - chunk * 64);  // queries of this workgroup
+  if (lq < nq)  // whole quads take the same branch
+    score_window<T, KS>(q, k, rpb, s, g, plane, hw, chunk * 64 + lq, j, rows + lq * KK);
+  __syncthreads();
+  float *dst = attn + ((int64_t)plane * hw + chunk * 64) * KK;
+  for (int e = tid; e < nq * KK; e += 256) dst[e] = rows[e];
 }
 
-// Unfused step 2: 64 rows per workgroup staged through LDS so that global
-// loads and stores are contiguous; one lane finishes one row.
-constexpr int kSoftmaxRows = 64;
+// Unfused step 2 (softmax over the last axis): a workgroup of 256 lanes
+// stages `rows` rows of k*k scores into LDS with direct global->LDS copies
+// (4 bytes per lane, contiguous), one lane finishes one row (odd row lengths
+// spread the lanes over distinct banks), and the workgroup writes the rows
+// back contiguously.
+constexpr int kSoftmaxThreads = 256;
 
-__global__ __launch_bounds__(kSoftmaxRows) void softmax_kernel(const float *__restrict__ in,
-                                                               float *__restrict__ out,
-                                                               int64_t rows, int nk) {
-  extern __shared__ float buf[];  // kSoftmaxRows * nk
-  const int64_t r0 = (int64_t)blockIdx.x * kSoftmaxRows;
-  const int nrows = rows - r0 < kSoftmaxRows ? (int)(rows - r0) : kSoftmaxRows;
+__global__ __launch_bounds__(kSoftmaxThreads) void softmax_kernel(const float *__restrict__ in,
+                                                                  float *__restrict__ out,
+                                                                  int64_t nrows_total, int nk,
+                                                                  int rows) {
+  extern __shared__ float buf[];  // rows * nk
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * rows;
+  const int nrows = nrows_total - r0 < rows ? (int)(nrows_total - r0) : rows;
   const int n = nrows * nk;
   const float *src = in + r0 * nk;
-  for (int e = threadIdx.x; e < n; e += kSoftmaxRows) buf[e] = src[e];
-  __syncthreads();
-  if ((int)threadIdx.x < nrows) {
-    float *row = buf + threadIdx.x * nk;  // nk is odd: rows hit distinct banks
+  // lane l of a copy lands 4 l bytes past the wave's (uniform) LDS address
+  const int lane = tid & 63, wbase = __builtin_amdgcn_readfirstlane(tid >> 6) * 64;
+  for (int e0 = wbase; e0 < n; e0 += kSoftmaxThreads)
+    if (e0 + lane < n)
+      __builtin_amdgcn_global_load_lds((const void *)(src + e0 + lane),
+                                       (__attribute__((address_space(3))) void *)(buf + e0), 4,
+                                       0, 0);
+  __syncthreads();  // also completes the copies
+  if (tid < nrows) {
+    float *row = buf + tid * nk;
     float m = -INFINITY;
     for (int e = 0; e < nk; ++e) m = fmaxf(m, row[e]);
     float sum = 0.f;
     for (int e = 0; e < nk; ++e) {
-      const float x = expf(row[e] - m);
+      const float x = __expf(row[e] - m);
       row[e] = x;
       sum += x;
     }
@@ -190,32 +358,112 @@ __global__ __launch_bounds__(kSoftmaxRows) void softmax_kernel(const float *__re
   }
   __syncthreads();
   float *dst = out + r0 * nk;
-  for (int e = threadIdx.x; e < n; e += kSoftmaxRows) dst[e] = buf[e];
+  for (int e = tid; e < n; e += kSoftmaxThreads) dst[e] = buf[e];
 }
 
-// Unfused step 3: one lane per (query, channel); the 32 lanes of a query read
-// one contiguous value row per neighbour and share the probability.
-template <typename T>
+// Unfused step 3 (weighted sum of values): four lanes per query, eight
+// channels each (16- or 32-byte value reads); 64 queries per workgroup,
+// whose probability rows (contiguous in attn) are first copied into LDS with
+// direct global->LDS copies.  KS = k: a window row's value loads issue
+// together.
+template <typename T, int KS>
 __global__ __launch_bounds__(256) void av_kernel(const float *__restrict__ attn,
                                                  const T *__restrict__ v,
-                                                 T *__restrict__ out, Shape s) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= s.n_query * D) return;
-  const int64_t qi = t / D;
-  const int e = (int)(t - qi * D);
-  const QueryPos p = decode_query(qi, s);
-  const int64_t hw = (int64_t)s.H * s.W;
-  const T *vp = v + p.plane * hw * D + e;
-  const float *pr = attn + qi * s.ks * s.ks;
-  float acc = 0.f;
-  for (int a = 0; a < s.ks; ++a) {
+                                                 T *__restrict__ out, Shape s, UnfusedGrid g) {
+  constexpr int KK = KS * KS;
+  __shared__ float prob[64 * KK];
+  const int tid = threadIdx.x;
+  const uint32_t plane = fast_div(blockIdx.x, g.chunks);
+  const int chunk = (int)(blockIdx.x - plane * g.chunks.div);
+  const int hw = s.H * s.W;
+  const int nq = min(64, hw - chunk * 64);  // queries of this workgroup
+  {
+    // lane l of a copy lands 4 l bytes past the wave's (uniform) LDS address
+    const float *src = attn + ((int64_t)plane * hw + chunk * 64) * KK;
+    const int lane = tid & 63, wbase = __builtin_amdgcn_readfirstlane(tid >> 6) * 64;
+    for (int e0 = wbase; e0 < nq * KK; e0 += 256)
+      if (e0 + lane < nq * KK)
+        __builtin_amdgcn_global_load_lds((const void *)(src + e0 + lane),
+                                         (__attribute__((address_space(3))) void *)(prob + e0),
+                                         4, 0, 0);
+  }
+  __syncthreads();  // also completes the copies
+  const int lq = tid >> 2;
+  if (lq >= nq) return;
+  const int pix = chunk * 64 + lq;
+  const int part = tid & 3;  // channels 8 part .. 8 part + 7
+  const PixPos p = decode_pixel(pix, s, g);
+  const int64_t pq = (int64_t)plane * hw + pix;
+  const float *pr = prob + lq * KK;
+  const T *vp = v + ((int64_t)plane * hw + p.rx + p.sx * s.dil) * D + 8 * part;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  const int64_t step = (int64_t)s.dil * D;
+  for (int a = 0; a < KS; ++a) {
     const int row = p.ry + (p.sy + a) * s.dil;
-    for (int c = 0; c < s.ks; ++c) {
-      const int col = p.rx + (p.sx + c) * s.dil;
-      acc = fmaf(pr[a * s.ks + c], Elem<T>::to_f(vp[((int64_t)row * s.W + col) * D]), acc);
+    const T *vr = vp + (int64_t)row * s.W * D;
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      const float w = pr[a * KS + c];
+      float f[8];
+      load8<T>(vr + c * step, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, f[i], acc[i]);
     }
   }
-  out[t] = Elem<T>::from_f(acc);
+  store8<T>(out + pq * D + 8 * part, acc);
+}
+
+// Launch functors: run<KS>() launches the kernel instantiated for k = KS.
+template <typename T> struct QkrpbLaunch {
+  template <int KS>
+  static void run(dim3 grid, hipStream_t st, const void *q, const void *k, const void *rpb,
+                  float *attn, const Shape &s, const UnfusedGrid &g) {
+    qkrpb_kernel<T, KS><<<grid, 256, 0, st>>>((const T *)q, (const T *)k, (const T *)rpb, attn,
+                                               s, g);
+  }
+};
+template <typename T> struct AvLaunch {
+  template <int KS>
+  static void run(dim3 grid, hipStream_t st, const float *attn, const void *v, void *out,
+                  const Shape &s, const UnfusedGrid &g) {
+    av_kernel<T, KS><<<grid, 256, 0, st>>>(attn, (const T *)v, (T *)out, s, g);
+  }
+};
+
+// Dispatches an odd kernel size 1..13 to its instantiation.
+template <typename L, typename... A>
+hipError_t launch_ks(int ks, dim3 grid, hipStream_t st, A... args) {
+  switch (ks) {
+    case 1: L::template run<1>(grid, st, args...); break;
+    case 3: L::template run<3>(grid, st, args...); break;
+    case 5: L::template run<5>(grid, st, args...); break;
+    case 7: L::template run<7>(grid, st, args...); break;
+    case 9: L::template run<9>(grid, st, args...); break;
+    case 11: L::template run<11>(grid, st, args...); break;
+    case 13: L::template run<13>(grid, st, args...); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Workgroups of an unfused launch with `per` queries each, or false when
+// the plane or the grid is too large for 32-bit workgroup arithmetic.
+bool unfused_grid(const Shape &s, int per, UnfusedGrid *g, dim3 *grid) {
+  const int64_t hw = (int64_t)s.H * s.W;
+  if (hw >= ((int64_t)1 << 31)) return false;
+  const int64_t chunks = (hw + per - 1) / per;
+  const int64_t planes = (int64_t)s.B * s.heads;
+  if (planes * chunks > INT32_MAX) return false;
+  g->chunks = make_fastdiv((uint32_t)chunks);
+  g->W = make_fastdiv((uint32_t)s.W);
+  g->dil = make_fastdiv((uint32_t)s.dil);
+  g->heads = make_fastdiv((uint32_t)s.heads);
+  g->ks = make_fastdiv((uint32_t)s.ks);
+  g->per = per;
+  *grid = dim3((unsigned)(planes * chunks));
+  return true;
 }
 
 // 1-D grid of 256-lane workgroups over `work` items, or false when too large.
@@ -255,50 +503,43 @@ hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const v
 
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st) {
+  UnfusedGrid g;
   dim3 grid;
-  if (!grid_for(s.n_query * s.ks * s.ks, 256, &grid)) return hipErrorInvalidConfiguration;
+  if (!unfused_grid(s, 64, &g, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
-    case NA2D_DTYPE_F32:
-      qkrpb_kernel<float><<<grid, 256, 0, st>>>((const float *)q, (const float *)k,
-                                               (const float *)rpb, attn, s);
-      break;
+    case NA2D_DTYPE_F32: return launch_ks<QkrpbLaunch<float>>(s.ks, grid, st, q, k, rpb, attn, s, g);
     case NA2D_DTYPE_BF16:
-      qkrpb_kernel<__bf16><<<grid, 256, 0, st>>>((const __bf16 *)q, (const __bf16 *)k,
-                                                (const __bf16 *)rpb, attn, s);
-      break;
+      return launch_ks<QkrpbLaunch<__bf16>>(s.ks, grid, st, q, k, rpb, attn, s, g);
     case NA2D_DTYPE_F16:
-      qkrpb_kernel<_Float16><<<grid, 256, 0, st>>>((const _Float16 *)q, (const _Float16 *)k,
-                                                  (const _Float16 *)rpb, attn, s);
-      break;
+      return launch_ks<QkrpbLaunch<_Float16>>(s.ks, grid, st, q, k, rpb, attn, s, g);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_softmax(const float *in, float *out, const Shape &s, hipStream_t st) {
-  dim3 grid;
-  if (!grid_for(s.n_query, kSoftmaxRows, &grid)) return hipErrorInvalidConfiguration;
   const int nk = s.ks * s.ks;
-  const size_t lds = sizeof(float) * kSoftmaxRows * nk;
-  softmax_kernel<<<grid, kSoftmaxRows, lds, st>>>(in, out, s.n_query, nk);
+  // rows per workgroup: as many as 64 KB of LDS holds, 64 to 256
+  int rows = kSoftmaxThreads;
+  while (rows > 64 && (int64_t)rows * nk * 4 > 64 * 1024) rows /= 2;
+  const int64_t blocks = (s.n_query + rows - 1) / rows;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const size_t lds = sizeof(float) * rows * nk;
+  softmax_kernel<<<dim3((unsigned)blocks), kSoftmaxThreads, lds, st>>>(in, out, s.n_query, nk,
+                                                                       rows);
   return hipGetLastError();
 }
 
 hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s,
                      na2d_dtype_t dt, hipStream_t st) {
+  UnfusedGrid g;
   dim3 grid;
-  if (!grid_for(s.n_query * D, 256, &grid)) return hipErrorInvalidConfiguration;
+  if (!unfused_grid(s, 64, &g, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
-    case NA2D_DTYPE_F32:
-      av_kernel<float><<<grid, 256, 0, st>>>(attn, (const float *)v, (float *)out, s);
-      break;
-    case NA2D_DTYPE_BF16:
-      av_kernel<__bf16><<<grid, 256, 0, st>>>(attn, (const __bf16 *)v, (__bf16 *)out, s);
-      break;
-    case NA2D_DTYPE_F16:
-      av_kernel<_Float16><<<grid, 256, 0, st>>>(attn, (const _Float16 *)v, (_Float16 *)out, s);
-      break;
+    case NA2D_DTYPE_F32: return launch_ks<AvLaunch<float>>(s.ks, grid, st, attn, v, out, s, g);
+    case NA2D_DTYPE_BF16: return launch_ks<AvLaunch<__bf16>>(s.ks, grid, st, attn, v, out, s, g);
+    case NA2D_DTYPE_F16: return launch_ks<AvLaunch<_Float16>>(s.ks, grid, st, attn, v, out, s, g);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace na2d
