@@ -40,7 +40,8 @@
  *    NULL or not 16-byte aligned; dtype or algorithm not in its enum;
  *    overlapping output and input; B*heads*H*W*max(D, k*k) beyond 2^60.
  *  NA2D_ERROR_NOT_SUPPORTED: a valid problem this build does not implement:
- *    D != 32, kernel_size > 13, or more than 2^31-1 workgroups.
+ *    D != 32, kernel_size > 13, more than 2^31-1 workgroups, or (na2d_qkrpb,
+ *    na2d_av) a (batch, head) plane of 2^31 pixels or more.
  *  NA2D_ERROR_LAUNCH_FAILURE: the HIP runtime refused a launch.
  */
 #ifndef NA2D_H
