@@ -230,7 +230,7 @@ __device__ __forceinline__ QueryOffs query_offsets(const RowPart &r, const ColPa
 // global->LDS path: 16 bytes per lane, lane i of an instruction lands at
 // base + 16*i, so each instruction fills 64 consecutive 16-byte slots.  Slot
 // (pixel, p) of the buffer holds logical chunk p ^ swz(column) of the pixel.
-template <typename T, int KS, int RY>
+template <typename T, int KS, int RY, bool WITH_V = true>
 __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__restrict__ v,
                                             const RowPart &r, const ColPart &c, const Shape &s,
                                             const ByteStrides &si, char *kbuf, char *vbuf,
@@ -257,15 +257,17 @@ __device__ __forceinline__ void stage_block(const T *__restrict__ k, const T *__
         const unsigned roff = (unsigned)min(row, r.HR - 1) * rowb;
         __builtin_amdgcn_global_load_lds((const void *)((kb0 + roff) + coff),
                                          (lds_void *)(kbuf + row * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)((vb0 + roff) + coff),
-                                         (lds_void *)(vbuf + row * 1024), 16, 0, 0);
+        if constexpr (WITH_V)
+          __builtin_amdgcn_global_load_lds((const void *)((vb0 + roff) + coff),
+                                           (lds_void *)(vbuf + row * 1024), 16, 0, 0);
       }
     }
   } else {
+    constexpr int NT = WITH_V ? 2 * NI : NI;  // copies (K, then V)
 #pragma unroll
-    for (int j = 0; j < (2 * NI + NW - 1) / NW; ++j) {
+    for (int j = 0; j < (NT + NW - 1) / NW; ++j) {
       const int ins = wave + j * NW;
-      if (ins < 2 * NI) {
+      if (ins < NT) {
         const bool isv = ins >= NI;
         const int slot = (isv ? ins - NI : ins) * 64 + lane;
         const int pix = slot >> 2, pch = slot & 3;
@@ -420,12 +422,24 @@ __device__ __forceinline__ TileOut finish(const PVAcc &acc, bool ok, float lse) 
   return TileOut{{w0[0], w0[1], w1[0], w1[1]}, ok, lse};
 }
 
-// One 16-query tile of a block (this wave's), from one LDS buffer; LSE: also
-// the query's log-sum-exp.
-template <typename T, int KS, bool LSE>
+// What a launch of the general kernel computes.
+enum Mode { kForward = 0, kForwardLse = 1, kScores = 2 };
+
+constexpr float kInvSqrtD = 0.17677669529663687f;  // 1 / sqrt(32)
+
+// One 16-query tile of a block (this wave's), from one LDS buffer.
+// kForwardLse: also the query's log-sum-exp.  kScores: only the scores
+// q.k / sqrt(D) + bias of the window, written to scores ([.., k*k] fp32,
+// dense query order; qbase = the plane's first query) through this wave's
+// LDS area stage (16 k*k floats); nothing is returned.
+template <typename T, int KS, int MODE>
 __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart &c,
                                                 const char *kbuf, const char *vbuf,
-                                                const float *tab, u32x4 qraw, int lane) {
+                                                const float *tab, u32x4 qraw, int lane,
+                                                float *stage = nullptr,
+                                                float *__restrict__ scores = nullptr,
+                                                int64_t qbase = 0, int W = 0, int dil = 1) {
+  constexpr bool LSE = MODE == kForwardLse;
   using G = Geometry<KS>;
   using vec = typename Mma<T>::vec;
   constexpr int TY = G::TY, TX = G::TX, NB = G::NB, SIDE = G::SIDE, HCM = G::HCM;
@@ -481,6 +495,34 @@ __device__ __forceinline__ TileOut compute_tile(const RowPart &r, const ColPart 
                        : fminf(bb[a * SIDE + i], ccap[i]);
       sc[a] = Mma<T>::run(__builtin_bit_cast(vec, kb[a * HCM * 4]), qv, cin);
     }
+  }
+
+  if constexpr (MODE == kScores) {
+    // the in-window entries to the wave's LDS rows (one per query), then
+    // the 16 rows out with consecutive lanes on consecutive floats
+    constexpr int KK = KS * KS;
+    const int ci = min(tci0 + qy, r.rc1 - 1), cj = min(tcj0 + qx, c.cc1 - 1);
+    const int sy = window_start(ci, r.Ly, KS), sx = window_start(cj, c.Lx, KS);
+    float *row = stage + ql * KK;
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const int wa = Y0 + a - sy;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int wc = X0 + 4 * g + i - sx;
+        if ((unsigned)wa < (unsigned)KS && (unsigned)wc < (unsigned)KS)
+          row[wa * KS + wc] = sc[a][i] * kInvSqrtD;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < 16 * KK; e += 64) {
+      const int qq = e / KK, slot = e - qq * KK;
+      const int qci = tci0 + qq / TX, qcj = tcj0 + qq % TX;
+      if (qci < r.rc1 && qcj < c.cc1)
+        scores[(qbase + (int64_t)(r.ry + qci * dil) * W + c.rx + qcj * dil) * KK + slot] = stage[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    return TileOut{{0u, 0u, 0u, 0u}, false, 0.f};
   }
 
   const float mc = softmax_weights<KS>(sc);
@@ -545,14 +587,21 @@ __device__ __forceinline__ void store_lse(float *__restrict__ lse, int64_t pofs,
 }
 
 // STREAM: Q and out accesses are non-temporal (dense maps without dilation).
-// LSE: each query's log-sum-exp goes to lse (dense q only).
-template <typename T, int KS, int RY, bool STREAM, bool LSE>
+// MODE (dense q only beyond kForward): kForwardLse also writes each query's
+// log-sum-exp to lse; kScores writes only the scores, to lse as a [.., k*k]
+// tensor (no V staged, no out).
+template <typename T, int KS, int RY, bool STREAM, int MODE>
 __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, Shape s, ByteStrides si, ByteStrides so,
     FastDiv fdil, FastDiv fnbx, FastDiv fnby, FastDiv fheads, int nblocks,
     float *__restrict__ lse) {
   using G = Geometry<KS, RY>;
+  constexpr bool LSE = MODE == kForwardLse, SCORES = MODE == kScores;
+  // kScores: each wave's score rows go through the free V buffers, half of
+  // the waves in each
+  constexpr int HALF = (G::NTILE + 1) / 2;
+  static_assert(!SCORES || HALF * 16 * KS * KS * 4 <= G::PIX * 64, "score staging exceeds LDS");
   __shared__ __attribute__((aligned(16))) char kbuf0[G::PIX * 64], vbuf0[G::PIX * 64];
   __shared__ __attribute__((aligned(16))) char kbuf1[G::PIX * 64], vbuf1[G::PIX * 64];
   __shared__ float tab0[G::NTAB], tab1[G::NTAB];
@@ -584,8 +633,10 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   u32x4 qcur = load_q<T, STREAM>(q, rcur.pofs, pcur.q, g);
   load_tables<T, KS, RY>(rpb, rcur.h, tid, treg);
   if (rcur.ok && ccur.ok)
-    stage_block<T, KS, RY>(k, v, rcur, ccur, s, si, kbuf0, vbuf0, wave, lane);
+    stage_block<T, KS, RY, !SCORES>(k, v, rcur, ccur, s, si, kbuf0, vbuf0, wave, lane);
   store_tables<T, KS, RY>(tab0, tid, has_rpb, treg);
+  float *const stage =
+      SCORES ? (float *)(wave < HALF ? vbuf0 : vbuf1) + (wave % HALF) * 16 * KS * KS : nullptr;
   int tab_h0 = rcur.h, tab_h1 = -1;  // head whose tables each buffer holds
   __syncthreads();
 
@@ -604,9 +655,11 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     const bool newtab = more && rnxt.h != tab_hn;
     if (newtab) load_tables<T, KS, RY>(rpb, rnxt.h, tid, treg);
     if (more && rnxt.ok && cnxt.ok)
-      stage_block<T, KS, RY>(k, v, rnxt, cnxt, s, si, kn, vn, wave, lane);
+      stage_block<T, KS, RY, !SCORES>(k, v, rnxt, cnxt, s, si, kn, vn, wave, lane);
     res = TileOut{{0u, 0u, 0u, 0u}, false, 0.f};
-    if (rcur.ok && ccur.ok) res = compute_tile<T, KS, LSE>(rcur, ccur, kc, vc, tc, qcur, lane);
+    if (rcur.ok && ccur.ok)
+      res = compute_tile<T, KS, MODE>(rcur, ccur, kc, vc, tc, qcur, lane, stage, lse,
+                                      rcur.pofs / (kHeadDim * (int64_t)sizeof(T)), s.W, s.dil);
     if (!more) return;
     if (newtab) {
       store_tables<T, KS, RY>(tn, tid, has_rpb, treg);
@@ -617,7 +670,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     // the next block's loads but not these stores
     // (STREAM runs dense maps only: out has q's strides)
     if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
-    else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
+    else if constexpr (!SCORES) store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
     if constexpr (LSE) store_lse<T>(lse, rcur.pofs, pcur.q, g, res);
     rcur = rnxt;
     ccur = cnxt;
@@ -633,7 +686,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   }
   // the last block
   if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
-  else store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
+  else if constexpr (!SCORES) store_out<T, STREAM>(out, rcur.opofs, pcur.o, g, res);
   if constexpr (LSE) store_lse<T>(lse, rcur.pofs, pcur.q, g, res);
 }
 
@@ -652,12 +705,13 @@ int device_cus() {
 }
 
 // Host-side view of a launch's layout: strides in bytes, whether q, k, v and
-// out are all dense [B, heads, H, W, D], and the optional log-sum-exp output
-// (dense maps only).
+// out are all dense [B, heads, H, W, D], the optional log-sum-exp output
+// (dense maps only), and the score output of a scores-only launch.
 struct Layout {
   ByteStrides in, out;
   bool planar;
   float *lse;
+  float *scores;
 };
 
 template <typename T, int KS, int RY>
@@ -673,14 +727,21 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   // Non-temporal Q/out only when each line belongs to one block: dense maps
   // without dilation (channels-last maps interleave the heads' channels).
   auto kernel = s.dil == 1 && lay.planar
-                    ? (lay.lse ? fused_mfma_kernel<T, KS, RY, true, true>
-                               : fused_mfma_kernel<T, KS, RY, true, false>)
-                    : (lay.lse ? fused_mfma_kernel<T, KS, RY, false, true>
-                               : fused_mfma_kernel<T, KS, RY, false, false>);
+                    ? (lay.lse ? fused_mfma_kernel<T, KS, RY, true, kForwardLse>
+                               : fused_mfma_kernel<T, KS, RY, true, kForward>)
+                    : (lay.lse ? fused_mfma_kernel<T, KS, RY, false, kForwardLse>
+                               : fused_mfma_kernel<T, KS, RY, false, kForward>);
+  float *extra = lay.lse;
+  if constexpr (KS <= 9) {
+    if (lay.scores != nullptr) {
+      kernel = fused_mfma_kernel<T, KS, RY, false, kScores>;
+      extra = lay.scores;
+    }
+  }
   kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)q, (const T *)k, (const T *)v, (const T *)rpb, (T *)out, s, lay.in, lay.out,
       make_fastdiv((uint32_t)s.dil), make_fastdiv((uint32_t)nbx), make_fastdiv((uint32_t)nby),
-      make_fastdiv((uint32_t)s.heads), (int)nblocks, lay.lse);
+      make_fastdiv((uint32_t)s.heads), (int)nblocks, extra);
   return hipGetLastError();
 }
 
@@ -725,6 +786,7 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
   Layout lay;
   lay.planar = is_planar(in, s) && is_planar(out_st, s);
   lay.lse = lse;
+  lay.scores = nullptr;
   if (lse != nullptr && !is_planar(in, s)) {  // its index comes from q's dense offsets
     *supported = false;
     return hipSuccess;
@@ -746,6 +808,25 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
   if (dt == NA2D_DTYPE_BF16)
     return launch_dtype<__bf16>(q, k, v, rpb, out, s, lay, st, supported);
   return launch_dtype<_Float16>(q, k, v, rpb, out, s, lay, st, supported);
+}
+
+hipError_t launch_scores_mfma(const void *q, const void *k, const void *rpb, float *attn,
+                              const Shape &s, na2d_dtype_t dt, hipStream_t st, bool *supported) {
+  *supported = false;
+  if ((dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) || s.ks > 9 ||
+      (int64_t)s.H * s.W >= kMaxPlanePixels)
+    return hipSuccess;
+  Layout lay;
+  const Strides pl = planar_strides(s);
+  if (!mfma::byte_strides(pl, s, 2, &lay.in)) return hipSuccess;
+  lay.out = lay.in;
+  lay.planar = true;
+  lay.lse = nullptr;
+  lay.scores = attn;
+  *supported = true;
+  if (dt == NA2D_DTYPE_BF16)
+    return launch_dtype<__bf16>(q, k, nullptr, rpb, nullptr, s, lay, st, supported);
+  return launch_dtype<_Float16>(q, k, nullptr, rpb, nullptr, s, lay, st, supported);
 }
 
 }  // namespace na2d

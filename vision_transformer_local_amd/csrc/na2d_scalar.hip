@@ -503,6 +503,9 @@ hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const v
 
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,
                         const Shape &s, na2d_dtype_t dt, hipStream_t st) {
+  bool mfma = false;
+  const hipError_t e = launch_scores_mfma(q, k, rpb, attn, s, dt, st, &mfma);
+  if (mfma) return e;
   UnfusedGrid g;
   dim3 grid;
   if (!unfused_grid(s, 64, &g, &grid)) return hipErrorInvalidConfiguration;
