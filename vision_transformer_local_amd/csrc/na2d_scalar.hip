@@ -146,11 +146,14 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2v;
 
-// Workgroup numbering of an unfused launch: `per` queries per workgroup,
-// `chunks` workgroups per plane.
+// Workgroup numbering of an unfused launch (kUnfusedQueries queries per
+// workgroup, `chunks` workgroups per plane) and the divisors of the pixel
+// decoding.
+constexpr int kUnfusedQueries = 64;
+static_assert(4 * kUnfusedQueries == 256, "four lanes per query in a 256-lane workgroup");
+
 struct UnfusedGrid {
-  FastDiv chunks, W, dil, heads, ks;
-  int per;
+  FastDiv chunks, W, dil, heads;
 };
 
 // Sub-grid position and window of in-plane pixel pix (32-bit arithmetic).
@@ -304,17 +307,17 @@ __global__ __launch_bounds__(256) void qkrpb_kernel(const T *__restrict__ q,
                                                     const T *__restrict__ rpb,
                                                     float *__restrict__ attn, Shape s,
                                                     UnfusedGrid g) {
-  constexpr int KK = KS * KS;
-  __shared__ float rows[64 * KK];
+  constexpr int KK = KS * KS, NQ = kUnfusedQueries;
+  __shared__ float rows[NQ * KK];
   const int tid = threadIdx.x, j = tid & 3, lq = tid >> 2;
   const uint32_t plane = fast_div(blockIdx.x, g.chunks);
   const int chunk = (int)(blockIdx.x - plane * g.chunks.div);
   const int hw = s.H * s.W;
-  const int nq = min(64, hw - chunk * 64);  // queries of this workgroup
+  const int nq = min(NQ, hw - chunk * NQ);  // queries of this workgroup
   if (lq < nq)  // whole quads take the same branch
-    score_window<T, KS>(q, k, rpb, s, g, plane, hw, chunk * 64 + lq, j, rows + lq * KK);
+    score_window<T, KS>(q, k, rpb, s, g, plane, hw, chunk * NQ + lq, j, rows + lq * KK);
   __syncthreads();
-  float *dst = attn + ((int64_t)plane * hw + chunk * 64) * KK;
+  float *dst = attn + ((int64_t)plane * hw + chunk * NQ) * KK;
   for (int e = tid; e < nq * KK; e += 256) dst[e] = rows[e];
 }
 
@@ -370,16 +373,16 @@ template <typename T, int KS>
 __global__ __launch_bounds__(256) void av_kernel(const float *__restrict__ attn,
                                                  const T *__restrict__ v,
                                                  T *__restrict__ out, Shape s, UnfusedGrid g) {
-  constexpr int KK = KS * KS;
-  __shared__ float prob[64 * KK];
+  constexpr int KK = KS * KS, NQ = kUnfusedQueries;
+  __shared__ float prob[NQ * KK];
   const int tid = threadIdx.x;
   const uint32_t plane = fast_div(blockIdx.x, g.chunks);
   const int chunk = (int)(blockIdx.x - plane * g.chunks.div);
   const int hw = s.H * s.W;
-  const int nq = min(64, hw - chunk * 64);  // queries of this workgroup
+  const int nq = min(NQ, hw - chunk * NQ);  // queries of this workgroup
   {
     // lane l of a copy lands 4 l bytes past the wave's (uniform) LDS address
-    const float *src = attn + ((int64_t)plane * hw + chunk * 64) * KK;
+    const float *src = attn + ((int64_t)plane * hw + chunk * NQ) * KK;
     const int lane = tid & 63, wbase = __builtin_amdgcn_readfirstlane(tid >> 6) * 64;
     for (int e0 = wbase; e0 < nq * KK; e0 += 256)
       if (e0 + lane < nq * KK)
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(256) void av_kernel(const float *__restrict__ attn,
   __syncthreads();  // also completes the copies
   const int lq = tid >> 2;
   if (lq >= nq) return;
-  const int pix = chunk * 64 + lq;
+  const int pix = chunk * NQ + lq;
   const int part = tid & 3;  // channels 8 part .. 8 part + 7
   const PixPos p = decode_pixel(pix, s, g);
   const int64_t pq = (int64_t)plane * hw + pix;
@@ -448,9 +451,10 @@ hipError_t launch_ks(int ks, dim3 grid, hipStream_t st, A... args) {
   return hipGetLastError();
 }
 
-// Workgroups of an unfused launch with `per` queries each, or false when
+// Workgroups of an unfused launch, or false when
 // the plane or the grid is too large for 32-bit workgroup arithmetic.
-bool unfused_grid(const Shape &s, int per, UnfusedGrid *g, dim3 *grid) {
+bool unfused_grid(const Shape &s, UnfusedGrid *g, dim3 *grid) {
+  constexpr int per = kUnfusedQueries;
   const int64_t hw = (int64_t)s.H * s.W;
   if (hw >= ((int64_t)1 << 31)) return false;
   const int64_t chunks = (hw + per - 1) / per;
@@ -460,8 +464,6 @@ bool unfused_grid(const Shape &s, int per, UnfusedGrid *g, dim3 *grid) {
   g->W = make_fastdiv((uint32_t)s.W);
   g->dil = make_fastdiv((uint32_t)s.dil);
   g->heads = make_fastdiv((uint32_t)s.heads);
-  g->ks = make_fastdiv((uint32_t)s.ks);
-  g->per = per;
   *grid = dim3((unsigned)(planes * chunks));
   return true;
 }
@@ -508,7 +510,7 @@ hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *at
   if (mfma) return e;
   UnfusedGrid g;
   dim3 grid;
-  if (!unfused_grid(s, 64, &g, &grid)) return hipErrorInvalidConfiguration;
+  if (!unfused_grid(s, &g, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
     case NA2D_DTYPE_F32: return launch_ks<QkrpbLaunch<float>>(s.ks, grid, st, q, k, rpb, attn, s, g);
     case NA2D_DTYPE_BF16:
@@ -536,7 +538,7 @@ hipError_t launch_av(const float *attn, const void *v, void *out, const Shape &s
                      na2d_dtype_t dt, hipStream_t st) {
   UnfusedGrid g;
   dim3 grid;
-  if (!unfused_grid(s, 64, &g, &grid)) return hipErrorInvalidConfiguration;
+  if (!unfused_grid(s, &g, &grid)) return hipErrorInvalidConfiguration;
   switch (dt) {
     case NA2D_DTYPE_F32: return launch_ks<AvLaunch<float>>(s.ks, grid, st, attn, v, out, s, g);
     case NA2D_DTYPE_BF16: return launch_ks<AvLaunch<__bf16>>(s.ks, grid, st, attn, v, out, s, g);
