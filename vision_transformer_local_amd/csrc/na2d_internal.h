@@ -142,7 +142,8 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
                              na2d_dtype_t dt, hipStream_t st, bool *supported,
                              float *lse = nullptr);
 // Scores + bias of the unfused path on the matrix cores (bf16/fp16, k <= 9,
-// planes below kMaxPlanePixels); *supported = false otherwise.
+// planes within the general forward kernel's 32-bit offsets); *supported =
+// false otherwise.
 hipError_t launch_scores_mfma(const void *q, const void *k, const void *rpb, float *attn,
                               const Shape &s, na2d_dtype_t dt, hipStream_t st, bool *supported);
 hipError_t launch_qkrpb(const void *q, const void *k, const void *rpb, float *attn,

@@ -813,9 +813,7 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
 hipError_t launch_scores_mfma(const void *q, const void *k, const void *rpb, float *attn,
                               const Shape &s, na2d_dtype_t dt, hipStream_t st, bool *supported) {
   *supported = false;
-  if ((dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) || s.ks > 9 ||
-      (int64_t)s.H * s.W >= kMaxPlanePixels)
-    return hipSuccess;
+  if ((dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) || s.ks > 9) return hipSuccess;
   Layout lay;
   const Strides pl = planar_strides(s);
   if (!mfma::byte_strides(pl, s, 2, &lay.in)) return hipSuccess;
