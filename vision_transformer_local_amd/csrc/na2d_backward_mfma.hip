@@ -296,12 +296,18 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
   constexpr int NB = G::NB, SIDE = G::SIDE, NT = G::NT, HC = G::HC, TY = G::TY, TX = G::TX;
   constexpr int R = KS / 2;
   constexpr int HALO = G::HR * HC * 64;  // bytes per staged tensor
-  // K then V halo; afterwards the waves' parking space for dS (bias gradient)
+  // K then V halo
   __shared__ __attribute__((aligned(16))) char halo[2 * HALO];
   __shared__ float tabI[G::IH * G::IW], tabE[G::EH * G::EW];
   __shared__ float dtab[G::WAVES][NT];
+  // each wave's parking space for dS (bias gradient): apart from the halo
+  // for 16-row blocks, so that no wave waits for the others before parking;
+  // in the halo, once every wave is done with it, for 8-row blocks (measured
+  // faster there: DiNAT 56 d8 170 vs 184 us)
   constexpr int PARK = TX * KS * 16;  // floats per wave: [query column][window row][16]
-  static_assert(G::WAVES * PARK * 4 <= 2 * HALO, "dS parking exceeds the halo buffers");
+  constexpr bool OWN_PARKING = RY == 16;
+  static_assert(OWN_PARKING || G::WAVES * PARK * 4 <= 2 * HALO, "dS parking exceeds the halo");
+  __shared__ __attribute__((aligned(16))) float parking[OWN_PARKING ? G::WAVES * PARK : 1];
   char *const kbuf = halo, *const vbuf = halo + HALO;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -439,14 +445,14 @@ __global__ __launch_bounds__((BG<KS, RY>::THREADS)) void bwd_query_mfma(
     }
   }
   if (!bias) return;
-  // Bias gradient of the tile.  Once every wave is done with the K/V halo,
-  // each wave parks its dS rows in its own slice of that LDS, one query row
-  // of the tile at a time ([query column][window row][16 halo columns]), and
-  // lane l sums window slot l over that row's queries, in column order, into
-  // the wave's table (plain read-add-write: the lanes' entries are distinct).
-  __syncthreads();
+  // Bias gradient of the tile.  Each wave parks its dS rows in its own LDS
+  // slice, one query row of the tile at a time ([query column][window row]
+  // [16 halo columns]), and lane l sums window slot l over that row's
+  // queries, in column order, into the wave's table (plain read-add-write:
+  // the lanes' entries are distinct).
+  if constexpr (!OWN_PARKING) __syncthreads();  // every wave is done with the halo
   if (tile_ok) {
-    float *park = (float *)halo + wave * PARK;
+    float *park = (OWN_PARKING ? parking : (float *)halo) + wave * PARK;
     float *wt = dtab[wave];
     constexpr int NS = (KS * KS + 63) / 64;  // window slots per lane
     int pslot[NS], eslot[NS];                // slot's parking / table offsets
