@@ -732,10 +732,12 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
                     : (lay.lse ? fused_mfma_kernel<T, KS, RY, false, kForwardLse>
                                : fused_mfma_kernel<T, KS, RY, false, kForward>);
   float *extra = lay.lse;
-  if constexpr (KS <= 9) {
-    if (lay.scores != nullptr) {
+  if (lay.scores != nullptr) {
+    if constexpr (KS <= 9) {
       kernel = fused_mfma_kernel<T, KS, RY, false, kScores>;
       extra = lay.scores;
+    } else {
+      return hipErrorInvalidValue;  // no scores-only variant (its LDS rows do not fit)
     }
   }
   kernel<<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
