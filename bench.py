@@ -19,8 +19,17 @@ HIP events recorded on the same stream give the per-launch kernel time used
 for the roofline figure.  After the replay, 100 eager steps are timed one by
 one with their own HIP events (median, p10, p90 in per_launch_us).  The
 default fused forward also times the unfused three-kernel path the same way
-(the "unfused" object), and the float64 oracle runs on all host cores
-(cpu_baseline) and on one (cpu_baseline_1core).
+(the "unfused" object), and the float64 oracle runs on the host CPUs
+(cpu_baseline: every CPU of the process's affinity mask, at most 16, the CPU
+share of a one-GPU job on the GPU host; the count used and the host's are
+both recorded) and on one (cpu_baseline_1core).  The default run also times
+the DiNAT stage-1 (56x56, d=8) and stage-2 (28x28, d=4) layers the same way,
+each a sub-object of "workloads" with its own roofline and cpu_baseline
+(--also selects them).
+
+Every pass checks a sample of its outputs against the oracle; the run exits
+with status 3 (after printing its line) when an error exceeds the stated
+tolerance: 1e-5 for fp32, 2e-2 for bf16/fp16, 2e-5 for the log-sum-exp.
 
 Prints ONE JSON line (rank 0).  --gpus N > 1 is refused: this library's
 benchmark runs on a single GPU.
@@ -141,7 +150,9 @@ def cpu_baseline(p, cpu_inputs, budget_s=10.0, min_runs=3, max_runs=500, backwar
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": p.n_query_heads / t, "unit": "queries*heads/s", "cores": threads,
-            "kind": "oracle",
+            "host_cpus": oracle.host_cpus(), "kind": "oracle",
+            "threads_rule": "every CPU of the process's affinity mask, at most %d (a one-GPU "
+                            "job's CPU share on the GPU host)" % oracle.MAX_THREADS,
             "sample": "whole workload (%d query-heads) run %d times in %.1f s, median pass, "
                       "float64" % (p.n_query_heads, len(times), time.perf_counter() - start)}
 
@@ -196,6 +207,10 @@ def main(argv=None):
     ap.add_argument("--no-copy-reference", action="store_true",
                     help="skip the device-copy bandwidth measurement")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--also", default="dinat_s1_d8,dinat_s2_d4",
+                    help="further forward workloads timed in the same run (plain fused "
+                         "forward only), each a sub-object of the JSON line under "
+                         "'workloads'; empty: none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -232,6 +247,38 @@ def main(argv=None):
     if args.which == "backward":
         return bench_backward(args, p, dev, L)
 
+    rec, ok = bench_forward(args, args.workload, dev, L, main_line=True)
+    if rec is None:
+        return 2
+    plain = (args.path == "fused" and args.layout == "dense" and not args.padded
+             and not args.lse)
+    extras = [w for w in args.also.split(",") if w and w != args.workload] if plain else []
+    for w in extras:
+        if w not in WORKLOADS:
+            print("--also: unknown workload %s" % w, file=sys.stderr)
+            return 2
+        sub, sub_ok = bench_forward(args, w, dev, L, main_line=False)
+        rec.setdefault("workloads", {})[w] = sub
+        ok = ok and sub_ok
+    print(json.dumps(rec), flush=True)
+    if not ok:
+        print("sample error above the stated tolerance (%s)" % json.dumps(TOLERANCE),
+              file=sys.stderr)
+        return 3
+    return 0
+
+
+# Accuracy the library promises against the float64 oracle (absolute, on the
+# same rounded inputs): the bench's own sample check fails the run above it.
+TOLERANCE = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2, "lse": 2e-5}
+
+
+def bench_forward(args, workload, dev, L, main_line=True):
+    """One workload of the forward pass: the timed steps, the sample check
+    against the oracle, the roofline figures and (unless switched off) the
+    oracle's own rate.  Returns (record, sample within tolerance); the record
+    of an extra workload (main_line False) carries no run-wide fields."""
+    p = WORKLOADS[workload]
     cpu = I.make_inputs(p, seed=0)
     q0, k0, v0, rpb0 = cpu
     dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
@@ -241,18 +288,18 @@ def main(argv=None):
     cl = args.layout == "channels_last"
     if (cl or args.padded) and args.path != "fused":
         print("--layout channels_last and --padded take the fused path only", file=sys.stderr)
-        return 2
+        return None, False
     if cl and args.padded:
         print("--padded takes the dense layout", file=sys.stderr)
-        return 2
+        return None, False
     if args.lse and (cl or args.padded or args.path != "fused"):
         print("--lse takes the fused path on the dense layout", file=sys.stderr)
-        return 2
+        return None, False
     span = p.kernel_size * p.dilation
     if not args.padded and (p.H < span or p.W < span):
-        print("workload %s needs --padded (map below kernel*dilation)" % args.workload,
+        print("workload %s needs --padded (map below kernel*dilation)" % workload,
               file=sys.stderr)
-        return 2
+        return None, False
     tbytes = q0.numel() * q0.element_size()
     attn_bytes = p.n_query_heads * p.kernel_size ** 2 * 4 if args.path == "unfused" else 0
     per_replica = 4 * tbytes + attn_bytes
@@ -329,10 +376,14 @@ def main(argv=None):
     got = reps[0][3].contiguous().reshape(-1, D)[torch.from_numpy(idx).to(dev)]
     got = got.double().cpu().numpy()
     max_err = float(np.abs(got - ref).max())
+    ok = max_err <= TOLERANCE[p.dtype]
     lse_err = None
     if args.lse:
         gl = reps[0][4].reshape(-1)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
         lse_err = float(np.abs(gl - r["lse"]).max())
+        ok = ok and lse_err <= TOLERANCE["lse"]
+    del reps
+    torch.cuda.empty_cache()
 
     value = p.n_query_heads / (ms_per_step / 1e3)
     abytes = algorithmic_bytes(p)
@@ -341,51 +392,60 @@ def main(argv=None):
     if args.lse:
         abytes += 4 * p.n_query_heads  # the fp32 log-sum-exp written
     achieved = abytes / (kernel_ms / 1e3) / 1e9
-    traffic = measured_traffic(args.workload,
+    traffic = measured_traffic(workload,
                                "strided" if cl else ("padded" if args.padded else
                                                      ("lse" if args.lse else args.path)))
-
-    rec = {
-        "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
-        "value": value,
-        "unit": "queries*heads/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": p.dtype,
-        "data": "synthetic (seeded N(0,1) q/k/v, 0.02*N(0,1) bias)",
-        "config": {"workload": "%s: %s" % (args.workload, p.describe()),
-                   "B": B, "heads": heads, "H": H, "W": W, "D": D,
-                   "kernel_size": ks, "dilation": dil, "path": args.path,
-                   "layout": args.layout, "padded": args.padded, "lse": args.lse,
-                   "timing": args.mode, "replicas": R},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic},
+    config = {"workload": "%s: %s" % (workload, p.describe()),
+              "B": B, "heads": heads, "H": H, "W": W, "D": D,
+              "kernel_size": ks, "dilation": dil, "path": args.path,
+              "layout": args.layout, "padded": args.padded, "lse": args.lse,
+              "timing": args.mode, "replicas": R}
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    if main_line:
+        rec = {
+            "metric": "NA2D fwd queries*heads/s (+ achieved HBM GB/s as % of MI355X peak)",
+            "value": value,
+            "unit": "queries*heads/s",
+            "n_gpus": 1,
+            "steps": K,
+            "warmup": args.warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": p.dtype,
+            "data": "synthetic (seeded N(0,1) q/k/v, 0.02*N(0,1) bias)",
+            "config": config,
+        }
+    else:
+        rec = {"value": value, "unit": "queries*heads/s", "ms_per_step": ms_per_step,
+               "dtype": p.dtype, "config": config}
+    rec.update({
+        "roofline": roofline,
         "kernel_ms": kernel_ms,
         "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
+        "sample_within_tolerance": ok,
         "kernel_source_hash": kernel_source_hash(),
-    }
+    })
     if args.lse:
         rec["sample_max_abs_err_lse"] = lse_err
-    if args.path == "fused" and not (cl or args.padded or args.lse) and not args.no_unfused:
+    if (main_line and args.path == "fused" and not (cl or args.padded or args.lse)
+            and not args.no_unfused):
         rec["unfused"] = unfused_beside(args, p, dev, L, cpu)
-    if not args.no_copy_reference:
+    if main_line and not args.no_copy_reference:
         copy_gbs = copy_bandwidth(dev)
         rec["copy_reference"] = {"copy_gbs": copy_gbs, "achieved_over_copy": achieved / copy_gbs,
                                  "what": "torch device copy of 1 GiB, read+write bytes"}
     if not args.no_cpu_baseline:
         pads = (pad_k.cpu(), pad_v.cpu()) if args.padded else None
         rec["cpu_baseline"] = cpu_baseline(p, cpu, pads=pads)
-        rec["cpu_baseline_1core"] = cpu_baseline(p, cpu, pads=pads, threads=1, budget_s=8.0)
-    print(json.dumps(rec), flush=True)
-    return 0
+        if main_line:
+            rec["cpu_baseline_1core"] = cpu_baseline(p, cpu, pads=pads, threads=1,
+                                                     budget_s=8.0)
+    return rec, ok
 
 
 def unfused_beside(args, p, dev, L, cpu):
@@ -549,7 +609,11 @@ def bench_block(args, dev, L):
         x0, w_qkv, b_qkv, rpb, w_out, b_out, p.heads, ks, dil,
         stored=lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt).double().numpy())
     got = reps[0][1].reshape(-1, C)[torch.from_numpy(idx).to(dev)].double().cpu().numpy()
-    max_err = float(np.abs(got - ref.reshape(-1, C)[idx]).max())
+    refs = ref.reshape(-1, C)[idx]
+    max_err = float(np.abs(got - refs).max())
+    # the block's bound: the operator's tolerance plus one rounding of y
+    ulp = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -23}[p.dtype]
+    ok = float((np.abs(got - refs) - ulp * np.abs(refs)).max()) <= TOLERANCE[p.dtype]
 
     abytes = block_algorithmic_bytes(p)
     achieved = abytes / (kernel_ms / 1e3) / 1e9
@@ -579,9 +643,13 @@ def bench_block(args, dev, L):
         "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
+        "sample_within_tolerance": ok,
         "kernel_source_hash": kernel_source_hash("block"),
     }
     print(json.dumps(rec), flush=True)
+    if not ok:
+        print("sample error above the stated tolerance", file=sys.stderr)
+        return 3
     return 0
 
 
@@ -619,13 +687,21 @@ def bench_backward(args, p, dev, L):
 
     # sanity: the first replica's gradients against the oracle (skipped on the
     # largest maps, where the parity tests cover them)
-    max_err = None
+    max_err, ok = None, True
     if p.n_query_heads * ks * ks <= 64 * 2 * 56 * 56 * 49:
         import oracle
         ref = oracle.backward(q0, k0, v0, rpb0, d0, ks, dil)
         got = [t.double().cpu().numpy() for t in reps[0][1]]
-        max_err = max(float(np.abs(g - ref[n]).max()) for g, n in zip(got, ("dq", "dk", "dv")))
-        max_err = max(max_err, float(np.abs(drpb.double().cpu().numpy() - ref["drpb"]).max()))
+        got.append(drpb.double().cpu().numpy())
+        names = ("dq", "dk", "dv", "drpb")
+        max_err = max(float(np.abs(g - ref[n]).max()) for g, n in zip(got, names))
+        # per element |gpu - oracle| <= r |oracle| + a rms(oracle): one
+        # rounding of each gradient to its type plus fp32 accumulation (the
+        # bias gradient is fp32 whatever the data type)
+        for g, n in zip(got, names):
+            r_, a_ = BACKWARD_TOLERANCE["f32" if n == "drpb" else p.dtype]
+            rms = float(np.sqrt(np.mean(ref[n] ** 2))) or 1.0
+            ok = ok and float((np.abs(g - ref[n]) - r_ * np.abs(ref[n])).max()) <= a_ * rms
 
     abytes = backward_algorithmic_bytes(p)
     achieved = abytes / (kernel_ms / 1e3) / 1e9
@@ -653,12 +729,20 @@ def bench_backward(args, p, dev, L):
         "per_launch_us": per_launch,
         "algorithmic_bytes_per_step": abytes,
         "sample_max_abs_err": max_err,
+        "sample_within_tolerance": ok,
         "kernel_source_hash": kernel_source_hash("backward"),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(p, (q0, k0, v0, rpb0, d0), backward=True)
     print(json.dumps(rec), flush=True)
+    if not ok:
+        print("gradient error above the stated tolerance", file=sys.stderr)
+        return 3
     return 0
+
+
+# (relative, absolute-over-rms) bounds of the backward pass per data type
+BACKWARD_TOLERANCE = {"bf16": (2.0 ** -8, 1e-3), "f16": (2.0 ** -10, 3e-4), "f32": (1e-5, 1e-5)}
 
 
 if __name__ == "__main__":

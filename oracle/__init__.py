@@ -70,12 +70,23 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def default_threads() -> int:
+def host_cpus() -> int:
+    """CPUs this process may run on (its affinity mask)."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+# A one-GPU job on the GPU host is granted a share of 16 CPUs, whatever the
+# machine's own count (nproc there reports every core of the host).
+MAX_THREADS = 16
+
+
+def default_threads() -> int:
+    """Oracle threads: every CPU available to the process, at most
+    MAX_THREADS."""
+    return max(1, min(MAX_THREADS, host_cpus()))
 
 
 def _f64(x):

@@ -116,21 +116,6 @@ __device__ __forceinline__ WeightLane weight_lane(int ql, int g) {
   return WeightLane{wl0, wl0 ^ 64};
 }
 
-// Compute units of the current device (queried once per device).
-int block_device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // Where a block sits: image, first query row / column, their ends, and the
 // first row / column of the key halo (the window start of the first query).
 struct BlockPos {
@@ -544,7 +529,7 @@ hipError_t launch_rt(const void *x, const void *w_qkv, const void *b_qkv, const 
   const int nby = (H + RY - 1) / RY, nbx = (W + G::RX - 1) / G::RX;
   const int64_t nblocks = (int64_t)B * nby * nbx;
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
-  const int64_t slots = 2 * (int64_t)block_device_cus();  // two workgroups per CU
+  const int64_t slots = 2 * (int64_t)device_compute_units();  // two workgroups per CU
   const int64_t grid = nblocks < slots ? nblocks : slots;
   block_fused_kernel<T, KS, RY><<<dim3((unsigned)grid), G::THREADS, 0, st>>>(
       (const T *)x, (const T *)w_qkv, (const T *)b_qkv, (const T *)rpb, (const T *)w_out,

@@ -390,19 +390,6 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u], rlse[u]);  // the last block
 }
 
-int dense_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <typename T, int KS>
 hipError_t launch_dense(const void *q, const void *k, const void *v, const void *rpb, void *out,
                         const Shape &s, const ByteStrides &si, const ByteStrides &so,
@@ -414,7 +401,7 @@ hipError_t launch_dense(const void *q, const void *k, const void *v, const void 
   if (nblocks > INT_MAX || per_head > INT_MAX) return hipErrorInvalidConfiguration;
   int log2d = 0;
   while ((1 << log2d) < s.dil) ++log2d;
-  const int64_t grid = nblocks < dense_cus() ? nblocks : dense_cus();
+  const int64_t grid = nblocks < device_compute_units() ? nblocks : device_compute_units();
   // heads interleaved within pixels: alternate heads between blocks
   const bool hfast = s.heads > 1 && (uint64_t)si.h < si.x;
   const bool padded = pad.Hp > s.H || pad.Wp > s.W;

@@ -63,6 +63,19 @@ __device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Compute units of the current device, queried at every launch: the runtime
+// answers from its cached device properties, and keeping no copy here leaves
+// the library without mutable global state (concurrent first launches from
+// several host threads need no synchronisation).
+inline int device_compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
 // Division by a divisor fixed at launch: n / d == (umulhi(n, mul) + n) >> shr
 // for 0 <= n < 2^31 (round-up multiplier method of Granlund and Montgomery,
 // "Division by invariant integers using multiplication", 1994).  Replaces

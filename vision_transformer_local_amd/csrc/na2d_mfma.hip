@@ -690,20 +690,6 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   if constexpr (LSE) store_lse<T>(lse, rcur.pofs, pcur.q, g, res);
 }
 
-// Compute units of the current device (queried once per device).
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // Host-side view of a launch's layout: strides in bytes, whether q, k, v and
 // out are all dense [B, heads, H, W, D], the optional log-sum-exp output
 // (dense maps only), and the score output of a scores-only launch.
@@ -723,7 +709,7 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   const int64_t nblocks = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
   // one persistent workgroup per compute unit (its LDS holds two blocks)
-  const int64_t grid = nblocks < device_cus() ? nblocks : device_cus();
+  const int64_t grid = nblocks < device_compute_units() ? nblocks : device_compute_units();
   // Non-temporal Q/out only when each line belongs to one block: dense maps
   // without dilation (channels-last maps interleave the heads' channels).
   auto kernel = s.dil == 1 && lay.planar
