@@ -77,7 +77,8 @@ BLOCK_WORKLOADS = {
 # only while the sources of its family are unchanged.
 _CSRC = "vision_transformer_local_amd/csrc/"
 _SHARED = [_CSRC + "na2d_mfma_common.h", _CSRC + "na2d_internal.h"]
-_FORWARD = [_CSRC + f for f in ("na2d_mfma.hip", "na2d_dense.hip", "na2d_scalar.hip")] + _SHARED
+_FORWARD = [_CSRC + f for f in (
+    "na2d_mfma.hip", "na2d_stream.hip", "na2d_dense.hip", "na2d_scalar.hip")] + _SHARED
 SOURCE_FAMILIES = {
     "forward": _FORWARD,
     "block": [_CSRC + "na2d_linear.hip", _CSRC + "na2d_block.hip"] + _FORWARD,
@@ -183,7 +184,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="nat_tiny_s1",
                     choices=sorted(WORKLOADS) + sorted(BLOCK_WORKLOADS))
-    ap.add_argument("--path", default="fused", choices=["fused", "fma", "unfused"])
+    ap.add_argument("--path", default="fused", choices=["fused", "tiled", "fma", "unfused"],
+                    help="fused: the library's choice; tiled: the block-tiled matrix-core "
+                         "kernel only; fma: the per-lane fp32 kernel; unfused: the three "
+                         "kernels of the decomposition the pages show")
     ap.add_argument("--pass", dest="which", default="forward",
                     choices=["forward", "backward", "block"],
                     help="forward: the operator; backward: its gradients; block: the "
@@ -282,7 +286,7 @@ def bench_forward(args, workload, dev, L, main_line=True):
     cpu = I.make_inputs(p, seed=0)
     q0, k0, v0, rpb0 = cpu
     dt_code = {"f32": 0, "bf16": 1, "f16": 2}[p.dtype]
-    algo = {"fused": 0, "fma": 1}.get(args.path, 0)
+    algo = {"fused": 0, "fma": 1, "tiled": 3}.get(args.path, 0)
     B, heads, H, W, D = p.shape
     ks, dil = p.kernel_size, p.dilation
     cl = args.layout == "channels_last"

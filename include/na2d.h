@@ -71,7 +71,9 @@ typedef enum {
 typedef enum {
     NA2D_ALGO_AUTO = 0, /* MFMA for bf16/fp16, FMA for fp32 */
     NA2D_ALGO_FMA = 1,  /* one lane per query, scalar fp32 FMA, any dtype */
-    NA2D_ALGO_MFMA = 2  /* matrix-core kernel, bf16/fp16 only */
+    NA2D_ALGO_MFMA = 2, /* matrix-core kernels (the library's choice), bf16/fp16 only */
+    NA2D_ALGO_MFMA_TILED = 3 /* the block-tiled matrix-core kernel only (never the
+                                row-streaming one): for comparisons and tests */
 } na2d_algo_t;
 
 /*

@@ -82,7 +82,7 @@ def test_forward_validation(args, expect):
     L = na2d.lib()
     B, h, H, W, D, ks, d, dt = args
     assert L.na2d_forward(P[0], P[1], P[2], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == expect
-    for algo in (0, 1, 2):
+    for algo in (0, 1, 2, 3):
         assert L.na2d_forward_algo(P[0], P[1], P[2], P[3], P[4], B, h, H, W, D, ks, d, dt,
                                    algo, S) == expect
     assert L.na2d_qkrpb(P[0], P[1], P[3], P[4], B, h, H, W, D, ks, d, dt, S) == expect
@@ -144,9 +144,10 @@ def test_forward_lse_rejects_overlaps():
 def test_forward_rejects_bad_algo_and_mfma_fp32():
     L = na2d.lib()
     B, h, H, W, D, ks, d, _ = VALID
-    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, BF16, 3, S) == INVALID
+    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, BF16, 4, S) == INVALID
     assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, BF16, -1, S) == INVALID
     assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, F32, 2, S) == UNSUPPORTED
+    assert L.na2d_forward_algo(*P[:5], B, h, H, W, D, ks, d, F32, 3, S) == UNSUPPORTED
 
 
 def test_qkrpb_and_av_pointer_rules():

@@ -24,9 +24,9 @@ import pytest
 
 from vision_transformer_local_amd import build as B
 
-SOURCES = ["na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip", "na2d_block.hip",
-           "na2d_backward_mfma.hip"]
-PIPELINED = {"na2d_mfma.hip", "na2d_dense.hip", "na2d_linear.hip"}
+SOURCES = ["na2d_mfma.hip", "na2d_dense.hip", "na2d_stream.hip", "na2d_linear.hip",
+           "na2d_block.hip", "na2d_backward_mfma.hip"]
+PIPELINED = {"na2d_mfma.hip", "na2d_dense.hip", "na2d_stream.hip", "na2d_linear.hip"}
 KERNEL = re.compile(r"^(_ZN4na2d12_GLOBAL__N_1\d+\w*(?:mfma_kernel|block_fused_kernel|"
                     r"bwd_query_mfma|bwd_key_mfma)\S*):", re.M)
 

@@ -2,8 +2,9 @@
 against the float64 oracle on the same seeded inputs, through the C ABI.
 
 Every forward kernel family writes it: the general matrix-core kernel, the
-whole-sub-grid kernel (maps of exactly k*d, k = 3, 5, 7, power-of-two d) and
-the per-lane kernel (fp32).  out must stay bit-identical to na2d_forward's.
+row-streaming kernel (no dilation, k = 3, 5, 7, maps 33 to 56 columns wide),
+the whole-sub-grid kernel (maps of exactly k*d, k = 3, 5, 7, power-of-two d)
+and the per-lane kernel (fp32).  out must stay bit-identical to na2d_forward's.
 
 Tolerance: the fp32 scores carry at most 1e-5 absolute error on these inputs
 (the bound the score test of the unfused path holds); lse is 1-Lipschitz in

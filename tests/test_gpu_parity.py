@@ -21,9 +21,11 @@ from parity_util import TOL, compare, gpu_inputs, note, run_path, sample_indices
 
 pytestmark = pytest.mark.gpu
 
+# "mfma" is the library's matrix-core choice (the row-streaming kernel for
+# maps without dilation at k <= 7), "mfma_tiled" the block-tiled kernel only
 PATHS = {"f32": ["auto", "fma", "unfused"],
-         "bf16": ["auto", "mfma", "fma", "unfused"],
-         "f16": ["auto", "mfma", "fma", "unfused"]}
+         "bf16": ["auto", "mfma", "mfma_tiled", "fma", "unfused"],
+         "f16": ["auto", "mfma", "mfma_tiled", "fma", "unfused"]}
 
 KD = [(1, 1), (1, 3), (3, 1), (3, 2), (3, 3), (5, 1), (5, 2), (7, 1), (7, 2), (7, 3),
       (7, 4), (7, 8), (9, 1), (9, 2), (11, 1), (13, 1), (13, 2)]

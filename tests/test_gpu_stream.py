@@ -1,0 +1,115 @@
+"""GPU parity of the row-streaming forward kernel (maps without dilation,
+k in {3, 5, 7}, bf16 / fp16, 33 to 56 columns, at least 16 rows) against the
+float64 oracle.
+
+The shapes are chosen for the kernel's own structure: every workgroup width
+(5, 6 and 7 tile columns of 8, ragged last tiles), query-row runs split into
+several units (small batches; odd units walk the map upward) whose last step
+holds 1, 2, 3 or 4 rows, maps whose first or last step has clamped windows on
+both tile rows, and the channels-last layout.  Each case also runs the
+block-tiled kernel on the same inputs, which must meet the same bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from vision_transformer_local_amd import inputs as I
+from vision_transformer_local_amd import na2d
+from vision_transformer_local_amd.inputs import Problem
+
+from parity_util import compare, gpu_inputs, note
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(16, 40), (21, 47), (29, 55), (56, 56), (61, 41), (30, 50), (64, 56), (17, 45),
+          (19, 33), (23, 38)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ks", [3, 5, 7])
+@pytest.mark.parametrize("H,W", SHAPES, ids=str)
+def test_stream_kernel_matches_oracle(H, W, ks, dtype):
+    if H < ks or W < ks:
+        pytest.skip("map smaller than the window")
+    p = Problem(2, 3, H, W, 32, ks, 1, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=H * 100 + W + ks)
+    for algo in ("mfma", "mfma_tiled"):
+        note("stream %s algo=%s" % (p.describe(), algo))
+        out = na2d.forward(q, k, v, rpb, ks, 1, algo=algo)
+        torch.cuda.synchronize()
+        compare(p, out, cpu)
+
+
+@pytest.mark.parametrize("B", [1, 3, 7, 16])
+def test_stream_kernel_unit_splits(B):
+    """The number of query-row units per plane depends on the batch (units
+    are split until they about match the compute units): B = 1 gives 4
+    units of 16 rows on a 56-row map, B = 16 two of 28."""
+    p = Problem(B, 2, 56, 56, 32, 7, 1, "bf16")
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=B)
+    note("stream units %s" % p.describe())
+    out = na2d.forward(q, k, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    compare(p, out, cpu)
+
+
+@pytest.mark.parametrize("p", [Problem(1, 2, 56, 56, 32, 7, 1, "bf16"),
+                               Problem(2, 2, 21, 47, 32, 5, 1, "f16"),
+                               Problem(3, 1, 30, 35, 32, 3, 1, "bf16")],
+                         ids=lambda p: p.describe().replace(" ", "_"))
+def test_stream_kernel_lse(p):
+    """The log-sum-exp variant: the same output bits as the plain forward,
+    and each query's lse within 2e-5 of the oracle's (the bound the lse tests
+    derive).  B = 1 splits each plane into units, half of them walking the
+    map upward."""
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=31)
+    note("stream lse %s" % p.describe())
+    out, lse = na2d.forward_lse(q, k, v, rpb, p.kernel_size, 1)
+    ref_out = na2d.forward(q, k, v, rpb, p.kernel_size, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    compare(p, out, cpu)
+    ref = oracle.forward(*cpu, p.kernel_size, 1, lse=True)["lse"]
+    err = float(np.abs(lse.cpu().double().numpy() - ref).max())
+    assert err <= 2e-5, err
+
+
+def test_stream_kernel_no_bias_and_zero_bias():
+    p = Problem(2, 2, 33, 41, 32, 7, 1, "bf16")  # (the stream kernel's shape)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=9)
+    note("stream no bias %s" % p.describe())
+    a = na2d.forward(q, k, v, None, 7, 1)
+    b = na2d.forward(q, k, v, torch.zeros_like(rpb), 7, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    compare(p, a, (cpu[0], cpu[1], cpu[2], torch.zeros_like(cpu[3])))
+
+
+def test_stream_kernel_channels_last():
+    """q, k, v and out as channels-last hidden states [B, H, W, heads*D]."""
+    p = Problem(2, 4, 28, 44, 32, 7, 1, "bf16")
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=12)
+
+    def cl(t):
+        return t.permute(0, 2, 3, 1, 4).reshape(p.B, p.H, p.W, -1).contiguous()
+    note("stream channels-last %s" % p.describe())
+    out = na2d.forward_channels_last(cl(q), cl(k), cl(v), rpb, p.heads, 7, 1)
+    torch.cuda.synchronize()
+    out = na2d.heads_view(out, p.heads).contiguous()
+    compare(p, out, cpu)
+    dense = na2d.forward(q, k, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dense)
+
+
+def test_stream_kernel_full_size_bit_stable():
+    """NAT-Tiny stage 1 at full size: two launches give identical bits (its
+    values against the oracle are test_gpu_parity's full-size case)."""
+    p = I.NAT_TINY_S1
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=0)
+    note("stream full size %s" % p.describe())
+    a = na2d.forward(q, k, v, rpb, 7, 1)
+    b = na2d.forward(q, k, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

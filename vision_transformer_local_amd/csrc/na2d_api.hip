@@ -89,11 +89,11 @@ na2d_status_t forward_checked(const void *q, const void *k, const void *v, const
                               float *lse = nullptr) {
   const bool automatic = algo == NA2D_ALGO_AUTO;
   if (automatic) algo = dtype == NA2D_DTYPE_F32 ? NA2D_ALGO_FMA : NA2D_ALGO_MFMA;
-  if (algo == NA2D_ALGO_MFMA) {
+  if (algo == NA2D_ALGO_MFMA || algo == NA2D_ALGO_MFMA_TILED) {
     if (dtype == NA2D_DTYPE_F32) return NA2D_ERROR_NOT_SUPPORTED;
     bool supported = true;
-    hipError_t e =
-        na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, &supported, lse);
+    hipError_t e = na2d::launch_fused_mfma(q, k, v, rpb, out, s, in, os, pad, dtype, stream,
+                                           &supported, lse, algo == NA2D_ALGO_MFMA);
     if (supported) return from_hip(e);
     if (!automatic) return NA2D_ERROR_NOT_SUPPORTED;
     // planes too large for 32-bit in-plane offsets, and padded maps that are
@@ -112,7 +112,8 @@ na2d_status_t na2d_forward_algo(const void *q, const void *k, const void *v, con
                                 na2d_algo_t algo, hipStream_t stream) {
   na2d::Shape s;
   if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
-  if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_FMA && algo != NA2D_ALGO_MFMA)
+  if (algo != NA2D_ALGO_AUTO && algo != NA2D_ALGO_FMA && algo != NA2D_ALGO_MFMA &&
+      algo != NA2D_ALGO_MFMA_TILED)
     return NA2D_ERROR_INVALID_VALUE;
   na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
   if (st != NA2D_SUCCESS) return st;

@@ -140,10 +140,13 @@ hipError_t launch_fused_fma(const void *q, const void *k, const void *v, const v
                             void *out, const Shape &s, const Strides &in, const Strides &out_st,
                             const Pad &pad, na2d_dtype_t dt, hipStream_t st,
                             float *lse = nullptr);
+// stream: the row-streaming kernel may run (maps without dilation, k <= 7,
+// no log-sum-exp output); false keeps to the block-tiled kernels.
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
                              const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
-                             hipStream_t st, bool *supported, float *lse = nullptr);
+                             hipStream_t st, bool *supported, float *lse = nullptr,
+                             bool stream = true);
 // Whole-sub-grid kernel (H == W == k*d); sets *supported = false when the
 // problem is not of that kind.  Strides in bytes (mfma::ByteStrides).
 namespace mfma {
@@ -154,6 +157,14 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
                              const mfma::ByteStrides &out_st, const Pad &pad,
                              na2d_dtype_t dt, hipStream_t st, bool *supported,
                              float *lse = nullptr);
+// Row-streaming kernel (no dilation, k in {3, 5, 7}, 16-bit data, maps 33
+// to 56 columns wide and at least 16 rows high); byte strides as the general
+// kernel's; lse (optional) as the general kernel's, dense q only.
+bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt);
+hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
+                              void *out, float *lse, const Shape &s,
+                              const mfma::ByteStrides &si, const mfma::ByteStrides &so,
+                              na2d_dtype_t dt, hipStream_t st);
 // Scores + bias of the unfused path on the matrix cores (bf16/fp16, k <= 9,
 // planes within the general forward kernel's 32-bit offsets); *supported =
 // false otherwise.

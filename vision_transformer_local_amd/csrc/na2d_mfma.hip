@@ -765,7 +765,7 @@ hipError_t launch_dtype(const void *q, const void *k, const void *v, const void 
 hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const void *rpb,
                              void *out, const Shape &s, const Strides &in,
                              const Strides &out_st, const Pad &pad, na2d_dtype_t dt,
-                             hipStream_t st, bool *supported, float *lse) {
+                             hipStream_t st, bool *supported, float *lse, bool stream) {
   *supported = true;
   if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) {
     *supported = false;
@@ -787,12 +787,14 @@ hipError_t launch_fused_mfma(const void *q, const void *k, const void *v, const 
   hipError_t e =
       launch_dense_mfma(q, k, v, rpb, out, s, lay.in, lay.out, pad, dt, st, supported, lse);
   if (*supported) return e;
-  // the general kernel runs unpadded maps only
+  // the general kernels run unpadded maps only
   if (pad.Hp > s.H || pad.Wp > s.W) {
     *supported = false;
     return hipSuccess;
   }
   *supported = true;
+  if (stream && stream_mfma_supported(s, dt))
+    return launch_stream_mfma(q, k, v, rpb, out, lse, s, lay.in, lay.out, dt, st);
   if (dt == NA2D_DTYPE_BF16)
     return launch_dtype<__bf16>(q, k, v, rpb, out, s, lay, st, supported);
   return launch_dtype<_Float16>(q, k, v, rpb, out, s, lay, st, supported);

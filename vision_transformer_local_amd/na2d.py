@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libna2d.so")
 
 SUCCESS, INVALID_VALUE, NOT_SUPPORTED, LAUNCH_FAILURE = 0, 1, 2, 3
-ALGOS = {"auto": 0, "fma": 1, "mfma": 2}
+ALGOS = {"auto": 0, "fma": 1, "mfma": 2, "mfma_tiled": 3}
 _DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 _lib = None
