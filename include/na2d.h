@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates no memory and keeps no mutable global state.
+ *    allocates no memory and keeps no mutable global state (the one
+ *    exception: na2d_backward_noalloc's fixed device array and the
+ *    once-per-device record of its address, described there).
  *  - q, k, v and out are dense [B, heads, H, W, D] (D fastest) in `dtype`.
  *  - rpb is dense [heads, 2k-1, 2k-1] in `dtype`; entry [h][dy+k-1][dx+k-1]
  *    is the bias of a key dy window-steps below and dx steps right of the
@@ -64,7 +66,9 @@ typedef enum {
     NA2D_SUCCESS = 0,
     NA2D_ERROR_INVALID_VALUE = 1,
     NA2D_ERROR_NOT_SUPPORTED = 2,
-    NA2D_ERROR_LAUNCH_FAILURE = 3
+    NA2D_ERROR_LAUNCH_FAILURE = 3,
+    NA2D_ERROR_WORKSPACE_LIMIT = 4  /* na2d_backward_noalloc: problem needs more
+                                       workspace than its fixed array holds */
 } na2d_status_t;
 
 /* Kernel family used by na2d_forward_algo. */
@@ -292,6 +296,37 @@ na2d_status_t na2d_backward(const void *q, const void *k, const void *v, const v
  * an invalid or unsupported problem. */
 size_t na2d_backward_workspace_size(int B, int heads, int H, int W, int D, int kernel_size,
                                     int dilation, int with_bias_grad);
+
+/*
+ * na2d_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and status codes are
+ * na2d_backward's; the gradients are bit-identical to its.
+ *
+ * The workspace is a fixed device array of na2d_backward_noalloc_limit()
+ * bytes (64 MiB) inside the library, one copy per GPU, present from the
+ * library's first use on that GPU until the process ends.  Its device address
+ * is looked up on the first call on each device (the device of `stream`, or
+ * the current one for the null stream) and kept for later calls.  The call
+ * allocates nothing and calls no allocating routine.
+ *
+ *  - A problem whose workspace (na2d_backward_workspace_size) exceeds the
+ *    limit returns NA2D_ERROR_WORKSPACE_LIMIT before any HIP call; every
+ *    configuration of the NAT/DiNAT layers up to 200x336 maps at k = 13 fits.
+ *  - Every call on one GPU uses the same array.  Calls whose work overlaps in
+ *    time on one GPU (different streams, or several host threads without
+ *    ordering) race on it and give undefined results; calls ordered on one
+ *    stream are safe.  The kernels write every workspace entry they read
+ *    first, so nothing needs clearing between calls.
+ */
+na2d_status_t na2d_backward_noalloc(const void *q, const void *k, const void *v,
+                                    const void *rpb, const void *dout, void *dq, void *dk,
+                                    void *dv, float *drpb, int B, int heads, int H, int W, int D,
+                                    int kernel_size, int dilation, na2d_dtype_t dtype,
+                                    hipStream_t stream);
+
+/* Bytes of na2d_backward_noalloc's device array. */
+size_t na2d_backward_noalloc_limit(void);
 
 /* Static, NUL-terminated description of a status code. */
 const char *na2d_status_string(na2d_status_t status);

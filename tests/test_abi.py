@@ -248,6 +248,50 @@ def test_backward_rejects_overlaps(a, b):
     assert _backward(L, ptrs, VALID) == INVALID
 
 
+# -- allocation-free backward: na2d_backward's rules, plus the array limit ---
+WORKSPACE_LIMIT = 4
+
+
+def _backward_noalloc(L, ptrs, args):
+    B, h, H, W, D, ks, d, dt = args
+    return L.na2d_backward_noalloc(*ptrs[:9], B, h, H, W, D, ks, d, dt, S)
+
+
+@pytest.mark.parametrize("args,expect", FORWARD_CASES)
+def test_backward_noalloc_validation(args, expect):
+    assert _backward_noalloc(na2d.lib(), BP, args) == expect
+
+
+@pytest.mark.parametrize("slot", [0, 1, 2, 4, 5, 6, 7])
+def test_backward_noalloc_null_pointers(slot):
+    ptrs = list(BP)
+    ptrs[slot] = NULL
+    assert _backward_noalloc(na2d.lib(), ptrs, VALID) == INVALID
+
+
+@pytest.mark.parametrize("a,b", [(5, 0), (5, 6), (6, 7), (7, 4), (8, 3), (5, 3)])
+def test_backward_noalloc_rejects_overlaps(a, b):
+    ptrs = list(BP)
+    ptrs[a] = ctypes.c_void_p(ptrs[b].value + 16)
+    assert _backward_noalloc(na2d.lib(), ptrs, VALID) == INVALID
+
+
+def test_backward_noalloc_limit():
+    """A problem whose workspace exceeds the fixed array is refused with its
+    own status before any HIP call (this host has no GPU); the limit is the
+    documented 64 MiB and covers the largest detection layer."""
+    L = na2d.lib()
+    limit = L.na2d_backward_noalloc_limit()
+    assert limit == 64 << 20
+    big = (16, 8, 256, 256, 32, 7, 1, BF16)   # 2^23 queries: 64 MiB of lse/Dq alone
+    assert L.na2d_backward_workspace_size(*big[:7], 1) > limit
+    assert _backward_noalloc(L, BP, big) == WORKSPACE_LIMIT
+    assert na2d.na2d_status_string(WORKSPACE_LIMIT).startswith("NA2D_ERROR_WORKSPACE_LIMIT")
+    for det in ((2, 6, 200, 336, 32, 13, 1), (2, 6, 200, 336, 32, 13, 8),
+                (64, 2, 56, 56, 32, 7, 1), (64, 2, 56, 56, 32, 7, 8)):
+        assert 0 < L.na2d_backward_workspace_size(*det, 1) <= limit
+
+
 # ---------------------------------------------------------------------------
 # na2d_forward_strided: same shape rules, plus the stride rules.
 def _strides(*vals):

@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <atomic>
+
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 60;   // keeps byte counts (x4) in int64
@@ -100,6 +102,86 @@ na2d_status_t forward_checked(const void *q, const void *k, const void *v, const
     // not k*d square: the FMA kernel handles them
   }
   return from_hip(na2d::launch_fused_fma(q, k, v, rpb, out, s, in, os, pad, dtype, stream, lse));
+}
+
+// Checks of the backward entry points, workspace aside; *need receives the
+// workspace bytes the problem takes.
+na2d_status_t check_backward(const void *q, const void *k, const void *v, const void *rpb,
+                             const void *dout, void *dq, void *dk, void *dv, float *drpb, int B,
+                             int heads, int H, int W, int D, int kernel_size, int dilation,
+                             na2d_dtype_t dtype, na2d::Shape *s, size_t *need) {
+  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
+  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, s);
+  if (st != NA2D_SUCCESS) return st;
+  const void *ins[] = {q, k, v, dout};
+  void *outs[] = {dq, dk, dv};
+  for (const void *p : ins)
+    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
+  for (void *p : outs)
+    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
+  if ((rpb && !aligned16(rpb)) || (drpb && !aligned16(drpb))) return NA2D_ERROR_INVALID_VALUE;
+  *need = na2d::backward_workspace_bytes(*s, drpb != nullptr);
+  return NA2D_SUCCESS;
+}
+
+// True when an output (or the workspace) overlaps another output or an input.
+bool overlaps_backward(const void *workspace, size_t need, const void *q, const void *k,
+                       const void *v, const void *rpb, const void *dout, void *dq, void *dk,
+                       void *dv, float *drpb, const na2d::Shape &s, na2d_dtype_t dtype) {
+  const int64_t tbytes = s.n_query * na2d::kHeadDim * elem_bytes(dtype);
+  const int64_t side = 2 * s.ks - 1;
+  const int64_t bbytes = s.heads * side * side * 4;
+  const int64_t rbytes = s.heads * side * side * elem_bytes(dtype);
+  struct Span { const void *p; int64_t n; };
+  const Span written[] = {{dq, tbytes}, {dk, tbytes}, {dv, tbytes}, {drpb, bbytes},
+                          {workspace, (int64_t)need}};
+  const Span read[] = {{q, tbytes}, {k, tbytes}, {v, tbytes}, {dout, tbytes}, {rpb, rbytes}};
+  for (int a = 0; a < 5; ++a) {
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(written[a].p, written[a].n, written[b].p, written[b].n)) return true;
+    for (const Span &r : read)
+      if (overlaps(written[a].p, written[a].n, r.p, r.n)) return true;
+  }
+  return false;
+}
+
+// Workspace of na2d_backward_noalloc: a fixed device array, one copy per GPU
+// (loaded with the library's code object, held until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device and kept in scratch_addr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> scratch_addr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// The device address of the scratch array on the device `stream` runs on
+// (the current device for the null stream).  The first call on a device
+// looks it up with that device current; a concurrent first call stores the
+// same value.
+na2d_status_t scratch_address(hipStream_t stream, void **addr) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return NA2D_ERROR_LAUNCH_FAILURE;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess)
+    return NA2D_ERROR_INVALID_VALUE;
+  if (dev < 0 || dev >= kMaxDevices) return NA2D_ERROR_NOT_SUPPORTED;
+  uintptr_t a = scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return NA2D_ERROR_LAUNCH_FAILURE;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return NA2D_ERROR_LAUNCH_FAILURE;
+    if (e != hipSuccess || p == nullptr) return NA2D_ERROR_LAUNCH_FAILURE;
+    a = reinterpret_cast<uintptr_t>(p);
+    scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *addr = reinterpret_cast<void *>(a);
+  return NA2D_SUCCESS;
 }
 
 }  // namespace
@@ -427,38 +509,43 @@ na2d_status_t na2d_backward(const void *q, const void *k, const void *v, const v
                             int W, int D, int kernel_size, int dilation, na2d_dtype_t dtype,
                             hipStream_t stream) {
   na2d::Shape s;
-  if (!dtype_ok(dtype)) return NA2D_ERROR_INVALID_VALUE;
-  na2d_status_t st = check_shape(B, heads, H, W, D, kernel_size, dilation, &s);
+  size_t need = 0;
+  na2d_status_t st = check_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, B, heads, H, W, D,
+                                    kernel_size, dilation, dtype, &s, &need);
   if (st != NA2D_SUCCESS) return st;
-  const void *ins[] = {q, k, v, dout};
-  void *outs[] = {dq, dk, dv};
-  for (const void *p : ins)
-    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
-  for (void *p : outs)
-    if (!p || !aligned16(p)) return NA2D_ERROR_INVALID_VALUE;
-  if ((rpb && !aligned16(rpb)) || (drpb && !aligned16(drpb))) return NA2D_ERROR_INVALID_VALUE;
-  if (!workspace || !aligned16(workspace)) return NA2D_ERROR_INVALID_VALUE;
-  const size_t need = na2d::backward_workspace_bytes(s, drpb != nullptr);
-  if (workspace_bytes < need) return NA2D_ERROR_INVALID_VALUE;
-  const int64_t tbytes = s.n_query * D * elem_bytes(dtype);
-  const int64_t side = 2 * kernel_size - 1;
-  const int64_t bbytes = heads * side * side * 4;
-  const int64_t rbytes = heads * side * side * elem_bytes(dtype);
-  // outputs (and the workspace) must not overlap each other or any input
-  struct Span { const void *p; int64_t n; };
-  const Span written[] = {{dq, tbytes}, {dk, tbytes}, {dv, tbytes}, {drpb, bbytes},
-                          {workspace, (int64_t)need}};
-  const Span read[] = {{q, tbytes}, {k, tbytes}, {v, tbytes}, {dout, tbytes}, {rpb, rbytes}};
-  for (int a = 0; a < 5; ++a) {
-    for (int b = a + 1; b < 5; ++b)
-      if (overlaps(written[a].p, written[a].n, written[b].p, written[b].n))
-        return NA2D_ERROR_INVALID_VALUE;
-    for (const Span &r : read)
-      if (overlaps(written[a].p, written[a].n, r.p, r.n)) return NA2D_ERROR_INVALID_VALUE;
-  }
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return NA2D_ERROR_INVALID_VALUE;
+  if (overlaps_backward(workspace, need, q, k, v, rpb, dout, dq, dk, dv, drpb, s, dtype))
+    return NA2D_ERROR_INVALID_VALUE;
   return from_hip(na2d::launch_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, workspace, s, dtype,
                                         stream));
 }
+
+na2d_status_t na2d_backward_noalloc(const void *q, const void *k, const void *v,
+                                    const void *rpb, const void *dout, void *dq, void *dk,
+                                    void *dv, float *drpb, int B, int heads, int H, int W, int D,
+                                    int kernel_size, int dilation, na2d_dtype_t dtype,
+                                    hipStream_t stream) {
+  na2d::Shape s;
+  size_t need = 0;
+  na2d_status_t st = check_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, B, heads, H, W, D,
+                                    kernel_size, dilation, dtype, &s, &need);
+  if (st != NA2D_SUCCESS) return st;
+  if (need > kScratchBytes) return NA2D_ERROR_WORKSPACE_LIMIT;  // before any HIP call
+  if (overlaps_backward(nullptr, 0, q, k, v, rpb, dout, dq, dk, dv, drpb, s, dtype))
+    return NA2D_ERROR_INVALID_VALUE;
+  void *ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != NA2D_SUCCESS) return st;
+  if (overlaps_backward(ws, need, q, k, v, rpb, dout, dq, dk, dv, drpb, s, dtype))
+    return NA2D_ERROR_INVALID_VALUE;
+  // the same kernels as na2d_backward, with the device array as workspace
+  // (they only write it before reading it: nothing needs clearing)
+  return from_hip(na2d::launch_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, ws, s, dtype,
+                                        stream));
+}
+
+size_t na2d_backward_noalloc_limit(void) { return kScratchBytes; }
 
 const char *na2d_status_string(na2d_status_t status) {
   switch (status) {
@@ -470,6 +557,10 @@ const char *na2d_status_string(na2d_status_t status) {
       return "NA2D_ERROR_NOT_SUPPORTED: valid but not implemented (D != 32, kernel_size > 13, "
              "MFMA with fp32, or grid too large)";
     case NA2D_ERROR_LAUNCH_FAILURE: return "NA2D_ERROR_LAUNCH_FAILURE: kernel launch failed";
+    case NA2D_ERROR_WORKSPACE_LIMIT:
+      return "NA2D_ERROR_WORKSPACE_LIMIT: the problem needs more workspace than the "
+             "allocation-free entry point's fixed device array holds "
+             "(na2d_backward_noalloc_limit() bytes)";
   }
   return "unknown na2d status";
 }

@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.na2d_backward.argtypes = [vp] * 10 + [ctypes.c_size_t] + [i] * 8 + [vp]
         L.na2d_backward_workspace_size.restype = ctypes.c_size_t
         L.na2d_backward_workspace_size.argtypes = [i] * 8
+        L.na2d_backward_noalloc.restype = i
+        L.na2d_backward_noalloc.argtypes = [vp] * 9 + [i] * 8 + [vp]
+        L.na2d_backward_noalloc_limit.restype = ctypes.c_size_t
+        L.na2d_backward_noalloc_limit.argtypes = []
         L.na2d_status_string.restype = ctypes.c_char_p
         L.na2d_status_string.argtypes = [i]
         L.na2d_version.restype = i
@@ -311,6 +315,30 @@ def na2d_backward(q, k, v, rpb, dout, dq, dk, dv, drpb, workspace, kernel_size: 
                              int(dilation), _DTYPE_CODES[q.dtype], _stream(q))
     _check(st, "na2d_backward")
     return dq, dk, dv, drpb
+
+
+def na2d_backward_noalloc(q, k, v, rpb, dout, dq, dk, dv, drpb, kernel_size: int,
+                          dilation: int):
+    """na2d_backward with the library's fixed device array as workspace (no
+    allocation in the call)."""
+    B, heads, H, W, D = _qkv_shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        _need(t, n, q.dtype, q.shape)
+    _rpb_check(rpb, q, heads, kernel_size)
+    side = 2 * kernel_size - 1
+    if drpb is not None:
+        _need(drpb, "drpb", torch.float32, (heads, side, side))
+    st = lib().na2d_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(rpb), _ptr(dout),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drpb), B, heads, H, W,
+                                     D, int(kernel_size), int(dilation), _DTYPE_CODES[q.dtype],
+                                     _stream(q))
+    _check(st, "na2d_backward_noalloc")
+    return dq, dk, dv, drpb
+
+
+def na2d_backward_noalloc_limit() -> int:
+    return int(lib().na2d_backward_noalloc_limit())
 
 
 # -- allocating conveniences (torch allocates the outputs; nothing else) ----
