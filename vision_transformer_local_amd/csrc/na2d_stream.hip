@@ -242,12 +242,15 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
   // only: from the fp32 weights' sum, not the 16-bit one the output is
   // divided by).
   auto weights = [&](f32x4 (&sc)[NB], vec (&pbs)[NB / 2]) -> float {
-    float mx = -INFINITY;
+    // the maximum as a tree (short dependency chains)
+    float m[NB];
 #pragma unroll
-    for (int a = 0; a < NB; ++a)
+    for (int a = 0; a < NB; ++a) m[a] = fmaxf(fmaxf(sc[a][0], sc[a][1]), fmaxf(sc[a][2], sc[a][3]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[a][i]);
-    mx = group_max(mx);
+    for (int w = 1; w < NB; w *= 2)
+#pragma unroll
+      for (int a = 0; a + w < NB; a += 2 * w) m[a] = fmaxf(m[a], m[a + w]);
+    const float mx = group_max(m[0]);
     const float mc = mx * c2;
     float l = 0.f;
 #pragma unroll
@@ -368,8 +371,8 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     // Key/value rows of the unit: those of step 0, [lo0, hi0], as np0
     // groups of 4 from lo0, then one group of 4 per step.  Step s needs
     // rows [window_start(R), window_start(R + 3) + k - 1], R = q0 + 4s: all
-    // in the groups up to s + 1, and no row below the one the group of step
-    // s + 1 overwrites (16 rows back).
+    // in the groups up to s, and none that the group of step s + 1
+    // overwrites (16 rows back).
     const int lo0 = window_start(t.q0, H, KS);
     const int hi0 = window_start(min(t.q0 + 3, t.q1 - 1), H, KS) + KS - 1;
     const int hiL = window_start(t.q1 - 1, H, KS) + KS - 1;  // the unit's last row
@@ -426,10 +429,10 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
                                                  kNonTemporal);
     };
 
-    // ---- unit prologue.  Loads first, in the order their results are
-    // needed (the bias values, the rows of step 0, the groups of steps 1
-    // and 2, the first two query slices), so that each wait below leaves
-    // the later loads in flight.
+    // ---- unit prologue.  The bias values, the rows of step 0 and its query
+    // slices first; the group of step 1, the query slices of step 1 and the
+    // group of step 2 only once the rows of step 0 are in, so that no unit's
+    // first rows queue behind other units' later ones.
     __syncthreads();  // the previous unit is done with the ring and the table
     const int tabkey = 2 * t.h + (t.flip ? 1 : 0);
     const bool newtab = tabkey != cur_h;
@@ -453,7 +456,6 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     issue(p1, lo0 + 4, live1);
     issue(p2, lo0 + 8, live2);
     q_load(0, qa0, qa1);
-    issue(set1, gbase + 4, gbase + 4 <= hiL);
     if (newtab) {
 #pragma unroll
       for (int it = 0; it < NT1; ++it) {
@@ -466,28 +468,23 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     commit(p0, lo0, true, 0);
     commit(p1, lo0 + 4, live1, hiL + 1);
     commit(p2, lo0 + 8, live2, lo0 + 8);
+    issue(set1, gbase + 4, gbase + 4 <= hiL);
+    q_load(1, qb0, qb1);
+    issue(set0, gbase + 8, gbase + 8 <= hiL);
     if (newtab) {
       __syncthreads();  // the table is complete
       cur_h = tabkey;
       build_cin();
     }
 
-    // One step: compute step s (query slices qs0, qs1), commit the group of
-    // step s + 1 from gc and reload gc with the group of step s + 3.
+    // One step: compute step s (query slices qs0, qs1, then reloaded with
+    // those of step s + 2), then commit the group of step s + 1 from gc and
+    // reload gc with the group of step s + 3.  The commit comes after the
+    // compute so that a step waits only for its own query slices; waves
+    // still computing step s read no slot it writes (it lands 16 rows past
+    // the step's first key row minus 4 or more).
     auto step = [&](int s, Regs<NP> &gc, u32x4 &qs0, u32x4 &qs1) {
-      __syncthreads();  // step s's rows visible; step s - 1 done with its slots
-      {
-        const int y1 = gbase + 4 * (s + 1), y3 = gbase + 4 * (s + 3);
-        commit(gc, y1, y1 <= hiL, hiL + 1);
-        if (s == 0) {
-          // the group and query slices of step 2 and 1: issued here, not in
-          // the prologue, so that the rows of step 0 do not queue behind
-          // them
-          issue(set0, gbase + 8, gbase + 8 <= hiL);
-          q_load(1, qb0, qb1);
-        }
-        issue(gc, y3, y3 <= hiL);
-      }
+      __syncthreads();  // step s's rows visible
       const int R0 = t.q0 + 4 * s;                    // the step's first query row
       const int R = min(R0, t.q1 - 1);                // (a step past the unit computes a real one)
       const vec q0v = __builtin_bit_cast(vec, shuffle(qs0, qsrc));
@@ -498,31 +495,34 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
         // all four query rows unclamped: tile 1's key rows are tile 0's
         // shifted by 2; the accumulator inputs are the per-wave ones
         const int Y0 = R - G::R;
+        // every LDS read of the step is issued before its first use: the
+        // key rows, then the V^T operands (needed after the softmax)
+        vec kr[NS];
+#pragma unroll
+        for (int a = 0; a < NS; ++a) kr[a] = k_row(Y0 + a);
+        vec va[NS / 2], vb[NS / 2];
+#pragma unroll
+        for (int j = 0; j < NS / 2; ++j) v_pair(Y0 + 2 * j, va[j], vb[j]);
         f32x4 sc0[NB], sc1[NB];
 #pragma unroll
-        for (int a = 0; a < NS; ++a) {
-          const vec kv = k_row(Y0 + a);
-          if (a < NB) sc0[a] = Mma<T>::run(kv, q0v, cin[a]);
-          if (a >= 2) sc1[a - 2] = Mma<T>::run(kv, q1v, cin[a - 2]);
-        }
+        for (int a = 0; a < NB; ++a) sc0[a] = Mma<T>::run(kr[a], q0v, cin[a]);
+#pragma unroll
+        for (int a = 0; a < NB; ++a) sc1[a] = Mma<T>::run(kr[a + 2], q1v, cin[a]);
         vec pb0[NB / 2], pb1[NB / 2];
         lse0 = weights(sc0, pb0);
-        lse1 = weights(sc1, pb1);
         f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, o2 = o0, u0 = o0, u1 = o0, u2 = o0;
 #pragma unroll
-        for (int j = 0; j < NS / 2; ++j) {
-          vec va, vb;
-          v_pair(Y0 + 2 * j, va, vb);
-          if (j < NB / 2) {
-            o0 = Mma<T>::run(va, pb0[j], o0);
-            o1 = Mma<T>::run(vb, pb0[j], o1);
-            o2 = Mma<T>::run(ones, pb0[j], o2);
-          }
-          if (j >= 1) {
-            u0 = Mma<T>::run(va, pb1[j - 1], u0);
-            u1 = Mma<T>::run(vb, pb1[j - 1], u1);
-            u2 = Mma<T>::run(ones, pb1[j - 1], u2);
-          }
+        for (int j = 0; j < NB / 2; ++j) {
+          o0 = Mma<T>::run(va[j], pb0[j], o0);
+          o1 = Mma<T>::run(vb[j], pb0[j], o1);
+          o2 = Mma<T>::run(ones, pb0[j], o2);
+        }
+        lse1 = weights(sc1, pb1);
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j) {
+          u0 = Mma<T>::run(va[j + 1], pb1[j], u0);
+          u1 = Mma<T>::run(vb[j + 1], pb1[j], u1);
+          u2 = Mma<T>::run(ones, pb1[j], u2);
         }
         res0 = finish(o0, o1, o2);
         res1 = finish(u0, u1, u2);
@@ -569,6 +569,9 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse0), lrs, lf0, 0, kNonTemporal);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse1), lrs, lf1, 0, kNonTemporal);
       }
+      const int y1 = gbase + 4 * (s + 1), y3 = gbase + 4 * (s + 3);
+      commit(gc, y1, y1 <= hiL, hiL + 1);
+      issue(gc, y3, y3 <= hiL);
     };
     // Two steps per iteration so that register sets are fixed: the group of
     // step s + 1 sits in set (s + 1) % 2, the query slices of step s in
