@@ -80,12 +80,17 @@ template <int KS, int RYV = default_rows(KS)> struct Geometry {
   // (u + TY-1) * IW + w + TX, holds bias * sqrt(D) inside the k x k window and
   // -inf outside.  Then the bias table (times sqrt(D)) with zero margins; its
   // entry (0, 0) sits at BOFF.  The interior table starts at offset 0 so that
-  // a lane's reads of it fit the immediate offsets of one base address.
-  static constexpr int IU = NB + TY - 1, IW = 16 + TX;
+  // a lane's reads of it fit the immediate offsets of one base address.  The
+  // row pitch IW (at least 16 + TX) is chosen for the LDS banks: the lanes of
+  // a read span TX + 4 consecutive entries in each of TY table rows, and a
+  // pitch of 16 (TY = 2) or 8 (TY = 4) banks mod 32 keeps those row ranges
+  // on distinct banks (TY = 2) or overlapping in one bank (TY = 4).
+  static constexpr int IU = NB + TY - 1, IW = TY == 2 ? 48 : 40;
   static constexpr int NINT = IU * IW;
   static constexpr int BOFF = NINT + MARGIN;
   static constexpr int NTAB = NINT + SIDE * SIDE + 2 * MARGIN;
   static_assert(TX + KS - 1 <= 16, "key columns do not cover the tile");
+  static_assert(IW >= 16 + TX, "interior table rows hold the tile's key columns");
   static_assert(NB % 2 == 0, "PV consumes key rows in pairs");
   static_assert(RY % TY == 0 && RX % TX == 0, "blocks hold whole tiles");
   static_assert(THREADS <= 1024, "one workgroup");
