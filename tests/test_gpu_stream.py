@@ -1,6 +1,6 @@
-"""GPU parity of the row-streaming forward kernel (maps without dilation,
-k in {3, 5, 7}, bf16 / fp16, 33 to 56 columns, at least 16 rows) against the
-float64 oracle.
+"""GPU parity of the row-streaming forward kernel (k in {3, 5, 7}, bf16 /
+fp16, maps -- with dilation d dividing H and W, residue classes -- 33 to 56
+columns wide and at least 16 rows high) against the float64 oracle.
 
 The shapes are chosen for the kernel's own structure: every workgroup width
 (5, 6 and 7 tile columns of 8, ragged last tiles), query-row runs split into
@@ -41,6 +41,34 @@ def test_stream_kernel_matches_oracle(H, W, ks, dtype):
         compare(p, out, cpu)
 
 
+DILATED = [(64, 80, 2, 7), (48, 105, 3, 5), (100, 168, 4, 7), (34, 66, 2, 3), (96, 264, 6, 7)]
+
+
+@pytest.mark.parametrize("H,W,d,ks", DILATED, ids=str)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stream_kernel_dilated(H, W, d, ks, dtype):
+    """Dilated maps whose residue classes are all (H/d) x (W/d): the kernel
+    runs on the classes; the block-tiled kernel on the same inputs too."""
+    p = Problem(2, 2, H, W, 32, ks, d, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=H + W + d)
+    for algo in ("mfma", "mfma_tiled"):
+        note("stream dilated %s algo=%s" % (p.describe(), algo))
+        out = na2d.forward(q, k, v, rpb, ks, d, algo=algo)
+        torch.cuda.synchronize()
+        compare(p, out, cpu)
+
+
+def test_stream_kernel_detection_d8_full_size():
+    """Detection resolution at d = 8 (classes of 25 x 42), one batch and two
+    heads, every output against the oracle."""
+    p = Problem(1, 2, 200, 336, 32, 7, 8, "bf16")
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=88)
+    note("stream detection d8 %s" % p.describe())
+    out = na2d.forward(q, k, v, rpb, 7, 8)
+    torch.cuda.synchronize()
+    compare(p, out, cpu)
+
+
 @pytest.mark.parametrize("B", [1, 3, 7, 16])
 def test_stream_kernel_unit_splits(B):
     """The number of query-row units per plane depends on the batch (units
@@ -56,7 +84,9 @@ def test_stream_kernel_unit_splits(B):
 
 @pytest.mark.parametrize("p", [Problem(1, 2, 56, 56, 32, 7, 1, "bf16"),
                                Problem(2, 2, 21, 47, 32, 5, 1, "f16"),
-                               Problem(3, 1, 30, 35, 32, 3, 1, "bf16")],
+                               Problem(3, 1, 30, 35, 32, 3, 1, "bf16"),
+                               Problem(1, 2, 64, 88, 32, 7, 2, "bf16"),
+                               Problem(2, 1, 48, 105, 32, 5, 3, "f16")],
                          ids=lambda p: p.describe().replace(" ", "_"))
 def test_stream_kernel_lse(p):
     """The log-sum-exp variant: the same output bits as the plain forward,
@@ -65,12 +95,12 @@ def test_stream_kernel_lse(p):
     map upward."""
     cpu, (q, k, v, rpb) = gpu_inputs(p, seed=31)
     note("stream lse %s" % p.describe())
-    out, lse = na2d.forward_lse(q, k, v, rpb, p.kernel_size, 1)
-    ref_out = na2d.forward(q, k, v, rpb, p.kernel_size, 1)
+    out, lse = na2d.forward_lse(q, k, v, rpb, p.kernel_size, p.dilation)
+    ref_out = na2d.forward(q, k, v, rpb, p.kernel_size, p.dilation)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out)
     compare(p, out, cpu)
-    ref = oracle.forward(*cpu, p.kernel_size, 1, lse=True)["lse"]
+    ref = oracle.forward(*cpu, p.kernel_size, p.dilation, lse=True)["lse"]
     err = float(np.abs(lse.cpu().double().numpy() - ref).max())
     assert err <= 2e-5, err
 
@@ -86,19 +116,20 @@ def test_stream_kernel_no_bias_and_zero_bias():
     compare(p, a, (cpu[0], cpu[1], cpu[2], torch.zeros_like(cpu[3])))
 
 
-def test_stream_kernel_channels_last():
+@pytest.mark.parametrize("d", [1, 2])
+def test_stream_kernel_channels_last(d):
     """q, k, v and out as channels-last hidden states [B, H, W, heads*D]."""
-    p = Problem(2, 4, 28, 44, 32, 7, 1, "bf16")
+    p = Problem(2, 4, 28 * d, 44 * d, 32, 7, d, "bf16")
     cpu, (q, k, v, rpb) = gpu_inputs(p, seed=12)
 
     def cl(t):
         return t.permute(0, 2, 3, 1, 4).reshape(p.B, p.H, p.W, -1).contiguous()
     note("stream channels-last %s" % p.describe())
-    out = na2d.forward_channels_last(cl(q), cl(k), cl(v), rpb, p.heads, 7, 1)
+    out = na2d.forward_channels_last(cl(q), cl(k), cl(v), rpb, p.heads, 7, d)
     torch.cuda.synchronize()
     out = na2d.heads_view(out, p.heads).contiguous()
     compare(p, out, cpu)
-    dense = na2d.forward(q, k, v, rpb, 7, 1)
+    dense = na2d.forward(q, k, v, rpb, 7, d)
     torch.cuda.synchronize()
     assert torch.equal(out, dense)
 

@@ -157,9 +157,10 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
                              const mfma::ByteStrides &out_st, const Pad &pad,
                              na2d_dtype_t dt, hipStream_t st, bool *supported,
                              float *lse = nullptr);
-// Row-streaming kernel (no dilation, k in {3, 5, 7}, 16-bit data, maps 33
-// to 56 columns wide and at least 16 rows high); byte strides as the general
-// kernel's; lse (optional) as the general kernel's, dense q only.
+// Row-streaming kernel (k in {3, 5, 7}, 16-bit data, maps -- with dilation d
+// dividing H and W, residue classes -- 33 to 56 columns wide and at least 16
+// rows high); byte strides as the general kernel's; lse (optional) as the
+// general kernel's, dense q only.
 bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt);
 hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
                               void *out, float *lse, const Shape &s,

@@ -1,6 +1,7 @@
-// na2d_stream.hip -- row-streaming fused forward of 2D Neighborhood Attention
-// (no dilation) on the CDNA4 matrix cores: bf16 / fp16 inputs, fp32
-// accumulation, D = 32, kernel sizes 3, 5, 7, maps up to 56 columns wide.
+// na2d_stream.hip -- row-streaming fused forward of 2D (dilated) Neighborhood
+// Attention on the CDNA4 matrix cores: bf16 / fp16 inputs, fp32
+// accumulation, D = 32, kernel sizes 3, 5, 7, maps (or, with dilation d,
+// residue classes) 33 to 56 columns wide.
 //
 // The operator is the one the DiNAT module composes from natten2dqkrpb,
 // softmax(dim=-1) and natten2dav (DiNAT walk-through blog, "What is DiNAT");
@@ -36,6 +37,15 @@
 //      pixels, 128 contiguous bytes, and the second channel block sits at a
 //      fixed offset.
 // Ring row y & 15 holds pixel row y.
+//
+// Dilation.  With dilation d the pixels (ry + d*i, rx + d*j) of one residue
+// class form an ordinary map on which the operator is plain neighborhood
+// attention (DiNAT walk-through blog, "What is DiNAT": the window samples
+// every d-th pixel).  When d divides H and W every class is (H/d) x (W/d);
+// the kernel then runs on the classes as on maps of that size, with the
+// row and column strides multiplied by d.  Units are numbered with rx
+// fastest, so the classes rx and rx + 1, whose pixels share 128-byte lines,
+// run at the same time on one XCD and the second read of each line hits L2.
 #include "na2d_mfma_common.h"
 
 #include <limits.h>
@@ -79,7 +89,8 @@ template <int KS, int NTX> struct StreamGeo {
   static_assert(VHALF < (1 << 16), "the second V half is a 16-bit immediate offset");
 };
 
-// One unit of work: a (batch, head) plane and a run of its query rows.
+// One unit of work: a residue class of a (batch, head) plane (the plane
+// itself without dilation) and a run of its query rows.
 // Units alternate direction: an even one walks down its rows, an odd one up
 // (it sees the map flipped upside down: row y of the unit is memory row
 // H - 1 - y, and the bias table's rows are reversed).  The two units that
@@ -88,27 +99,41 @@ template <int KS, int NTX> struct StreamGeo {
 // finds them in the cache, and the first and last units of a plane start at
 // the map's edge, where the windows of the first query rows overlap most.
 struct Unit {
-  int64_t pin, pout;     // byte offsets of the plane in q/k/v and in out
+  int64_t pin, pout;     // byte offsets of the class origin in q/k/v and in out
+  int64_t lpix;          // pixel index of the class origin in [B, heads, H, W]
   int h, q0, q1, nsteps; // query rows [q0, q1) in the unit's own row order
   bool flip;
 };
 
+// s: the class map (H/d x W/d, dilation 1); si, so: strides within a class
+// (row and column strides of the map times d); pixel strides of the map
+// for the class origins, and the map's size for the log-sum-exp index.
 struct StreamArgs {
   Shape s;
   ByteStrides si, so;
-  int seg, nseg;           // query rows per unit, units per plane
+  int dil, Hm, Wm;         // dilation; the map's rows and columns
+  int oyi, oxi, oyo, oxo;  // map row / column strides of q, k, v and of out (bytes)
+  int seg, nseg;           // query rows per unit, units per class
   int nunits;
-  FastDiv fseg, fheads;
+  FastDiv fseg, fheads, fdil;
 };
 
 __device__ __forceinline__ Unit unit_at(int u, const StreamArgs &a) {
   Unit t;
-  const uint32_t plane = fast_div((uint32_t)u, a.fseg);
-  const int sg = u - (int)plane * a.nseg;
-  const uint32_t b = fast_div(plane, a.fheads);
-  t.h = (int)(plane - b * a.s.heads);
-  t.pin = (int64_t)b * a.si.b + (int64_t)t.h * a.si.h;
-  t.pout = (int64_t)b * a.so.b + (int64_t)t.h * a.so.h;
+  // u = ((((b * heads + h) * d + ry) * d + rx) * nseg + sg
+  const uint32_t cls = fast_div((uint32_t)u, a.fseg);
+  const int sg = u - (int)cls * a.nseg;
+  const uint32_t t1 = fast_div(cls, a.fdil);
+  const int rx = (int)(cls - t1 * a.dil);
+  const uint32_t bh = fast_div(t1, a.fdil);
+  const int ry = (int)(t1 - bh * a.dil);
+  const uint32_t b = fast_div(bh, a.fheads);
+  t.h = (int)(bh - b * a.s.heads);
+  t.pin = (int64_t)b * a.si.b + (int64_t)t.h * a.si.h + (int64_t)ry * a.oyi +
+          (int64_t)rx * a.oxi;
+  t.pout = (int64_t)b * a.so.b + (int64_t)t.h * a.so.h + (int64_t)ry * a.oyo +
+           (int64_t)rx * a.oxo;
+  t.lpix = (int64_t)bh * a.Hm * a.Wm + (int64_t)ry * a.Wm + rx;
   const int r0 = sg * a.seg, r1 = min(r0 + a.seg, a.s.H);
   t.flip = (sg & 1) != 0;
   t.q0 = t.flip ? a.s.H - r1 : r0;
@@ -137,11 +162,15 @@ constexpr int kNonTemporal = 2;
 constexpr int kRsrcWord3 = 0x00020000;
 
 // LSE: also write each query's log-sum-exp to lse, [B, heads, H, W] (dense
-// q only).
-template <typename T, int KS, int NTX, bool LSE>
+// q only).  STREAM: query loads and output / lse stores are non-temporal
+// (without dilation each line belongs to one unit); with dilation the
+// classes rx and rx + 1 share every line of q and out, so those accesses stay
+// cached and the second class finds the line in L2.
+template <typename T, int KS, int NTX, bool LSE, bool STREAM>
 __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, float *__restrict__ lse, StreamArgs A) {
+  constexpr int kQO = STREAM ? kNonTemporal : 0;  // cache policy of q, out and lse
   using G = StreamGeo<KS, NTX>;
   using vec = typename Mma<T>::vec;
   constexpr int NB = G::NB, NS = G::NS, NP = G::NP, SIDE = G::SIDE, R = G::R;
@@ -361,12 +390,11 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     // which the hardware drops
     const __amdgpu_buffer_rsrc_t ors =
         __builtin_amdgcn_make_buffer_rsrc((char *)out + t.pout, 0, outspan, kRsrcWord3);
-    // the plane of lse (dense q: the plane's offset over the D channels of a
-    // pixel is its offset in pixels)
+    // lse from the class origin: class pixel (i, j) is map pixel
+    // (d*i, d*j) from there
     __amdgpu_buffer_rsrc_t lrs;
     if constexpr (LSE)
-      lrs = __builtin_amdgcn_make_buffer_rsrc(lse + t.pin / (kHeadDim * (int64_t)sizeof(T)), 0,
-                                              H * W * 4, kRsrcWord3);
+      lrs = __builtin_amdgcn_make_buffer_rsrc(lse + t.lpix, 0, A.Hm * A.Wm * 4, kRsrcWord3);
 
     // Key/value rows of the unit: those of step 0, [lo0, hi0], as np0
     // groups of 4 from lo0, then one group of 4 per step.  Step s needs
@@ -424,9 +452,9 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
         rb = H - 1 - rb;
       }
       qa = __builtin_amdgcn_raw_buffer_load_b128(qr, (uint32_t)ra * A.si.y + qcol, 0,
-                                                 kNonTemporal);
+                                                 kQO);
       qb = __builtin_amdgcn_raw_buffer_load_b128(qr, (uint32_t)rb * A.si.y + qcol, 0,
-                                                 kNonTemporal);
+                                                 kQO);
     };
 
     // ---- unit prologue.  The bias values, the rows of step 0 and its query
@@ -555,8 +583,8 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
       const int yb = t.flip ? H - 3 - (R0 + lpy) : R0 + 2 + lpy;
       const uint32_t oo0 = ok0 ? (uint32_t)ya * A.so.y + ocol : 0x80000000u;
       const uint32_t oo1 = ok1 ? (uint32_t)yb * A.so.y + ocol : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b128(res0, ors, oo0, 0, kNonTemporal);
-      __builtin_amdgcn_raw_buffer_store_b128(res1, ors, oo1, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b128(res0, ors, oo0, 0, kQO);
+      __builtin_amdgcn_raw_buffer_store_b128(res1, ors, oo1, 0, kQO);
       if constexpr (LSE) {
         // lane (0, ql) writes query ql of each tile: row R0 + qy (+ 2),
         // column C + qx
@@ -564,10 +592,10 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
         const bool l0 = col_ok && R0 + qy < t.q1, l1 = col_ok && R0 + 2 + qy < t.q1;
         const int la = t.flip ? H - 1 - (R0 + qy) : R0 + qy;
         const int lb = t.flip ? H - 3 - (R0 + qy) : R0 + 2 + qy;
-        const uint32_t lf0 = l0 ? (uint32_t)(la * W + C + qx) * 4u : 0x80000000u;
-        const uint32_t lf1 = l1 ? (uint32_t)(lb * W + C + qx) * 4u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse0), lrs, lf0, 0, kNonTemporal);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse1), lrs, lf1, 0, kNonTemporal);
+        const uint32_t lf0 = l0 ? (uint32_t)(la * A.Wm + C + qx) * (uint32_t)(4 * A.dil) : 0x80000000u;
+        const uint32_t lf1 = l1 ? (uint32_t)(lb * A.Wm + C + qx) * (uint32_t)(4 * A.dil) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse0), lrs, lf0, 0, kQO);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse1), lrs, lf1, 0, kQO);
       }
       const int y1 = gbase + 4 * (s + 1), y3 = gbase + 4 * (s + 3);
       commit(gc, y1, y1 <= hiL, hiL + 1);
@@ -591,30 +619,42 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
   }
 }
 
+// m: the map's shape; c: the class map (m.H / d x m.W / d, dilation 1).
 template <typename T, int KS, int NTX>
 hipError_t launch_stream_t(const void *q, const void *k, const void *v, const void *rpb,
-                           void *out, float *lse, const Shape &s, const ByteStrides &si,
-                           const ByteStrides &so, hipStream_t st) {
+                           void *out, float *lse, const Shape &m, const Shape &c,
+                           const ByteStrides &si, const ByteStrides &so, hipStream_t st) {
   using G = StreamGeo<KS, NTX>;
   StreamArgs a;
-  a.s = s;
-  a.si = si;
-  a.so = so;
-  const int64_t planes = (int64_t)s.B * s.heads;
+  a.s = c;
+  a.si = ByteStrides{si.b, si.h, si.y * (uint32_t)m.dil, si.x * (uint32_t)m.dil};
+  a.so = ByteStrides{so.b, so.h, so.y * (uint32_t)m.dil, so.x * (uint32_t)m.dil};
+  a.dil = m.dil;
+  a.Hm = m.H;
+  a.Wm = m.W;
+  a.oyi = (int)si.y;
+  a.oxi = (int)si.x;
+  a.oyo = (int)so.y;
+  a.oxo = (int)so.x;
+  const int64_t classes = (int64_t)m.B * m.heads * m.dil * m.dil;
   const int cus = device_compute_units();
   // rows per unit: a multiple of 4, split until there are about as many
   // units as compute units (one workgroup per compute unit)
   int nseg = 1;
-  while (planes * (nseg + 1) <= cus && (s.H + nseg) / (nseg + 1) >= 12) ++nseg;
-  a.seg = (((s.H + nseg - 1) / nseg) + 3) & ~3;
-  a.nseg = (s.H + a.seg - 1) / a.seg;
-  const int64_t nunits = planes * a.nseg;
+  while (classes * (nseg + 1) <= cus && (c.H + nseg) / (nseg + 1) >= 12) ++nseg;
+  a.seg = (((c.H + nseg - 1) / nseg) + 3) & ~3;
+  a.nseg = (c.H + a.seg - 1) / a.seg;
+  const int64_t nunits = classes * a.nseg;
   if (nunits > INT_MAX) return hipErrorInvalidConfiguration;
   a.nunits = (int)nunits;
   a.fseg = make_fastdiv((uint32_t)a.nseg);
-  a.fheads = make_fastdiv((uint32_t)s.heads);
+  a.fheads = make_fastdiv((uint32_t)m.heads);
+  a.fdil = make_fastdiv((uint32_t)m.dil);
   const int grid = (int)(nunits < cus ? nunits : cus);
-  auto kern = lse ? stream_mfma_kernel<T, KS, NTX, true> : stream_mfma_kernel<T, KS, NTX, false>;
+  auto kern = m.dil == 1 ? (lse ? stream_mfma_kernel<T, KS, NTX, true, true>
+                                 : stream_mfma_kernel<T, KS, NTX, false, true>)
+                         : (lse ? stream_mfma_kernel<T, KS, NTX, true, false>
+                                : stream_mfma_kernel<T, KS, NTX, false, false>);
   kern<<<dim3((unsigned)grid), G::THREADS, 0, st>>>((const T *)q, (const T *)k, (const T *)v,
                                                     (const T *)rpb, (T *)out, lse, a);
   return hipGetLastError();
@@ -622,25 +662,33 @@ hipError_t launch_stream_t(const void *q, const void *k, const void *v, const vo
 
 template <typename T, int KS>
 hipError_t launch_stream_k(const void *q, const void *k, const void *v, const void *rpb,
-                           void *out, float *lse, const Shape &s, const ByteStrides &si,
+                           void *out, float *lse, const Shape &m, const ByteStrides &si,
                            const ByteStrides &so, hipStream_t st) {
-  // one wave per 8-column tile column of the map
-  switch ((s.W + 7) / 8) {
-    case 5: return launch_stream_t<T, KS, 5>(q, k, v, rpb, out, lse, s, si, so, st);
-    case 6: return launch_stream_t<T, KS, 6>(q, k, v, rpb, out, lse, s, si, so, st);
-    default: return launch_stream_t<T, KS, 7>(q, k, v, rpb, out, lse, s, si, so, st);
+  Shape c = m;
+  c.H = m.H / m.dil;
+  c.W = m.W / m.dil;
+  c.dil = 1;
+  // one wave per 8-column tile column of the class map
+  switch ((c.W + 7) / 8) {
+    case 5: return launch_stream_t<T, KS, 5>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 6: return launch_stream_t<T, KS, 6>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    default: return launch_stream_t<T, KS, 7>(q, k, v, rpb, out, lse, m, c, si, so, st);
   }
 }
 
 }  // namespace
 
-// Maps 33 to 56 columns wide (5 to 7 waves per workgroup) and at least 16
-// rows high.  Narrower or shorter maps run faster on the block-tiled kernel:
-// their planes hold too few rows to hide a unit's first window, and too few
-// waves would share a compute unit.
+// Maps (with dilation d: residue classes, all of one size when d divides H
+// and W) 33 to 56 columns wide (5 to 7 waves per workgroup) and at least 16
+// rows high.  Narrower or shorter ones run faster on the block-tiled kernel:
+// they hold too few rows to hide a unit's first window, and too few waves
+// would share a compute unit.
 bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt) {
-  return (dt == NA2D_DTYPE_BF16 || dt == NA2D_DTYPE_F16) && s.dil == 1 &&
-         (s.ks == 3 || s.ks == 5 || s.ks == 7) && s.W > 32 && s.W <= 56 && s.H >= 16;
+  if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) return false;
+  if (s.ks != 3 && s.ks != 5 && s.ks != 7) return false;
+  if (s.H % s.dil != 0 || s.W % s.dil != 0) return false;
+  const int hc = s.H / s.dil, wc = s.W / s.dil;
+  return wc > 32 && wc <= 56 && hc >= 16;
 }
 
 hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
