@@ -1,6 +1,7 @@
 """GPU parity of the row-streaming forward kernel (k in {3, 5, 7}, bf16 /
-fp16, maps -- with dilation d dividing H and W, residue classes -- 33 to 56
-columns wide and at least 16 rows high) against the float64 oracle.
+fp16, maps -- with dilation d dividing H and W, residue classes -- more than
+32 columns wide, in strips of 56 columns beyond 56, and at least 16 rows
+high) against the float64 oracle.
 
 The shapes are chosen for the kernel's own structure: every workgroup width
 (5, 6 and 7 tile columns of 8, ragged last tiles), query-row runs split into
@@ -41,7 +42,39 @@ def test_stream_kernel_matches_oracle(H, W, ks, dtype):
         compare(p, out, cpu)
 
 
-DILATED = [(64, 80, 2, 7), (48, 105, 3, 5), (100, 168, 4, 7), (34, 66, 2, 3), (96, 264, 6, 7)]
+WIDE = [(20, 57, 7), (33, 120, 5), (17, 200, 3), (24, 113, 7), (16, 64, 7)]
+
+
+@pytest.mark.parametrize("H,W,ks", WIDE, ids=str)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stream_kernel_column_strips(H, W, ks, dtype):
+    """Maps wider than 56 columns: units cover strips of 56 query columns
+    (the last one ragged) with k - 1 staged key columns past the strip."""
+    p = Problem(2, 2, H, W, 32, ks, 1, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=H * 7 + W)
+    for algo in ("mfma", "mfma_tiled"):
+        note("stream strips %s algo=%s" % (p.describe(), algo))
+        out = na2d.forward(q, k, v, rpb, ks, 1, algo=algo)
+        torch.cuda.synchronize()
+        compare(p, out, cpu)
+
+
+def test_stream_kernel_detection_d1_full_size():
+    """Detection resolution without dilation (six strips of 56 columns), one
+    batch and two heads, every output against the oracle; lse too."""
+    p = Problem(1, 2, 200, 336, 32, 7, 1, "bf16")
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=89)
+    note("stream detection d1 %s" % p.describe())
+    out, lse = na2d.forward_lse(q, k, v, rpb, 7, 1)
+    ref_out = na2d.forward(q, k, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    compare(p, out, cpu)
+    ref = oracle.forward(*cpu, 7, 1, lse=True)["lse"]
+    assert float(np.abs(lse.cpu().double().numpy() - ref).max()) <= 2e-5
+
+
+DILATED = [(130, 130, 2, 7), (64, 80, 2, 7), (48, 105, 3, 5), (100, 168, 4, 7), (34, 66, 2, 3), (96, 264, 6, 7)]
 
 
 @pytest.mark.parametrize("H,W,d,ks", DILATED, ids=str)

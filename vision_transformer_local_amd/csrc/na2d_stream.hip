@@ -62,12 +62,18 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // 16-byte chunk permutation of the K ring (see the header comment).
 __device__ __forceinline__ int kswz(int c) { return (c >> 1) & 3; }
 
-template <int KS, int NTX> struct StreamGeo {
+// STRIPS: the map is wider than 8 * NTX columns and each unit covers one
+// strip of 8 * NTX query columns (its staged key columns reach k - 1 past
+// it); one more wave then shares the loads (and repeats the last tile
+// column's compute on the otherwise idle fourth SIMD, storing nothing), so
+// that each lane stages as many pieces as without strips.
+template <int KS, int NTX, bool STRIPS = false> struct StreamGeo {
   static constexpr int R = KS / 2;
   static constexpr int TX = 8;                    // tile: 2 rows x 8 columns
   static constexpr int NB = KS + 1;               // key rows per tile
   static constexpr int NS = NB + 2;               // key rows of a wave's two tiles
-  static constexpr int THREADS = 64 * NTX;        // one wave per tile column
+  static constexpr int WAVES = NTX + (STRIPS ? 1 : 0);
+  static constexpr int THREADS = 64 * WAVES;      // one wave per tile column
   static constexpr int CW = 8 * NTX;              // query columns
   static constexpr int SCW = CW + 8;              // staged columns (reads reach CW + 7)
   static constexpr int RING = 16;                 // staged rows
@@ -82,8 +88,10 @@ template <int KS, int NTX> struct StreamGeo {
   static constexpr int TABOFF = VOFF + 2 * VHALF; // bias table (times sqrt(D)), zero margins
   static constexpr int LDS = TABOFF + NTAB * 4;
   // 16-byte pieces per lane and tensor for one group of 4 rows (at most CW
-  // columns of 4 chunks)
-  static constexpr int NP = (16 * CW + THREADS - 1) / THREADS;
+  // staged columns of 4 chunks, CW + k - 1 with strips)
+  static constexpr int NK = STRIPS ? CW + KS - 1 : CW;
+  static constexpr int NP = (16 * NK + THREADS - 1) / THREADS;
+  static_assert(NK <= SCW, "staged columns fit the ring rows");
   static_assert(NB % 2 == 0 && NB <= 8, "tile key rows");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(VHALF < (1 << 16), "the second V half is a 16-bit immediate offset");
@@ -102,6 +110,7 @@ struct Unit {
   int64_t pin, pout;     // byte offsets of the class origin in q/k/v and in out
   int64_t lpix;          // pixel index of the class origin in [B, heads, H, W]
   int h, q0, q1, nsteps; // query rows [q0, q1) in the unit's own row order
+  int strip;             // query columns [strip * CW, strip * CW + CW) of the map
   bool flip;
 };
 
@@ -113,16 +122,19 @@ struct StreamArgs {
   ByteStrides si, so;
   int dil, Hm, Wm;         // dilation; the map's rows and columns
   int oyi, oxi, oyo, oxo;  // map row / column strides of q, k, v and of out (bytes)
-  int seg, nseg;           // query rows per unit, units per class
+  int seg, nseg;           // query rows per unit, units per class and strip
+  int nstrip;              // column strips per class
   int nunits;
-  FastDiv fseg, fheads, fdil;
+  FastDiv fseg, fheads, fdil, fstrip;
 };
 
 __device__ __forceinline__ Unit unit_at(int u, const StreamArgs &a) {
   Unit t;
-  // u = ((((b * heads + h) * d + ry) * d + rx) * nseg + sg
-  const uint32_t cls = fast_div((uint32_t)u, a.fseg);
-  const int sg = u - (int)cls * a.nseg;
+  // u = (((((b * heads + h) * d + ry) * d + rx) * nstrip + strip) * nseg + sg
+  const uint32_t cs = fast_div((uint32_t)u, a.fseg);
+  const int sg = u - (int)cs * a.nseg;
+  const uint32_t cls = fast_div(cs, a.fstrip);
+  t.strip = (int)(cs - cls * a.nstrip);
   const uint32_t t1 = fast_div(cls, a.fdil);
   const int rx = (int)(cls - t1 * a.dil);
   const uint32_t bh = fast_div(t1, a.fdil);
@@ -166,12 +178,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 // (without dilation each line belongs to one unit); with dilation the
 // classes rx and rx + 1 share every line of q and out, so those accesses stay
 // cached and the second class finds the line in L2.
-template <typename T, int KS, int NTX, bool LSE, bool STREAM>
-__global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_kernel(
+template <typename T, int KS, int NTX, bool LSE, bool STREAM, bool STRIPS>
+__global__ __launch_bounds__((StreamGeo<KS, NTX, STRIPS>::THREADS)) void stream_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ rpb, T *__restrict__ out, float *__restrict__ lse, StreamArgs A) {
   constexpr int kQO = STREAM ? kNonTemporal : 0;  // cache policy of q, out and lse
-  using G = StreamGeo<KS, NTX>;
+  using G = StreamGeo<KS, NTX, STRIPS>;
   using vec = typename Mma<T>::vec;
   constexpr int NB = G::NB, NS = G::NS, NP = G::NP, SIDE = G::SIDE, R = G::R;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
@@ -184,37 +196,21 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
   const bool has_rpb = rpb != nullptr;
   const float c2 = kLog2e / kSqrtD;
 
-  // ---- per-lane constants of the kernel (the map width is fixed)
-  // this lane's pieces of a 4-row group: (row, column, chunk); lanes beyond
-  // the group's 16*W pieces repeat one (same data, same place).  Every load,
-  // LDS write and store below is unconditional, so that the count of memory
-  // operations in flight is the same on every path and the compiler's waits
-  // before a use cover exactly the operation it needs.
+  // ---- per-lane constants of a column strip (the whole map without
+  // strips): set by set_strip when a unit's strip differs from the last one.
+  // This lane's pieces of a 4-row group: (row, staged column, chunk); lanes
+  // beyond the group's 16 * nk pieces repeat one (same data, same place).
+  // Every load, LDS write and store below is unconditional, so that the
+  // count of memory operations in flight is the same on every path and the
+  // compiler's waits before a use cover exactly the operation it needs.
   Piece<NP> pc;
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    int f = tid + j * G::THREADS;
-    f = f < 16 * W ? f : f % (16 * W);
-    const int p = f & 3, cx = f >> 2;            // chunk; row * W + column
-    int rr = 0;
-#pragma unroll
-    for (int m = 1; m < 4; ++m) rr += cx >= m * W;
-    const int x = cx - rr * W;
-    pc.row[j] = rr;
-    pc.goff[j] = (uint32_t)rr * A.si.y + (uint32_t)x * A.si.x + p * 16;
-    pc.klds[j] = (uint32_t)(x * 64 + ((p ^ kswz(x)) * 16));
-    pc.vlds[j] = (uint32_t)(G::VOFF + (p >> 1) * G::VHALF + x * 32 + (p & 1) * 16);
-  }
-  // this wave's tiles: query columns C .. C+7; first key column X0
-  const int C = 8 * tx;
-  const int Cc = min(C, W - 1);
-  const int X0 = window_start(Cc, W, KS);
-  const int cq = min(C + qx, W - 1);               // this lane's query column (clamped)
-  const int sx = window_start(cq, W, KS);          // ... its window's first column
-  // K read: key (row a, column X0 + ql), chunk g; V^T read: column
-  // X0 + 4g + ql/4, channels 4*(ql%4) .. + 3 of each channel half
-  const uint32_t klane = (uint32_t)((X0 + ql) * 64 + ((g ^ kswz(X0 + ql)) * 16));
-  const uint32_t vlane = (uint32_t)(G::VOFF + (X0 + 4 * g + (ql >> 2)) * 32 + (ql & 3) * 8);
+  // this wave's tiles: query columns C .. C+7; first key column X0; this
+  // lane's query column cq (clamped) and its window's first column sx; the
+  // K read of key (row a, column X0 + ql), chunk g, and the V^T read of
+  // column X0 + 4g + ql/4, channels 4*(ql%4) .. + 3 of each channel half, at
+  // ring columns counted from the strip's first staged column
+  int C = 0, X0 = 0, cq = 0, sx = 0;
+  uint32_t klane = 0, vlane = 0;
   // Query slices and outputs move through memory in "pixel order": lane L
   // holds 16-byte chunk L%4 of the tile's query L/4 (row L/32, column
   // (L/4)%8), so that each 16-lane quarter of a wave touches 4 whole 64-byte
@@ -222,9 +218,46 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
   // matrix-core layout, where lane (g, ql) holds chunk g of query ql.
   const int lp = lane >> 2, lc = lane & 3;
   const int lpy = lp >> 3, lpx = lp & 7;
-  const bool lcol_ok = C + lpx < W;
-  const uint32_t qcol = (uint32_t)min(C + lpx, W - 1) * A.si.x + lc * 16;
-  const uint32_t ocol = (uint32_t)(C + lpx) * A.so.x + lc * 16;
+  bool lcol_ok = false;
+  uint32_t qcol = 0, ocol = 0;
+  // Window caps of this lane's key columns X0 + 4g + i: +inf inside its
+  // query's window, -inf outside (hidden from the optimiser so that each
+  // masked entry costs one min).
+  float ccap[4];
+  auto set_strip = [&](int strip) {
+    const int c0 = strip * G::CW, c1 = min(c0 + G::CW, W);
+    const int xs0 = window_start(c0, W, KS);
+    const int nk = window_start(c1 - 1, W, KS) + KS - xs0;  // staged columns
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      int f = tid + j * G::THREADS;
+      f = f < 16 * nk ? f : f % (16 * nk);
+      const int p = f & 3, cx = f >> 2;            // chunk; row * nk + staged column
+      int rr = 0;
+#pragma unroll
+      for (int m = 1; m < 4; ++m) rr += cx >= m * nk;
+      const int lx = cx - rr * nk;
+      pc.row[j] = rr;
+      pc.goff[j] = (uint32_t)rr * A.si.y + (uint32_t)(xs0 + lx) * A.si.x + p * 16;
+      pc.klds[j] = (uint32_t)(lx * 64 + ((p ^ kswz(lx)) * 16));
+      pc.vlds[j] = (uint32_t)(G::VOFF + (p >> 1) * G::VHALF + lx * 32 + (p & 1) * 16);
+    }
+    C = c0 + 8 * min(tx, NTX - 1);
+    X0 = window_start(min(C, W - 1), W, KS);
+    cq = min(C + qx, W - 1);
+    sx = window_start(cq, W, KS);
+    const int kx = X0 - xs0 + ql;
+    klane = (uint32_t)(kx * 64 + ((g ^ kswz(kx)) * 16));
+    vlane = (uint32_t)(G::VOFF + (X0 - xs0 + 4 * g + (ql >> 2)) * 32 + (ql & 3) * 8);
+    lcol_ok = tx < NTX && C + lpx < c1;
+    qcol = (uint32_t)min(C + lpx, W - 1) * A.si.x + lc * 16;
+    ocol = (uint32_t)(C + lpx) * A.so.x + lc * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ccap[i] = (unsigned)(X0 + 4 * g + i - sx) < (unsigned)KS ? INFINITY : -INFINITY;
+      asm volatile("" : "+v"(ccap[i]));
+    }
+  };
   const int qsrc = (4 * ql + g) * 4;
   // out: the lane holding chunk lc of query lp after the pair swap below
   const int osrc = (16 * ((lc >> 1) + 2 * (lc & 1)) + lp) * 4;
@@ -257,15 +290,6 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     }
   };
 
-  // Window caps of this lane's key columns X0 + 4g + i: +inf inside its
-  // query's window, -inf outside (hidden from the optimiser so that each
-  // masked entry costs one min).
-  float ccap[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ccap[i] = (unsigned)(X0 + 4 * g + i - sx) < (unsigned)KS ? INFINITY : -INFINITY;
-    asm volatile("" : "+v"(ccap[i]));
-  }
   // Softmax weights of one tile's scores, as the 16-bit P^T operands of its
   // NB / 2 key-row pairs; returns the log-sum-exp of the lane's query (LSE
   // only: from the fp32 weights' sum, not the 16-bit one the output is
@@ -381,9 +405,14 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
   for (int e = tid * 16; e < G::TABOFF; e += G::THREADS * 16)
     *(u32x4 *)(lds + e) = u32x4{0u, 0u, 0u, 0u};
 
-  int cur_h = -1;
+  int cur_h = -1, cur_strip = -1;
   for (int u = xcd_contiguous_id(blockIdx.x, gridDim.x); u < A.nunits; u += gridDim.x) {
     const Unit t = unit_at(u, A);
+    const bool newstrip = t.strip != cur_strip;
+    if (newstrip) {
+      set_strip(t.strip);
+      cur_strip = t.strip;
+    }
     // the plane of q, k, v and of out as buffer resources (scalar
     // registers): loads take a 32-bit lane offset plus a scalar row offset;
     // stores of lanes without a query get an offset past the plane's end,
@@ -502,8 +531,8 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
     if (newtab) {
       __syncthreads();  // the table is complete
       cur_h = tabkey;
-      build_cin();
     }
+    if (newtab || newstrip) build_cin();
 
     // One step: compute step s (query slices qs0, qs1, then reloaded with
     // those of step s + 2), then commit the group of step s + 1 from gc and
@@ -588,7 +617,7 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
       if constexpr (LSE) {
         // lane (0, ql) writes query ql of each tile: row R0 + qy (+ 2),
         // column C + qx
-        const bool col_ok = g == 0 && s < t.nsteps && C + qx < W;
+        const bool col_ok = g == 0 && s < t.nsteps && tx < NTX && C + qx < W;
         const bool l0 = col_ok && R0 + qy < t.q1, l1 = col_ok && R0 + 2 + qy < t.q1;
         const int la = t.flip ? H - 1 - (R0 + qy) : R0 + qy;
         const int lb = t.flip ? H - 3 - (R0 + qy) : R0 + 2 + qy;
@@ -620,11 +649,11 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX>::THREADS)) void stream_mfma_ker
 }
 
 // m: the map's shape; c: the class map (m.H / d x m.W / d, dilation 1).
-template <typename T, int KS, int NTX>
+template <typename T, int KS, int NTX, bool STRIPS>
 hipError_t launch_stream_t(const void *q, const void *k, const void *v, const void *rpb,
                            void *out, float *lse, const Shape &m, const Shape &c,
                            const ByteStrides &si, const ByteStrides &so, hipStream_t st) {
-  using G = StreamGeo<KS, NTX>;
+  using G = StreamGeo<KS, NTX, STRIPS>;
   StreamArgs a;
   a.s = c;
   a.si = ByteStrides{si.b, si.h, si.y * (uint32_t)m.dil, si.x * (uint32_t)m.dil};
@@ -636,25 +665,27 @@ hipError_t launch_stream_t(const void *q, const void *k, const void *v, const vo
   a.oxi = (int)si.x;
   a.oyo = (int)so.y;
   a.oxo = (int)so.x;
-  const int64_t classes = (int64_t)m.B * m.heads * m.dil * m.dil;
+  a.nstrip = (c.W + G::CW - 1) / G::CW;
+  const int64_t columns = (int64_t)m.B * m.heads * m.dil * m.dil * a.nstrip;
   const int cus = device_compute_units();
   // rows per unit: a multiple of 4, split until there are about as many
   // units as compute units (one workgroup per compute unit)
   int nseg = 1;
-  while (classes * (nseg + 1) <= cus && (c.H + nseg) / (nseg + 1) >= 12) ++nseg;
+  while (columns * (nseg + 1) <= cus && (c.H + nseg) / (nseg + 1) >= 12) ++nseg;
   a.seg = (((c.H + nseg - 1) / nseg) + 3) & ~3;
   a.nseg = (c.H + a.seg - 1) / a.seg;
-  const int64_t nunits = classes * a.nseg;
+  const int64_t nunits = columns * a.nseg;
   if (nunits > INT_MAX) return hipErrorInvalidConfiguration;
   a.nunits = (int)nunits;
   a.fseg = make_fastdiv((uint32_t)a.nseg);
   a.fheads = make_fastdiv((uint32_t)m.heads);
   a.fdil = make_fastdiv((uint32_t)m.dil);
+  a.fstrip = make_fastdiv((uint32_t)a.nstrip);
   const int grid = (int)(nunits < cus ? nunits : cus);
-  auto kern = m.dil == 1 ? (lse ? stream_mfma_kernel<T, KS, NTX, true, true>
-                                 : stream_mfma_kernel<T, KS, NTX, false, true>)
-                         : (lse ? stream_mfma_kernel<T, KS, NTX, true, false>
-                                : stream_mfma_kernel<T, KS, NTX, false, false>);
+  auto kern = m.dil == 1 ? (lse ? stream_mfma_kernel<T, KS, NTX, true, true, STRIPS>
+                                 : stream_mfma_kernel<T, KS, NTX, false, true, STRIPS>)
+                         : (lse ? stream_mfma_kernel<T, KS, NTX, true, false, STRIPS>
+                                : stream_mfma_kernel<T, KS, NTX, false, false, STRIPS>);
   kern<<<dim3((unsigned)grid), G::THREADS, 0, st>>>((const T *)q, (const T *)k, (const T *)v,
                                                     (const T *)rpb, (T *)out, lse, a);
   return hipGetLastError();
@@ -668,11 +699,13 @@ hipError_t launch_stream_k(const void *q, const void *k, const void *v, const vo
   c.H = m.H / m.dil;
   c.W = m.W / m.dil;
   c.dil = 1;
-  // one wave per 8-column tile column of the class map
+  // one wave per 8-column tile column of the class map; wider maps in
+  // strips of 56 columns
+  if (c.W > 56) return launch_stream_t<T, KS, 7, true>(q, k, v, rpb, out, lse, m, c, si, so, st);
   switch ((c.W + 7) / 8) {
-    case 5: return launch_stream_t<T, KS, 5>(q, k, v, rpb, out, lse, m, c, si, so, st);
-    case 6: return launch_stream_t<T, KS, 6>(q, k, v, rpb, out, lse, m, c, si, so, st);
-    default: return launch_stream_t<T, KS, 7>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 5: return launch_stream_t<T, KS, 5, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 6: return launch_stream_t<T, KS, 6, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    default: return launch_stream_t<T, KS, 7, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
   }
 }
 
@@ -688,7 +721,7 @@ bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt) {
   if (s.ks != 3 && s.ks != 5 && s.ks != 7) return false;
   if (s.H % s.dil != 0 || s.W % s.dil != 0) return false;
   const int hc = s.H / s.dil, wc = s.W / s.dil;
-  return wc > 32 && wc <= 56 && hc >= 16;
+  return wc > 32 && hc >= 16;
 }
 
 hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
