@@ -19,7 +19,7 @@ from vision_transformer_local_amd import inputs as I
 from vision_transformer_local_amd import na2d
 from vision_transformer_local_amd.inputs import Problem
 
-from parity_util import compare, gpu_inputs, note
+from parity_util import compare, gpu_inputs, note, sample_indices
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,25 @@ def test_stream_kernel_detection_d1_full_size():
     compare(p, out, cpu)
     ref = oracle.forward(*cpu, 7, 1, lse=True)["lse"]
     assert float(np.abs(lse.cpu().double().numpy() - ref).max()) <= 2e-5
+
+
+@pytest.mark.parametrize("p", [Problem(64, 4, 16, 120, 32, 7, 1, "bf16"),
+                               Problem(6, 4, 200, 336, 32, 7, 8, "bf16"),
+                               Problem(40, 3, 18, 60, 32, 5, 1, "f16")],
+                         ids=lambda p: p.describe().replace(" ", "_"))
+def test_stream_kernel_several_units_per_workgroup(p):
+    """More units than compute units: each workgroup walks several, whose
+    strips, classes and heads differ from one to the next (the per-strip
+    constants and the bias table are set again when they change).  The
+    first and last plane in full plus a random sample against the oracle,
+    and every output equal to the block-tiled kernel's within the bound."""
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=5)
+    note("stream several units %s" % p.describe())
+    out = na2d.forward(q, k, v, rpb, p.kernel_size, p.dilation)
+    tiled = na2d.forward(q, k, v, rpb, p.kernel_size, p.dilation, algo="mfma_tiled")
+    torch.cuda.synchronize()
+    compare(p, out, cpu, idx=sample_indices(p, 150_000))
+    assert float((out.float() - tiled.float()).abs().max()) <= 2e-2
 
 
 DILATED = [(130, 130, 2, 7), (64, 80, 2, 7), (48, 105, 3, 5), (100, 168, 4, 7), (34, 66, 2, 3), (96, 264, 6, 7)]
