@@ -584,10 +584,11 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX, STRIPS>::THREADS)) void stream_
         res0 = finish(o0, o1, o2);
         res1 = finish(u0, u1, u2);
       } else {
-        // clamped rows (the first and last steps of a plane): one tile at a
-        // time, in a loop that is not unrolled (it keeps the code small)
+        // clamped rows (the first and last steps of a plane): the two tiles
+        // each with its own key rows and accumulator inputs from the table
+        // (unrolled, so that their independent products interleave)
         res0 = res1 = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll 1
+#pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int Rt = min(R + 2 * tt, H - 1);
           vec qv;
