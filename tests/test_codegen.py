@@ -8,7 +8,9 @@ hipcc cross-compiles to assembly, nothing runs).
   buffers apart (it loses track once an address is derived through too many
   steps), it makes the read wait for that copy, which stalls every tile on
   the next block's loads.  (The fused block kernel loads its x operands into
-  registers for its own next products; waits for those are expected.)
+  registers for its own next products; waits for those are expected, and so
+  is a full wait that no further load follows before the loop branches back
+  or the kernel ends: the last steps of a unit need every load in flight.)
 * No vector-register spills and no scratch memory, in every matrix-core
   kernel: forward, projection, fused block, backward.  (Scalar registers may
   spill into vector-register lanes, which costs no memory traffic.)
@@ -48,6 +50,27 @@ def _kernels(asm):
         yield m.group(1), asm[m.end():end].split("\n")
 
 
+def _loads_follow(ops, i):
+    """Whether a vector-memory load is issued after ops[i] before a branch
+    back to an earlier label (the loop's next iteration) or the end of the
+    kernel, scanning the code in its layout order."""
+    labels = {}
+    for j, op in enumerate(ops):
+        if op.endswith(":"):
+            labels[op[:-1]] = j
+    for op in ops[i + 1:]:
+        mnem = op.split()[0]
+        if mnem.startswith(("buffer_load", "global_load")):
+            return True
+        if mnem == "s_endpgm":
+            return False
+        if mnem.startswith(("s_branch", "s_cbranch")):
+            target = op.split()[-1]
+            if labels.get(target, len(ops)) <= i:
+                return False
+    return False
+
+
 def _metadata(asm, name):
     meta = asm[asm.index(".amdgpu_metadata"):]
     for block in meta.split("- .agpr_count")[1:]:
@@ -62,11 +85,15 @@ def test_kernel_code_properties(src, tmp_path):
     kernels = list(_kernels(asm))
     assert kernels, "no kernels found in " + src
     for name, body in kernels:
-        ops = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
+        ops = [l.split(";")[0].strip() for l in body]
+        ops = [o for o in ops if o and (not o.startswith(".") or o.startswith(".LBB"))]
         for i, op in enumerate(ops):
+            if op.endswith(":"):
+                continue
             if src in PIPELINED and re.fullmatch(r"s_waitcnt vmcnt\(0\)", op):
                 near = [o.split()[0] for o in ops[max(0, i - 2):i + 3]]
-                assert not any(o.startswith("ds_read") for o in near), (
+                assert not (any(o.startswith("ds_read") for o in near)
+                            and _loads_follow(ops, i)), (
                     "%s: full vector-memory wait next to an LDS read: %s" % (name, near))
             mnem = op.split()[0]
             assert not mnem.startswith("flat_"), "%s: flat access %s" % (name, op)

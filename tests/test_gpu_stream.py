@@ -1,7 +1,7 @@
 """GPU parity of the row-streaming forward kernel (k in {3, 5, 7}, bf16 /
-fp16, maps -- with dilation d dividing H and W, residue classes -- more than
-32 columns wide, in strips of 56 columns beyond 56, and at least 16 rows
-high) against the float64 oracle.
+fp16, maps -- with dilation d dividing H and W, residue classes -- of any
+width at k = 3 and 5 and more than 32 columns wide at k = 7, in strips of 56
+columns beyond 56) against the float64 oracle.
 
 The shapes are chosen for the kernel's own structure: every workgroup width
 (5, 6 and 7 tile columns of 8, ragged last tiles), query-row runs split into
@@ -42,6 +42,23 @@ def test_stream_kernel_matches_oracle(H, W, ks, dtype):
         compare(p, out, cpu)
 
 
+NARROW = [(28, 28, 5), (14, 14, 3), (9, 20, 5), (12, 7, 5), (30, 17, 3), (8, 32, 3), (7, 7, 5), (4, 26, 3)]
+
+
+@pytest.mark.parametrize("H,W,ks", NARROW, ids=str)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stream_kernel_narrow_maps(H, W, ks, dtype):
+    """Maps at most 32 columns wide (1 to 4 waves per workgroup, several
+    workgroups per compute unit) and short ones, at k = 3 and 5 (at k = 7
+    the block-tiled kernel takes them)."""
+    p = Problem(3, 2, H, W, 32, ks, 1, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=H * 11 + W)
+    note("stream narrow %s" % p.describe())
+    out = na2d.forward(q, k, v, rpb, ks, 1)
+    torch.cuda.synchronize()
+    compare(p, out, cpu)
+
+
 WIDE = [(20, 57, 7), (33, 120, 5), (17, 200, 3), (24, 113, 7), (16, 64, 7)]
 
 
@@ -76,7 +93,8 @@ def test_stream_kernel_detection_d1_full_size():
 
 @pytest.mark.parametrize("p", [Problem(64, 4, 16, 120, 32, 7, 1, "bf16"),
                                Problem(6, 4, 200, 336, 32, 7, 8, "bf16"),
-                               Problem(40, 3, 18, 60, 32, 5, 1, "f16")],
+                               Problem(40, 3, 18, 60, 32, 5, 1, "f16"),
+                               Problem(64, 4, 28, 28, 32, 5, 1, "bf16")],
                          ids=lambda p: p.describe().replace(" ", "_"))
 def test_stream_kernel_several_units_per_workgroup(p):
     """More units than compute units: each workgroup walks several, whose

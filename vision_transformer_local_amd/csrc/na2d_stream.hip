@@ -50,6 +50,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 namespace na2d {
 namespace {
 
@@ -75,7 +77,14 @@ template <int KS, int NTX, bool STRIPS = false> struct StreamGeo {
   static constexpr int WAVES = NTX + (STRIPS ? 1 : 0);
   static constexpr int THREADS = 64 * WAVES;      // one wave per tile column
   static constexpr int CW = 8 * NTX;              // query columns
-  static constexpr int SCW = CW + 8;              // staged columns (reads reach CW + 7)
+  // staged columns: at most CW (the map, at most CW wide) or, with strips,
+  // CW + k - 1; a tile's reads of the 16 key columns from its first one are
+  // clamped to the last staged column (columns past it are only ever masked)
+  static constexpr int NK = STRIPS ? CW + KS - 1 : CW;
+  // ring row pitch in columns: NK where several workgroups share a compute
+  // unit (NTX < 5) and LDS is the limit; 8 * (NTX + 1) otherwise, as it
+  // measured a little faster than 8 * NTX at NTX = 7
+  static constexpr int SCW = (STRIPS || NTX < 5) ? NK : CW + 8;
   static constexpr int RING = 16;                 // staged rows
   static constexpr int KROW = SCW * 64;           // bytes per K ring row
   static constexpr int VROW = SCW * 32;           // bytes per V ring row (one channel half)
@@ -87,11 +96,8 @@ template <int KS, int NTX, bool STRIPS = false> struct StreamGeo {
   static constexpr int NTAB = SIDE * SIDE + 2 * MARGIN;
   static constexpr int TABOFF = VOFF + 2 * VHALF; // bias table (times sqrt(D)), zero margins
   static constexpr int LDS = TABOFF + NTAB * 4;
-  // 16-byte pieces per lane and tensor for one group of 4 rows (at most CW
-  // staged columns of 4 chunks, CW + k - 1 with strips)
-  static constexpr int NK = STRIPS ? CW + KS - 1 : CW;
+  // 16-byte pieces per lane and tensor for one group of 4 rows
   static constexpr int NP = (16 * NK + THREADS - 1) / THREADS;
-  static_assert(NK <= SCW, "staged columns fit the ring rows");
   static_assert(NB % 2 == 0 && NB <= 8, "tile key rows");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(VHALF < (1 << 16), "the second V half is a 16-bit immediate offset");
@@ -246,9 +252,9 @@ __global__ __launch_bounds__((StreamGeo<KS, NTX, STRIPS>::THREADS)) void stream_
     X0 = window_start(min(C, W - 1), W, KS);
     cq = min(C + qx, W - 1);
     sx = window_start(cq, W, KS);
-    const int kx = X0 - xs0 + ql;
+    const int kx = min(X0 - xs0 + ql, nk - 1);
     klane = (uint32_t)(kx * 64 + ((g ^ kswz(kx)) * 16));
-    vlane = (uint32_t)(G::VOFF + (X0 - xs0 + 4 * g + (ql >> 2)) * 32 + (ql & 3) * 8);
+    vlane = (uint32_t)(G::VOFF + min(X0 - xs0 + 4 * g + (ql >> 2), nk - 1) * 32 + (ql & 3) * 8);
     lcol_ok = tx < NTX && C + lpx < c1;
     qcol = (uint32_t)min(C + lpx, W - 1) * A.si.x + lc * 16;
     ocol = (uint32_t)(C + lpx) * A.so.x + lc * 16;
@@ -668,9 +674,12 @@ hipError_t launch_stream_t(const void *q, const void *k, const void *v, const vo
   a.oxo = (int)so.x;
   a.nstrip = (c.W + G::CW - 1) / G::CW;
   const int64_t columns = (int64_t)m.B * m.heads * m.dil * m.dil * a.nstrip;
-  const int cus = device_compute_units();
+  // workgroups per compute unit: as many as its LDS holds, at most two
+  // waves per SIMD (eight per compute unit)
+  const int per_cu = std::max(1, std::min(160 * 1024 / G::LDS, 8 / G::WAVES));
+  const int cus = device_compute_units() * per_cu;
   // rows per unit: a multiple of 4, split until there are about as many
-  // units as compute units (one workgroup per compute unit)
+  // units as workgroups that run at once
   int nseg = 1;
   while (columns * (nseg + 1) <= cus && (c.H + nseg) / (nseg + 1) >= 12) ++nseg;
   a.seg = (((c.H + nseg - 1) / nseg) + 3) & ~3;
@@ -704,6 +713,10 @@ hipError_t launch_stream_k(const void *q, const void *k, const void *v, const vo
   // strips of 56 columns
   if (c.W > 56) return launch_stream_t<T, KS, 7, true>(q, k, v, rpb, out, lse, m, c, si, so, st);
   switch ((c.W + 7) / 8) {
+    case 1: return launch_stream_t<T, KS, 1, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 2: return launch_stream_t<T, KS, 2, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 3: return launch_stream_t<T, KS, 3, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
+    case 4: return launch_stream_t<T, KS, 4, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
     case 5: return launch_stream_t<T, KS, 5, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
     case 6: return launch_stream_t<T, KS, 6, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
     default: return launch_stream_t<T, KS, 7, false>(q, k, v, rpb, out, lse, m, c, si, so, st);
@@ -713,16 +726,19 @@ hipError_t launch_stream_k(const void *q, const void *k, const void *v, const vo
 }  // namespace
 
 // Maps (with dilation d: residue classes, all of one size when d divides H
-// and W) 33 to 56 columns wide (5 to 7 waves per workgroup) and at least 16
-// rows high.  Narrower or shorter ones run faster on the block-tiled kernel:
-// they hold too few rows to hide a unit's first window, and too few waves
-// would share a compute unit.
+// and W) on which the kernel beats the block-tiled one as measured: at k = 7
+// those 33 columns wide or wider and at least 16 rows high (narrower or
+// shorter classes spend a large share of their keys on clamped edge windows
+// and too few rows to hide a unit's first window); at k = 3 and 5 any map at
+// least one window and 4 rows high, several workgroups sharing a compute
+// unit when the map is 32 columns wide or narrower.
 bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt) {
   if (dt != NA2D_DTYPE_BF16 && dt != NA2D_DTYPE_F16) return false;
   if (s.ks != 3 && s.ks != 5 && s.ks != 7) return false;
   if (s.H % s.dil != 0 || s.W % s.dil != 0) return false;
   const int hc = s.H / s.dil, wc = s.W / s.dil;
-  return wc > 32 && hc >= 16;
+  if (s.ks == 7) return wc > 32 && hc >= 16;
+  return wc >= s.ks && hc >= s.ks && hc >= 4;
 }
 
 hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
