@@ -186,39 +186,60 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     }
   };
 
-  // ---- staging of one block into a buffer (uniform per-class bases) ----
-  auto stage = [&](const DenseBlock &bk, char *kb, char *vb) {
+  // ---- per-wave addresses of a block: the bases of the wave's copies and of
+  // its tiles in q and out (uniform).  They are formed a round ahead, so
+  // that the scalar arithmetic sits beside the previous block's compute and
+  // the copies a barrier releases go out right after it.
+  struct Addr {
+    DenseBlock bk;
+    const char *src[DPW];   // copy m: the class base in k or v (+ doff[m] per lane)
+    int jh[DPW];            // copy m: its class (padded maps)
+    int64_t qb[TPW], ob[TPW];  // tile u: its class base in q and in out
+  };
+  auto addr = [&](int id) -> Addr {
+    Addr a;
+    a.bk = dense_block<KS>(id, fblk, per_head, hfast);
+#pragma unroll
+    for (int m = 0; m < DPW; ++m) {
+      const int i = wave + WAVES * m;
+      const int c = (i % DPT) / (NK / 16);
+      a.jh[m] = a.bk.j0 + min(c, a.bk.n - 1);
+      a.src[m] = (const char *)(i >= DPT ? v : k) + class_base(a.bk.h, a.jh[m], s, log2d, si);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int jt = a.bk.j0 + min((wave * TPW + u) / NT, a.bk.n - 1);
+      a.qb[u] = class_base(a.bk.h, jt, s, log2d, si);
+      a.ob[u] = class_base(a.bk.h, jt, s, log2d, so);
+    }
+    return a;
+  };
+  // ---- staging of one block into a buffer ----
+  auto stage = [&](const Addr &a, char *kb, char *vb) {
 #pragma unroll
     for (int m = 0; m < DPW; ++m) {
       const int i = wave + WAVES * m;
       const bool isv = i >= DPT;
       const int it = i % DPT, c = it / (NK / 16), kg = it % (NK / 16);
-      const int jh = bk.j0 + min(c, bk.n - 1);
-      const int64_t base = class_base(bk.h, jh, s, log2d, si);
-      const char *src = (const char *)(isv ? v : k) + base + doff[m];
+      const char *src = a.src[m] + doff[m];
       if constexpr (PAD) {
-        if (!real(jh, drow[m], dcol[m])) {
+        if (!real(a.jh[m], drow[m], dcol[m])) {
           const T *pv = isv ? pad_v : pad_k;
-          src = (pv != nullptr ? (const char *)(pv + bk.h * kHeadDim) : kZeroPixel) + dlch[m];
+          src = (pv != nullptr ? (const char *)(pv + a.bk.h * kHeadDim) : kZeroPixel) + dlch[m];
         }
       }
       char *dst = (isv ? vb : kb) + c * CB + kg * 1024;
       __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
     }
   };
-  // byte offset of the class of this wave's tile u in block bk (strides st)
-  auto tile_base = [&](const DenseBlock &bk, int u, const ByteStrides &st) -> int64_t {
-    const int c = (wave * TPW + u) / NT;
-    return class_base(bk.h, bk.j0 + min(c, bk.n - 1), s, log2d, st);
-  };
-  auto load_q = [&](const DenseBlock &bk, int u) -> u32x4 {
+  auto load_q = [&](const Addr &a, int u) -> u32x4 {
     if constexpr (PAD) {
       // a padded query is never stored: read pixel (0, 0) of its plane instead
-      const int jh = bk.j0 + min((wave * TPW + u) / NT, bk.n - 1);
+      const int jh = a.bk.j0 + min((wave * TPW + u) / NT, a.bk.n - 1);
       if (!real(jh, qrow[u], qcol[u]))
-        return *(const u32x4 *)((const char *)q + plane_base(bk.h, jh, log2d, si) + g * 16u);
+        return *(const u32x4 *)((const char *)q + plane_base(a.bk.h, jh, log2d, si) + g * 16u);
     }
-    return *(const u32x4 *)((const char *)q + tile_base(bk, u, si) + qoff[u] + g * 16u);
+    return *(const u32x4 *)((const char *)q + a.qb[u] + qoff[u] + g * 16u);
   };
 
   const float c2 = kLog2e / kSqrtD;
@@ -318,28 +339,29 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     if constexpr (PAD) ok = ok && real(bk.j0 + min(c, bk.n - 1), qrow[u], qcol[u]);
     return ok;
   };
-  auto store = [&](const DenseBlock &bk, int u, u32x4 val, bool ok, float tlse) {
+  auto store = [&](const Addr &a, int u, u32x4 val, bool ok, float tlse) {
     if (ok) {
-      char *o = (char *)out + tile_base(bk, u, so) + ooff[u] + g * 8u;
+      char *o = (char *)out + a.ob[u] + ooff[u] + g * 8u;
       *(u32x2 *)o = u32x2{val[0], val[1]};
       *(u32x2 *)(o + 16 * sizeof(T)) = u32x2{val[2], val[3]};
       // with dense q, the query's index in [B, heads, H, W] order is its q
       // byte offset over the pixel's D channels
       if (LSE && g == 0)
-        lse[(tile_base(bk, u, si) + qoff[u]) / (kHeadDim * sizeof(T))] = tlse;
+        lse[(a.qb[u] + qoff[u]) / (kHeadDim * sizeof(T))] = tlse;
     }
   };
 
   // ---- prologue ----
-  DenseBlock cur = dense_block<KS>(b0, fblk, per_head, hfast);
+  Addr acur = addr(b0);
   u32x4 qcur[TPW];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) qcur[u] = load_q(cur, u);
-  load_ctab(cur.h);
-  stage(cur, kbuf0, vbuf0);
-  store_ctab(cur.h & 1);
+  for (int u = 0; u < TPW; ++u) qcur[u] = load_q(acur, u);
+  load_ctab(acur.bk.h);
+  stage(acur, kbuf0, vbuf0);
+  store_ctab(acur.bk.h & 1);
   int slot_h[2] = {-1, -1};  // head whose table each slot holds
-  slot_h[cur.h & 1] = cur.h;
+  slot_h[acur.bk.h & 1] = acur.bk.h;
+  Addr anxt = addr(min(b0 + 1, b1 - 1));
   __syncthreads();
 
   u32x4 res[TPW];
@@ -350,14 +372,14 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
   // buffer being read.
   auto step = [&](int bi, const char *kc, const char *vc, char *kn, char *vn) {
     const bool more = bi + 1 < b1;
-    const DenseBlock nxt = dense_block<KS>(more ? bi + 1 : bi, fblk, per_head, hfast);
+    if (more) stage(anxt, kn, vn);
     u32x4 qnxt[TPW];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) qnxt[u] = load_q(nxt, u);
+    for (int u = 0; u < TPW; ++u) qnxt[u] = load_q(anxt, u);
+    const DenseBlock &cur = acur.bk, &nxt = anxt.bk;
     const int nslot = nxt.h & 1;
     const bool newtab = more && slot_h[nslot] != nxt.h;
     if (newtab) load_ctab(nxt.h);
-    if (more) stage(nxt, kn, vn);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       rok[u] = tile_ok(cur, u);
@@ -366,6 +388,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
                                              : u32x4{0u, 0u, 0u, 0u};
     }
     if (!more) return;
+    const Addr a2 = addr(min(bi + 2, b1 - 1));  // the round after next
     if (newtab) {
       // the slot the current block reads: wait until every wave is done with
       // it (the other slot was last read before the previous barrier)
@@ -376,8 +399,9 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     __syncthreads();  // also waits for the DMA (workgroup fence)
     // results leave after the barrier, whose wait then covers only the loads
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u], rlse[u]);
-    cur = nxt;
+    for (int u = 0; u < TPW; ++u) store(acur, u, res[u], rok[u], rlse[u]);
+    acur = anxt;
+    anxt = a2;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) qcur[u] = qnxt[u];
   };
@@ -387,7 +411,7 @@ __global__ __launch_bounds__(DenseGeometry<KS>::THREADS) void dense_mfma_kernel(
     step(bi + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) store(cur, u, res[u], rok[u], rlse[u]);  // the last block
+  for (int u = 0; u < TPW; ++u) store(acur, u, res[u], rok[u], rlse[u]);  // the last block
 }
 
 template <typename T, int KS>
