@@ -2,7 +2,7 @@
 against the float64 oracle on the same seeded inputs, through the C ABI.
 
 Every forward kernel family writes it: the general matrix-core kernel, the
-row-streaming kernel (no dilation, k = 3, 5, 7, maps 33 to 56 columns wide),
+row-streaming kernel (k = 3, 5, 7; at k = 7 maps more than 32 columns wide),
 the whole-sub-grid kernel (maps of exactly k*d, k = 3, 5, 7, power-of-two d)
 and the per-lane kernel (fp32).  out must stay bit-identical to na2d_forward's.
 

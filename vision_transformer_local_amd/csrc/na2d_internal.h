@@ -158,9 +158,10 @@ hipError_t launch_dense_mfma(const void *q, const void *k, const void *v, const 
                              na2d_dtype_t dt, hipStream_t st, bool *supported,
                              float *lse = nullptr);
 // Row-streaming kernel (k in {3, 5, 7}, 16-bit data, maps -- with dilation d
-// dividing H and W, residue classes -- 33 to 56 columns wide and at least 16
-// rows high); byte strides as the general kernel's; lse (optional) as the
-// general kernel's, dense q only.
+// dividing H and W, residue classes -- at k = 7 more than 32 columns wide and
+// at least 16 rows high, at k = 3 and 5 at least k columns and max(k, 4)
+// rows); byte strides as the general kernel's; lse (optional) as the general
+// kernel's, dense q only.
 bool stream_mfma_supported(const Shape &s, na2d_dtype_t dt);
 hipError_t launch_stream_mfma(const void *q, const void *k, const void *v, const void *rpb,
                               void *out, float *lse, const Shape &s,

@@ -1,7 +1,8 @@
 // na2d_stream.hip -- row-streaming fused forward of 2D (dilated) Neighborhood
 // Attention on the CDNA4 matrix cores: bf16 / fp16 inputs, fp32
 // accumulation, D = 32, kernel sizes 3, 5, 7, maps (or, with dilation d,
-// residue classes) 33 to 56 columns wide.
+// residue classes) of any width: up to 56 columns in one workgroup of 1 to 7
+// waves, wider ones in strips of 56 columns.
 //
 // The operator is the one the DiNAT module composes from natten2dqkrpb,
 // softmax(dim=-1) and natten2dav (DiNAT walk-through blog, "What is DiNAT");
