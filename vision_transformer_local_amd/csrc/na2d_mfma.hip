@@ -98,9 +98,16 @@ template <int KS, int RYV = default_rows(KS)> struct Geometry {
 };
 
 // Block ids enumerate (batch, head, ry, by, bx, rx) with rx fastest.  A
-// workgroup visits consecutive ids, so it keeps the mixed-radix digits and
-// steps them.  (With channels-last maps the heads of a pixel share its
-// lines; making the head the fastest digit was tried and lost the halo
+// workgroup keeps the mixed-radix digits and steps them.  Without dilation it
+// visits a contiguous run of ids.  With dilation d the workgroups form crews
+// of d (consecutive workgroup numbers, so one XCD): member rx of a crew keeps
+// column class rx and the crew walks a contiguous run of the other digits in
+// step.  The classes rx and rx + 1 share every 128-byte line (their 64-byte
+// pixels alternate along a row), so the crew's members request each line
+// within the same block time and the second request finds it in L2; and
+// the next block column of a class, whose halo overlaps this one's, is the
+// member's next block.  (With channels-last maps the heads of a pixel share
+// its lines; making the head the fastest digit was tried and lost the halo
 // reuse between neighbouring blocks: 2.6x the L2 misses.)
 struct BlockCursor {
   int b, h, ry, by, bx, rx;
@@ -127,10 +134,14 @@ __device__ __forceinline__ BlockCursor cursor_at(uint32_t id, int dil, const Fas
   return c;
 }
 
-// Steps to the next id; true when the row part (batch, head, ry, by) changed.
-__device__ __forceinline__ bool cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads) {
-  if (++c.rx < dil) return false;
-  c.rx = 0;
+// Steps to the next id (with fixrx, to the next id of the same column class
+// rx); true when the row part (batch, head, ry, by) changed.
+__device__ __forceinline__ bool cursor_step(BlockCursor &c, int dil, int nbx, int nby, int heads,
+                                            bool fixrx) {
+  if (!fixrx) {
+    if (++c.rx < dil) return false;
+    c.rx = 0;
+  }
   if (++c.bx < nbx) return false;
   c.bx = 0;
   if (++c.by < nby) return true;
@@ -615,11 +626,25 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   // it) in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 15, g = lane >> 4;
-  // this workgroup's contiguous run of blocks
+  // this workgroup's blocks: a contiguous run of ids, or, in a crew of d
+  // (the launch makes the grid a multiple of d when d > 1), every d-th id of
+  // the crew's run of d * count ids, from the member's own class
   const int wg = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int b0 = (int)((int64_t)nblocks * wg / gridDim.x);
-  const int b1 = (int)((int64_t)nblocks * (wg + 1) / gridDim.x);
-  if (b0 >= b1) return;
+  const int ngrid = (int)gridDim.x;
+  const bool crew = s.dil > 1 && ngrid % s.dil == 0;
+  int first, count;
+  if (crew) {
+    const int nsets = ngrid / s.dil, set = (int)fast_div((uint32_t)wg, fdil);
+    const int units = nblocks / s.dil;  // blocks per column class digit
+    const int p0 = (int)((int64_t)units * set / nsets);
+    const int p1 = (int)((int64_t)units * (set + 1) / nsets);
+    first = p0 * s.dil + (wg - set * s.dil);
+    count = p1 - p0;
+  } else {
+    first = (int)((int64_t)nblocks * wg / ngrid);
+    count = (int)((int64_t)nblocks * (wg + 1) / ngrid) - first;
+  }
+  if (count <= 0) return;
   const bool has_rpb = rpb != nullptr;
   // this wave's tile and this lane's query position within a block
   const int ty = wave / G::NTX, tx = wave % G::NTX;
@@ -631,7 +656,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   // nothing consumes them before the end-of-block barrier, so the loads
   // overlap the whole compute of block n.
   T treg[TableRegs<KS, RY>::N];
-  BlockCursor cc = cursor_at(b0, s.dil, fdil, fnbx, fnby, fheads);
+  BlockCursor cc = cursor_at((uint32_t)first, s.dil, fdil, fnbx, fnby, fheads);
   RowPart rcur = row_part<T, KS, RY>(cc, s, fdil, si, so, ty, lr);
   ColPart ccur = col_part<T, KS>(cc, s, fdil, si, tx, lc);
   QueryOffs pcur = query_offsets(rcur, ccur, s, si, so, lr, lc);
@@ -652,7 +677,7 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
   auto step = [&](const char *kc, const char *vc, const float *tc, char *kn, char *vn, float *tn,
                   int &tab_hn, bool more) {
     RowPart rnxt = rcur;
-    if (more && cursor_step(cc, s.dil, nbx, nby, s.heads))
+    if (more && cursor_step(cc, s.dil, nbx, nby, s.heads, crew))
       rnxt = row_part<T, KS, RY>(cc, s, fdil, si, so, ty, lr);
     const ColPart cnxt = col_part<T, KS>(cc, s, fdil, si, tx, lc);
     const QueryOffs pnxt = query_offsets(rnxt, cnxt, s, si, so, lr, lc);
@@ -683,11 +708,11 @@ __global__ __launch_bounds__((Geometry<KS, RY>::THREADS)) void fused_mfma_kernel
     qcur = qnxt;
   };
   // Two blocks per iteration so that each buffer is a fixed LDS array.
-  for (int bi = b0; bi < b1; bi += 2) {
-    const bool more0 = bi + 1 < b1;
+  for (int bi = 0; bi < count; bi += 2) {
+    const bool more0 = bi + 1 < count;
     step(kbuf0, vbuf0, tab0, kbuf1, vbuf1, tab1, tab_h1, more0);
     if (!more0) break;
-    step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < b1);
+    step(kbuf1, vbuf1, tab1, kbuf0, vbuf0, tab0, tab_h0, bi + 2 < count);
   }
   // the last block
   if constexpr (STREAM) store_out<T, STREAM>(out, rcur.pofs, pcur.q, g, res);
@@ -713,8 +738,11 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const void *rpb
   const int nby = (Lymax + G::RY - 1) / G::RY, nbx = (Lxmax + G::RX - 1) / G::RX;
   const int64_t nblocks = (int64_t)s.B * s.heads * s.dil * s.dil * nby * nbx;
   if (nblocks > INT_MAX) return hipErrorInvalidConfiguration;
-  // one persistent workgroup per compute unit (its LDS holds two blocks)
-  const int64_t grid = nblocks < device_compute_units() ? nblocks : device_compute_units();
+  // one persistent workgroup per compute unit (its LDS holds two blocks);
+  // with dilation a multiple of d (crews of d workgroups, one per column
+  // class; nblocks is a multiple of d)
+  int64_t grid = nblocks < device_compute_units() ? nblocks : device_compute_units();
+  if (s.dil > 1 && grid >= s.dil) grid -= grid % s.dil;
   // Non-temporal Q/out only when each line belongs to one block: dense maps
   // without dilation (channels-last maps interleave the heads' channels).
   auto kernel = s.dil == 1 && lay.planar
