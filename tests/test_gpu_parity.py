@@ -202,3 +202,20 @@ def test_whole_class_maps(p):
     for path in ("auto", "mfma"):
         note("%s path=%s" % (p.describe(), path))
         compare(p, run_path(path, p, g), cpu, idx=sample_indices(p, 200_000))
+
+
+# Dilated maps on the block-tiled kernel with more blocks than compute units:
+# its workgroups then form crews of d (one per column class, the grid rounded
+# down to a multiple of d).  d = 3 and 5 give crews that straddle two XCDs,
+# d = 8 crews within one; d = 257 exceeds the grid, so the workgroups walk
+# contiguous runs instead.
+CREWS = [Problem(6, 1, 60, 60, 32, 13, 3, "bf16"), Problem(4, 2, 75, 75, 32, 7, 5, "f16"),
+         Problem(2, 3, 64, 72, 32, 7, 8, "bf16"), Problem(1, 1, 771, 771, 32, 3, 257, "bf16")]
+
+
+@pytest.mark.parametrize("p", CREWS, ids=lambda p: p.describe().replace(" ", "_"))
+def test_dilated_crews(p):
+    cpu, g = gpu_inputs(p, seed=12)
+    for path in ("auto", "mfma_tiled"):
+        note("%s path=%s" % (p.describe(), path))
+        compare(p, run_path(path, p, g), cpu, idx=sample_indices(p, 100_000))
