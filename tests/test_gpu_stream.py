@@ -214,3 +214,35 @@ def test_stream_kernel_full_size_bit_stable():
     b = na2d.forward(q, k, v, rpb, 7, 1)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# Scores far from zero: q scaled up (scores in the hundreds: unshifted bf16
+# weights would overflow at the larger scales, fp16 ones already at the
+# smaller), and keys near a constant vector with q opposite to it (every
+# score far below zero: unshifted weights would underflow).  The softmax
+# subtracts each query's maximum first, so the output stays within the
+# usual bound.
+LARGE = [("bf16", 16.0), ("bf16", 64.0), ("f16", 4.0), ("f16", 16.0)]
+
+
+@pytest.mark.parametrize("dtype,scale", LARGE, ids=str)
+def test_stream_kernel_large_scores(dtype, scale):
+    p = Problem(2, 2, 40, 48, 32, 7, 1, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=21)
+    qs = (q.float() * scale).to(q.dtype)
+    note("stream large scores %s q*%g" % (p.describe(), scale))
+    out = na2d.forward(qs, k, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    compare(p, out, (qs.cpu(), cpu[1], cpu[2], cpu[3]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stream_kernel_scores_far_below_zero(dtype):
+    p = Problem(2, 2, 40, 48, 32, 7, 1, dtype)
+    cpu, (q, k, v, rpb) = gpu_inputs(p, seed=22)
+    kk = (1.0 + 0.1 * k.float()).to(k.dtype)
+    qq = torch.full_like(q, -8.0)
+    note("stream scores far below zero %s" % p.describe())
+    out = na2d.forward(qq, kk, v, rpb, 7, 1)
+    torch.cuda.synchronize()
+    compare(p, out, (qq.cpu(), kk.cpu(), cpu[2], cpu[3]))
